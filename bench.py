@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""SGEMM throughput on one MI355X: TFLOP/s and fraction of the fp32 peak.
+
+Default workload: 8192 x 8192 x 8192 row-major NN, A and B uniform[-1,1)
+from seed 4, alpha = 1, beta = 0 (the headline compute-bound shape). One
+"step" is one full SGEMM call through the C ABI (fg_sgemm). Inputs are
+resident in device memory before timing starts.
+
+Prints ONE JSON line (rank 0) with the metric, the roofline of the dominant
+kernel (timed with HIP events on the stream the kernel is launched on) and
+the CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C5a]
+                       [--suite] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_TFLOPS = 157.3  # MI355X dense fp32 matrix peak (256 CU x 2.4 GHz x 256 FLOP/clk)
+HBM_PEAK_GBS = 8000.0
+METRIC = "fp32 SGEMM TFLOP/s and % of MI355X fp32 peak at 4096^3 and 8192^3"
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("sgemm_mfma.hip", "fg_device.h", "fg_kernels.h", "fg_api.cpp"):
+        with open(os.path.join(ROOT, "fp32_gemm_tile_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """Measured HBM traffic per launch from committed rocprofv3 counter runs,
+    if they were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_gpu(w, steps, warmup, config=-1):
+    import torch
+    import fp32_gemm_tile_amd as fg
+    from fp32_gemm_tile_amd import workloads as wl
+
+    A, B, C = wl.make_inputs(w)
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    dC = torch.from_numpy(C).cuda() if C is not None else torch.empty(
+        (w.M, w.LDC), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step():
+        st = fg.fg_sgemm_ex(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
+                            w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
+                            sp, config)
+        if st != 0:
+            raise fg.FgError(st, fg.fg_last_bad_arg(), fg.fg_last_error())
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_events = ev0.elapsed_time(ev1)
+    cfg = fg.fg_select_config(w.transA, w.transB, w.M, w.N, w.K, dA.data_ptr(), w.LDA,
+                              dB.data_ptr(), w.LDB, dC.data_ptr(), w.LDC) if config < 0 \
+        else fg.fg_get_config(config)
+    return {"ms_per_launch": ms_events / steps, "wall_s": wall, "config": cfg["name"]}
+
+
+def cpu_baseline(w, target_s=15.0):
+    """The oracle as it is, on a bounded sample of output rows of the same
+    workload, scaled to TFLOP/s (2*N*K FLOP per output row)."""
+    import numpy as np
+    import oracle
+    from fp32_gemm_tile_amd import workloads as wl
+
+    A, B, C = wl.make_inputs(w)
+    threads = oracle.num_threads()
+    rows = 8
+    t0 = time.perf_counter()
+    oracle.gemm_rows(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A, w.LDA, B, w.LDB,
+                     w.beta, C, w.LDC, rows=np.arange(rows))
+    dt = time.perf_counter() - t0
+    rows = int(max(8, min(w.M, rows * target_s / max(dt, 1e-3))))
+    rng = np.random.default_rng(0)
+    sel = np.sort(rng.choice(w.M, size=rows, replace=False))
+    t0 = time.perf_counter()
+    oracle.gemm_rows(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A, w.LDA, B, w.LDB,
+                     w.beta, C, w.LDC, rows=sel)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows} of {w.M} output rows of {w.name} (binary64 oracle), {dt:.1f} s"}
+
+
+def run_one(name, steps, warmup, with_cpu, config=-1):
+    from fp32_gemm_tile_amd import workloads as wl
+    w = wl.WORKLOADS[name]
+    g = time_gpu(w, steps, warmup, config)
+    tflops = w.flops / (g["ms_per_launch"] * 1e-3) / 1e12
+    traffic = load_traffic(name)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(g["ms_per_launch"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"sgemm_{w.M}x{w.N}x{w.K}_{w.transA.lower()}{w.transB.lower()}",
+                   "M": w.M, "N": w.N, "K": w.K, "transA": w.transA, "transB": w.transB,
+                   "alpha": w.alpha, "beta": w.beta, "inputs": f"{w.dist} seed {w.seed}",
+                   "kernel_config": g["config"]},
+        "pct_of_fp32_peak": round(100 * tflops / PEAK_FP32_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
+                     "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_FP32_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if with_cpu:
+        out["cpu_baseline"] = cpu_baseline(w)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C5a")
+    ap.add_argument("--config", type=int, default=-1, help="force a table entry")
+    ap.add_argument("--suite", action="store_true",
+                    help="one line per workload C1..C6 (no CPU baseline)")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (--gpus 1); "
+              "multi-GPU sharding is not implemented", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import fp32_gemm_tile_amd as fg
+    fg.load_library()
+
+    if args.suite:
+        for name in ("C1", "C2", "C3", "C4", "C5a", "C5b", "C6"):
+            r = run_one(name, args.steps, args.warmup, False, args.config)
+            print(json.dumps(r), flush=True)
+        return
+
+    r = run_one(args.workload, args.steps, args.warmup, False, args.config)
+    # The 4096^3 shape of the metric, timed in the same run.
+    if args.workload == "C5a":
+        r2 = run_one("C6", args.steps, args.warmup, False, args.config)
+        r["also"] = {"sgemm_4096x4096x4096_nn": {"value": r2["value"], "unit": "TFLOP/s",
+                                                  "ms_per_step": r2["ms_per_step"],
+                                                  "pct_of_fp32_peak": r2["pct_of_fp32_peak"]}}
+    if not args.no_cpu:
+        from fp32_gemm_tile_amd import workloads as wl
+        r["cpu_baseline"] = cpu_baseline(wl.WORKLOADS[args.workload])
+    print(json.dumps(r), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+"""fp32_gemm_tile_amd -- true-fp32 SGEMM for MI355X (gfx950) behind a C ABI.
+
+    C = alpha * op(A) * op(B) + beta * C     (row-major, see include/fp32gemm.h)
+
+This module is a thin ctypes binding over ``libfp32gemm.so``: it marshals
+arguments and nothing else; every step of the product runs in the library's
+HIP kernels. There is no fallback: if the library is missing or cannot load,
+importing the binding's functions raises.
+
+Entry points (same names as the C ABI):
+  fg_sgemm(...), fg_sgemm_ex(...)      raw pointers and sizes
+  fg_num_configs(), fg_get_config(i), fg_select_config(...)
+  fg_last_bad_arg(), fg_last_error(), fg_status_string(s), fg_abi_version()
+Convenience:
+  sgemm(A, B, C, alpha, beta, transA, transB, config=-1, stream=None)
+      for torch tensors on the GPU (PyTorch only supplies memory and stream).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp32gemm.so")
+
+FG_OP_N, FG_OP_T = 0, 1
+FG_OK, FG_ERR_INVALID_ARG, FG_ERR_HIP, FG_ERR_UNSUPPORTED = 0, 1, 2, 3
+FG_KIND_MFMA, FG_KIND_VALU = 1, 2
+FG_MAX_LD = 2097152
+
+
+class FgError(RuntimeError):
+    def __init__(self, status, bad_arg, message):
+        self.status = status
+        self.bad_arg = bad_arg
+        super().__init__(f"{status_name(status)} (bad argument {bad_arg}): {message}")
+
+
+class fg_config(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int32), ("kind", ctypes.c_int32),
+                ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
+                ("wm", ctypes.c_int32), ("wn", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("name", ctypes.c_char * 40)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["name"] = self.name.decode()
+        return d
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load (once) and return the ctypes handle. Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+            " (there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+    gemm_args = [i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, vp]
+    lib.fg_sgemm.argtypes = gemm_args
+    lib.fg_sgemm.restype = i32
+    lib.fg_sgemm_ex.argtypes = gemm_args + [i32]
+    lib.fg_sgemm_ex.restype = i32
+    lib.fg_num_configs.argtypes = []
+    lib.fg_num_configs.restype = i32
+    lib.fg_get_config.argtypes = [i32, ctypes.POINTER(fg_config)]
+    lib.fg_get_config.restype = i32
+    lib.fg_select_config.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64,
+                                     ctypes.POINTER(fg_config)]
+    lib.fg_select_config.restype = i32
+    lib.fg_last_bad_arg.argtypes = []
+    lib.fg_last_bad_arg.restype = i32
+    lib.fg_last_error.argtypes = []
+    lib.fg_last_error.restype = ctypes.c_char_p
+    lib.fg_status_string.argtypes = [i32]
+    lib.fg_status_string.restype = ctypes.c_char_p
+    lib.fg_abi_version.argtypes = []
+    lib.fg_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _op(t) -> int:
+    if t in (0, 1):
+        return int(t)
+    if isinstance(t, str) and t.upper() in ("N", "T"):
+        return FG_OP_T if t.upper() == "T" else FG_OP_N
+    return int(t)  # let the library reject out-of-domain values
+
+
+def status_name(s: int) -> str:
+    return load_library().fg_status_string(int(s)).decode()
+
+
+def _raise_if(st: int):
+    if st != FG_OK:
+        lib = load_library()
+        raise FgError(st, lib.fg_last_bad_arg(), lib.fg_last_error().decode())
+
+
+# ---- C-ABI mirror ---------------------------------------------------------
+
+def fg_sgemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0):
+    """Raw call: A, B, C are device addresses (int), stream a hipStream_t (int)."""
+    return load_library().fg_sgemm(_op(transA), _op(transB), M, N, K, alpha, A, lda,
+                                   B, ldb, beta, C, ldc, stream or None)
+
+
+def fg_sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0,
+                config_id=-1):
+    return load_library().fg_sgemm_ex(_op(transA), _op(transB), M, N, K, alpha, A, lda,
+                                      B, ldb, beta, C, ldc, stream or None, config_id)
+
+
+def fg_num_configs() -> int:
+    return load_library().fg_num_configs()
+
+
+def fg_get_config(i: int) -> dict:
+    c = fg_config()
+    _raise_if(load_library().fg_get_config(i, ctypes.byref(c)))
+    return c.as_dict()
+
+
+def fg_select_config(transA, transB, M, N, K, A=0, lda=None, B=0, ldb=None, C=0,
+                     ldc=None) -> dict:
+    ta, tb = _op(transA), _op(transB)
+    lda = lda if lda is not None else max(1, K if ta == FG_OP_N else M)
+    ldb = ldb if ldb is not None else max(1, N if tb == FG_OP_N else K)
+    ldc = ldc if ldc is not None else max(1, N)
+    c = fg_config()
+    _raise_if(load_library().fg_select_config(ta, tb, M, N, K, A or None, lda, B or None,
+                                              ldb, C or None, ldc, ctypes.byref(c)))
+    return c.as_dict()
+
+
+def fg_last_bad_arg() -> int:
+    return load_library().fg_last_bad_arg()
+
+
+def fg_last_error() -> str:
+    return load_library().fg_last_error().decode()
+
+
+def fg_status_string(s: int) -> str:
+    return status_name(s)
+
+
+def fg_abi_version() -> int:
+    return load_library().fg_abi_version()
+
+
+def configs() -> list:
+    return [fg_get_config(i) for i in range(fg_num_configs())]
+
+
+# ---- torch convenience ----------------------------------------------------
+
+def _ld(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its rows")
+    return t.stride(0) if t.size(0) > 1 else max(1, t.size(1))
+
+
+def sgemm(A, B, C, alpha=1.0, beta=0.0, transA="N", transB="N", config=-1, stream=None):
+    """C <- alpha * op(A) @ op(B) + beta * C for float32 GPU tensors (row-major,
+    unit inner stride; leading dimensions are taken from the row strides).
+    Returns C. Enqueued on ``stream`` (default: torch's current stream)."""
+    import torch
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+    ta, tb = _op(transA), _op(transB)
+    M, N = C.shape
+    K = A.shape[1] if ta == FG_OP_N else A.shape[0]
+    if (A.shape[0] if ta == FG_OP_N else A.shape[1]) != M:
+        raise ValueError("op(A) rows != C rows")
+    if (B.shape[0] if tb == FG_OP_N else B.shape[1]) != K:
+        raise ValueError("op(B) rows != op(A) columns")
+    if (B.shape[1] if tb == FG_OP_N else B.shape[0]) != N:
+        raise ValueError("op(B) columns != C columns")
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = fg_sgemm_ex(ta, tb, M, N, K, float(alpha), A.data_ptr(), _ld(A, "A"),
+                     B.data_ptr(), _ld(B, "B"), float(beta), C.data_ptr(), _ld(C, "C"),
+                     stream, config)
+    _raise_if(st)
+    return C

@@ -1,0 +1,314 @@
+// Host side of the C ABI declared in include/fp32gemm.h: argument
+// validation, BLAS quick returns, the tile-configuration table and its
+// per-shape selection, and kernel launch on the caller's stream.
+//
+// The argument list and its meaning follow the BLAS-style routine of
+// "CuTe-ly writing an SM86 SGEMM", section "host-side setup" (row-major
+// here, with transpose flags); the per-shape choice of tile follows "Matmul
+// II: register blocking, warp tiling, tensor cores", section 8 (many kernel
+// variants and a heuristic that picks one per call).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "../../include/fp32gemm.h"
+#include "fg_kernels.h"
+
+namespace {
+
+thread_local int32_t t_bad_arg = 0;
+thread_local char t_error[256] = "";
+
+fg_status fail(fg_status s, int32_t bad_arg, const char* fmt, ...) {
+    t_bad_arg = bad_arg;
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(t_error, sizeof t_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+void clear_error() {
+    t_bad_arg = 0;
+    t_error[0] = '\0';
+}
+
+// ---------------------------------------------------------------------------
+// Tile-configuration table.
+//
+// MFMA rows: workgroup tile bm x bn, k-tile 16, wave tile wm x wn built from
+// 32x32 accumulator blocks. `wps` is how many waves of that kernel one SIMD
+// holds at once (a 128 x 128 wave tile keeps 256 accumulators plus its
+// operands, which fills the 512 registers a SIMD lane has, so one). `eff` is
+// the fraction of a SIMD's matrix-core peak one wave reaches when it has the
+// SIMD to itself; it only ranks the candidates.
+struct Entry {
+    fg_config cfg;
+    int variant;  // index inside the kernel family's launcher
+    int wps;      // resident waves per SIMD
+    double eff;   // relative efficiency for the cost model
+};
+
+constexpr int kNumCUs = 256;
+constexpr int kSimdsPerCU = 4;
+
+Entry make_entry(int id, fg_kind kind, int variant, int bm, int bn, int bk, int wm, int wn,
+                 int threads, int stages, int wps, double eff, const char* name) {
+    Entry e;
+    memset(&e, 0, sizeof e);
+    e.cfg.id = id;
+    e.cfg.kind = kind;
+    e.cfg.bm = bm;
+    e.cfg.bn = bn;
+    e.cfg.bk = bk;
+    e.cfg.wm = wm;
+    e.cfg.wn = wn;
+    e.cfg.threads = threads;
+    e.cfg.stages = stages;
+    e.cfg.lds_bytes = stages * (bm + bn) * bk * 4;
+    snprintf(e.cfg.name, sizeof e.cfg.name, "%s", name);
+    e.variant = variant;
+    e.wps = wps;
+    e.eff = eff;
+    return e;
+}
+
+const Entry* table() {
+    static const Entry t[] = {
+        make_entry(0, FG_KIND_MFMA, 0, 256, 256, 16, 128, 128, 256, 2, 1, 0.85, "mfma_256x256x16_w2x2"),
+        make_entry(1, FG_KIND_MFMA, 1, 256, 128, 16, 128, 128, 128, 2, 1, 0.80, "mfma_256x128x16_w2x1"),
+        make_entry(2, FG_KIND_MFMA, 2, 128, 128, 16, 128, 128, 64, 2, 1, 0.75, "mfma_128x128x16_w1x1"),
+        make_entry(3, FG_KIND_MFMA, 3, 64, 128, 16, 64, 128, 64, 2, 1, 0.55, "mfma_64x128x16_w1x1"),
+        make_entry(4, FG_KIND_MFMA, 4, 32, 128, 16, 32, 128, 64, 2, 2, 0.35, "mfma_32x128x16_w1x1"),
+        // VALU rows: wm x wn is the per-thread tile.
+        make_entry(5, FG_KIND_VALU, 0, 128, 128, 8, 8, 8, 256, 2, 2, 0.40, "valu_128x128x8_t8x8"),
+        make_entry(6, FG_KIND_VALU, 1, 64, 64, 8, 4, 4, 256, 2, 4, 0.25, "valu_64x64x8_t4x4"),
+    };
+    return t;
+}
+constexpr int kNumEntries = 7;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Estimated time (arbitrary units) of the call with MFMA entry e: the number
+// of rounds of resident waves times the time of one wave tile, which grows
+// with the number of waves sharing a SIMD.
+double cost(const Entry& e, int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = cdiv(M, e.cfg.bm) * cdiv(N, e.cfg.bn);
+    const int64_t waves = tiles * (e.cfg.threads / 64);
+    const int64_t simds = (int64_t)kNumCUs * kSimdsPerCU;
+    const int64_t rounds = cdiv(waves, simds * e.wps);
+    int64_t share = cdiv(waves, simds);
+    if (share > e.wps) share = e.wps;
+    const double kpad = (double)cdiv(K, e.cfg.bk) * e.cfg.bk;
+    return (double)rounds * e.cfg.wm * e.cfg.wn * kpad * (double)share / e.eff;
+}
+
+int select_entry(int64_t M, int64_t N, int64_t K) {
+    int best = -1;
+    double best_cost = 0;
+    for (int i = 0; i < kNumEntries; ++i) {
+        const Entry& e = table()[i];
+        if (e.cfg.kind != FG_KIND_MFMA) continue;
+        const double c = cost(e, M, N, K);
+        if (best < 0 || c < best_cost) {
+            best = i;
+            best_cost = c;
+        }
+    }
+    return best;
+}
+
+int group_m_override() {
+    static int v = [] {
+        const char* s = getenv("FG_GROUP_M");
+        return s ? atoi(s) : 0;
+    }();
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Device check: the kernels are built for gfx950 only.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+fg_status check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(FG_ERR_HIP, 0, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(FG_ERR_UNSUPPORTED, 0, "device index %d out of range", dev);
+    int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(FG_ERR_HIP, 0, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    if (st != 1)
+        return fail(FG_ERR_UNSUPPORTED, 0, "device %d is not gfx950", dev);
+    return FG_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validation shared by fg_sgemm_ex and fg_select_config.
+fg_status validate(fg_op ta, fg_op tb, int64_t M, int64_t N, int64_t K, float alpha,
+                   const float* A, int64_t lda, const float* B, int64_t ldb,
+                   const float* C, int64_t ldc, bool check_ptrs) {
+    if (ta != FG_OP_N && ta != FG_OP_T) return fail(FG_ERR_INVALID_ARG, 1, "transA must be N or T");
+    if (tb != FG_OP_N && tb != FG_OP_T) return fail(FG_ERR_INVALID_ARG, 2, "transB must be N or T");
+    if (M < 0) return fail(FG_ERR_INVALID_ARG, 3, "M < 0");
+    if (N < 0) return fail(FG_ERR_INVALID_ARG, 4, "N < 0");
+    if (K < 0) return fail(FG_ERR_INVALID_ARG, 5, "K < 0");
+    const int64_t min_lda = ta == FG_OP_N ? K : M;
+    const int64_t min_ldb = tb == FG_OP_N ? N : K;
+    if (lda < (min_lda > 1 ? min_lda : 1))
+        return fail(FG_ERR_INVALID_ARG, 8, "lda=%lld < %lld", (long long)lda, (long long)min_lda);
+    if (ldb < (min_ldb > 1 ? min_ldb : 1))
+        return fail(FG_ERR_INVALID_ARG, 10, "ldb=%lld < %lld", (long long)ldb, (long long)min_ldb);
+    if (ldc < (N > 1 ? N : 1))
+        return fail(FG_ERR_INVALID_ARG, 13, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+    if (check_ptrs) {
+        const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
+        if (reads_ab && !A) return fail(FG_ERR_INVALID_ARG, 7, "A is NULL");
+        if (reads_ab && !B) return fail(FG_ERR_INVALID_ARG, 9, "B is NULL");
+        if (M > 0 && N > 0 && !C) return fail(FG_ERR_INVALID_ARG, 12, "C is NULL");
+    }
+    // Limits of this implementation (valid BLAS arguments it cannot run).
+    const int64_t kMaxDim = 0x3FFFFFFF;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return fail(FG_ERR_UNSUPPORTED, 0, "dimension above %lld", (long long)kMaxDim);
+    if (lda > FG_MAX_LD || ldb > FG_MAX_LD || ldc > FG_MAX_LD)
+        return fail(FG_ERR_UNSUPPORTED, 0, "leading dimension above %d", FG_MAX_LD);
+    return FG_OK;
+}
+
+int32_t build_flags(const float* A, int64_t lda, const float* B, int64_t ldb, const float* C,
+                    int64_t ldc, float beta) {
+    int32_t f = fg::FLAG_XCD_REMAP;
+    if (aligned16(A) && lda % 4 == 0) f |= fg::FLAG_VEC_A;
+    if (aligned16(B) && ldb % 4 == 0) f |= fg::FLAG_VEC_B;
+    if (aligned16(C) && ldc % 4 == 0) f |= fg::FLAG_VEC_C;
+    if (beta == 0.0f) f |= fg::FLAG_BETA0;
+    return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fg_abi_version(void) { return 1; }
+
+int32_t fg_last_bad_arg(void) { return t_bad_arg; }
+
+const char* fg_last_error(void) { return t_error; }
+
+const char* fg_status_string(fg_status s) {
+    switch (s) {
+        case FG_OK: return "FG_OK";
+        case FG_ERR_INVALID_ARG: return "FG_ERR_INVALID_ARG";
+        case FG_ERR_HIP: return "FG_ERR_HIP";
+        case FG_ERR_UNSUPPORTED: return "FG_ERR_UNSUPPORTED";
+        default: return "FG_UNKNOWN_STATUS";
+    }
+}
+
+int32_t fg_num_configs(void) { return kNumEntries; }
+
+fg_status fg_get_config(int32_t id, fg_config* out) {
+    clear_error();
+    if (id < 0 || id >= kNumEntries) return fail(FG_ERR_INVALID_ARG, 1, "config id %d out of range", id);
+    if (!out) return fail(FG_ERR_INVALID_ARG, 2, "out is NULL");
+    *out = table()[id].cfg;
+    return FG_OK;
+}
+
+fg_status fg_select_config(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                           const float* A, int64_t lda, const float* B, int64_t ldb,
+                           const float* C, int64_t ldc, fg_config* out) {
+    clear_error();
+    fg_status s = validate(transA, transB, M, N, K, 1.0f, A, lda, B, ldb, C, ldc, false);
+    if (s != FG_OK) return s;
+    if (!out) return fail(FG_ERR_INVALID_ARG, 12, "out is NULL");
+    *out = table()[select_entry(M, N, K)].cfg;
+    return FG_OK;
+}
+
+fg_status fg_sgemm_ex(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, float alpha,
+                      const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                      float* C, int64_t ldc, hipStream_t stream, int32_t config_id) {
+    clear_error();
+    fg_status s = validate(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
+    if (s != FG_OK) return s;
+    if (config_id < -1 || config_id >= kNumEntries)
+        return fail(FG_ERR_INVALID_ARG, 15, "config id %d out of range", config_id);
+
+    // Quick returns.
+    if (M == 0 || N == 0) return FG_OK;
+    const bool no_product = (K == 0 || alpha == 0.0f);
+    if (no_product && beta == 1.0f) return FG_OK;
+
+    s = check_device();
+    if (s != FG_OK) return s;
+
+    fg::GemmParams p;
+    memset(&p, 0, sizeof p);
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.M = (int32_t)M;
+    p.N = (int32_t)N;
+    p.K = (int32_t)K;
+    p.lda = (int32_t)lda;
+    p.ldb = (int32_t)ldb;
+    p.ldc = (int32_t)ldc;
+    p.alpha = alpha;
+    p.beta = beta;
+    // Extent of each stored matrix: rows * ld, minus the unused tail of the last row.
+    const int64_t a_rows = transA == FG_OP_N ? M : K, a_cols = transA == FG_OP_N ? K : M;
+    const int64_t b_rows = transB == FG_OP_N ? K : N, b_cols = transB == FG_OP_N ? N : K;
+    p.a_extent = a_rows > 0 && a_cols > 0 ? (a_rows - 1) * lda + a_cols : 0;
+    p.b_extent = b_rows > 0 && b_cols > 0 ? (b_rows - 1) * ldb + b_cols : 0;
+    p.c_extent = (M - 1) * ldc + N;
+    p.flags = build_flags(A, lda, B, ldb, C, ldc, beta);
+
+    hipError_t e;
+    if (no_product) {
+        e = fg::launch_scale(p, stream);
+    } else {
+        const int idx = config_id >= 0 ? config_id : select_entry(M, N, K);
+        const Entry& en = table()[idx];
+        p.tiles_m = (int32_t)cdiv(M, en.cfg.bm);
+        p.tiles_n = (int32_t)cdiv(N, en.cfg.bn);
+        const int64_t nblocks = (int64_t)p.tiles_m * p.tiles_n;
+        if (nblocks > 0x7FFFFFFF) return fail(FG_ERR_UNSUPPORTED, 0, "too many tiles");
+        p.group_m = group_m_override() > 0 ? group_m_override() : 4;
+        if (p.group_m > p.tiles_m) p.group_m = p.tiles_m;
+        if (en.cfg.kind == FG_KIND_MFMA)
+            e = fg::launch_mfma(en.variant, transA, transB, p, stream);
+        else
+            e = fg::launch_valu(en.variant, transA, transB, p, stream);
+    }
+    if (e != hipSuccess) return fail(FG_ERR_HIP, 0, "kernel launch: %s", hipGetErrorString(e));
+    return FG_OK;
+}
+
+fg_status fg_sgemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, float alpha,
+                   const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                   float* C, int64_t ldc, hipStream_t stream) {
+    return fg_sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1);
+}
+
+}  // extern "C"

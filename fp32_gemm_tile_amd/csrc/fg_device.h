@@ -1,0 +1,86 @@
+// Device-side helpers shared by the GEMM kernels: buffer resources, guarded
+// loads/stores, and the workgroup-to-tile mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fg_kernels.h"
+
+namespace fg {
+
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs (32-bit data format,
+// no swizzle, no stride).
+constexpr int32_t kBufferWord3 = 0x00020000;
+
+// A raw buffer over [base, base + records_bytes). Loads whose byte offset is
+// at or past the end return 0 and stores there are dropped by the hardware;
+// the kernels still predicate every access themselves, so this is only a
+// safety net that keeps any index error inside the caller's matrix.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base,
+                                                            int64_t extent_floats) {
+    int64_t bytes = extent_floats * 4;
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0xFFFFFFFFll) bytes = 0xFFFFFFFFll;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0,
+                                             (int)(uint32_t)bytes, kBufferWord3);
+}
+
+__device__ __forceinline__ f4 ld4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+__device__ __forceinline__ float ld1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ void st4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void st1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
+}
+
+// Four consecutive floats starting at element `e` of a row whose valid length
+// is `len` (elements at or past `len` read as 0). `off` is the byte offset of
+// element e. vec: the row start and e are 16-byte aligned, so a 128-bit load
+// is allowed when all four are in range.
+__device__ __forceinline__ f4 ld4_guard(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                        int e, int len, bool vec) {
+    f4 v = {0.f, 0.f, 0.f, 0.f};
+    if (vec && e + 3 < len) return ld4(r, off);
+    if (e + 0 < len) v[0] = ld1(r, off);
+    if (e + 1 < len) v[1] = ld1(r, off + 4);
+    if (e + 2 < len) v[2] = ld1(r, off + 8);
+    if (e + 3 < len) v[3] = ld1(r, off + 12);
+    return v;
+}
+
+// Workgroup id -> (tile_m, tile_n).
+//
+// 1. XCD remap: consecutive workgroup ids are handed to the 8 XCDs in turn,
+//    and each XCD has its own L2. Renumbering so that XCD x receives the
+//    contiguous range [x*G/8, (x+1)*G/8) makes the tiles that run together on
+//    one XCD neighbours in the order below, so they share operand panels in
+//    that XCD's L2.
+// 2. Grouped raster order: tiles are visited in bands of `group_m` tile rows,
+//    column by column inside a band, so that a run of consecutive ids covers
+//    a compact block of C (few distinct A row-panels and B column-panels).
+__device__ __forceinline__ void map_tile(int bid, int nblocks, const GemmParams& p,
+                                         int& tm, int& tn) {
+    int L = bid;
+    if ((p.flags & FLAG_XCD_REMAP) && (nblocks % 8) == 0)
+        L = (bid % 8) * (nblocks / 8) + bid / 8;
+    const int per_group = p.group_m * p.tiles_n;
+    const int g = L / per_group;
+    const int first_m = g * p.group_m;
+    int gm = p.tiles_m - first_m;
+    if (gm > p.group_m) gm = p.group_m;
+    const int r = L - g * per_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
+}  // namespace fg

@@ -1,0 +1,45 @@
+// Internal interface between the host dispatcher (fg_api.cpp) and the
+// kernel translation units. Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fg {
+
+// Everything a GEMM kernel needs, passed by value as the kernel argument.
+// Element counts and leading dimensions are in floats.
+struct GemmParams {
+    const float* A;
+    const float* B;
+    float* C;
+    int32_t M, N, K;
+    int32_t lda, ldb, ldc;
+    float alpha, beta;
+    int64_t a_extent;  // floats from A to one past the last element read
+    int64_t b_extent;
+    int64_t c_extent;
+    int32_t tiles_m, tiles_n;
+    int32_t group_m;   // tile rows per raster group
+    int32_t flags;     // FLAG_* below
+};
+
+enum : int32_t {
+    FLAG_VEC_A = 1,    // A rows start 16-byte aligned: 128-bit loads allowed
+    FLAG_VEC_B = 2,
+    FLAG_VEC_C = 4,    // C rows start 16-byte aligned: 128-bit loads/stores
+    FLAG_BETA0 = 8,    // beta == 0: C is written, never read
+    FLAG_XCD_REMAP = 16,  // remap workgroup ids so each XCD gets a contiguous tile range
+};
+
+// Launchers: enqueue one kernel on `stream`; return the HIP launch status.
+// `variant` indexes the kernel's compile-time tile shape (see the table in
+// fg_api.cpp); trans_a / trans_b select the operand layouts.
+hipError_t launch_mfma(int variant, int trans_a, int trans_b, const GemmParams& p,
+                       hipStream_t stream);
+hipError_t launch_valu(int variant, int trans_a, int trans_b, const GemmParams& p,
+                       hipStream_t stream);
+// C = beta * C (beta == 0: C = 0 without reading it); for K == 0 or alpha == 0.
+hipError_t launch_scale(const GemmParams& p, hipStream_t stream);
+
+}  // namespace fg

@@ -1,0 +1,157 @@
+/*
+ * fp32gemm -- true-fp32 GEMM for AMD Instinct MI355X (gfx950).
+ *
+ *     C = alpha * op(A) * op(B) + beta * C
+ *
+ * Operation: the general matrix multiply as defined in "Optimising fp32 GEMM
+ * on A100", section "What is GEMM?" (A is M x K, B is K x N, C is M x N,
+ * alpha and beta scalars), with the BLAS-style argument list of "CuTe-ly
+ * writing an SM86 SGEMM", section "host-side setup" (m, n, k, alpha, A, ldA,
+ * B, ldB, beta, C, ldC, stream), extended by the two transpose flags.
+ *
+ * Arithmetic: binary32 inputs, binary32 products and accumulation on the
+ * matrix cores (v_mfma_f32_32x32x2_f32) or on the vector ALU, binary32
+ * output. Nothing is converted to a narrower format.
+ *
+ * Storage convention: ROW-MAJOR with explicit leading dimensions (elements).
+ *   op(A)(i,k) = A[i*lda + k]  when transA == FG_OP_N  (A stored M x K, lda >= K)
+ *   op(A)(i,k) = A[k*lda + i]  when transA == FG_OP_T  (A stored K x M, lda >= M)
+ *   op(B)(k,j) = B[k*ldb + j]  when transB == FG_OP_N  (B stored K x N, ldb >= N)
+ *   op(B)(k,j) = B[j*ldb + k]  when transB == FG_OP_T  (B stored N x K, ldb >= K)
+ *   C(i,j)     = C[i*ldc + j]                          (ldc >= N)
+ * A column-major caller computes C^T = op(B)^T op(A)^T by swapping the
+ * operands (and M with N).
+ *
+ * Ownership: the caller owns every buffer. A, B and C are device pointers
+ * (e.g. from hipMalloc or a framework's allocator). The library allocates,
+ * frees and copies nothing and keeps no workspace. C must not overlap A or B.
+ *
+ * Streams: work is enqueued on `stream` (NULL = the null stream) and the call
+ * returns without synchronising; C is complete once the stream reaches that
+ * point. The library holds no per-stream state; calls are thread-safe.
+ *
+ * Errors: no exception or abort crosses this boundary. Invalid arguments are
+ * reported before any GPU work is enqueued, and fg_last_bad_arg() then gives
+ * the 1-based position of the first bad argument (BLAS numbering below).
+ * fg_last_error() gives a message for the last failure on the calling thread.
+ */
+#ifndef FP32GEMM_H
+#define FP32GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same opaque type as HIP's hipStream_t, so HIP callers can pass theirs. */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum fg_op { FG_OP_N = 0, FG_OP_T = 1 } fg_op;
+
+typedef enum fg_status {
+    FG_OK = 0,
+    FG_ERR_INVALID_ARG = 1, /* an argument is out of its domain; nothing enqueued */
+    FG_ERR_HIP = 2,         /* the HIP runtime reported an error (launch, device query) */
+    FG_ERR_UNSUPPORTED = 3  /* valid BLAS arguments this build cannot run, e.g. a
+                               device that is not gfx950 or a leading dimension
+                               above FG_MAX_LD */
+} fg_status;
+
+/* Kernel families. */
+typedef enum fg_kind {
+    FG_KIND_MFMA = 1, /* matrix-core contraction, v_mfma_f32_32x32x2_f32 */
+    FG_KIND_VALU = 2  /* vector-ALU v_fma_f32 outer products (comparison path) */
+} fg_kind;
+
+/* Largest leading dimension (elements) the kernels address with 32-bit
+ * offsets. Larger values return FG_ERR_UNSUPPORTED. */
+#define FG_MAX_LD 2097152
+
+/* One entry of the tile-configuration table. */
+typedef struct fg_config {
+    int32_t id;        /* position in the table (0 .. fg_num_configs()-1) */
+    int32_t kind;      /* fg_kind */
+    int32_t bm, bn;    /* output tile of one workgroup */
+    int32_t bk;        /* depth of one k-tile staged in LDS */
+    int32_t wm, wn;    /* output tile of one wavefront (MFMA) or thread (VALU) */
+    int32_t threads;   /* work-items per workgroup */
+    int32_t stages;    /* LDS buffers in the k-tile ring */
+    int32_t lds_bytes; /* LDS per workgroup */
+    char name[40];
+} fg_config;
+
+/*
+ * fg_sgemm: C = alpha * op(A) * op(B) + beta * C on `stream`.
+ *
+ * Arguments (BLAS positions used by fg_last_bad_arg):
+ *   1 transA, 2 transB : FG_OP_N or FG_OP_T
+ *   3 M, 4 N, 5 K      : >= 0
+ *   6 alpha
+ *   7 A, 8 lda         : lda >= max(1, transA == FG_OP_N ? K : M)
+ *   9 B, 10 ldb        : ldb >= max(1, transB == FG_OP_N ? N : K)
+ *   11 beta
+ *   12 C, 13 ldc       : ldc >= max(1, N)
+ *   14 stream
+ * A and B must be non-NULL when M, N and K are all > 0 and alpha != 0;
+ * C must be non-NULL when M and N are > 0.
+ *
+ * Quick returns (BLAS convention; no kernel reads A or B):
+ *   M == 0 or N == 0                       -> FG_OK, nothing enqueued
+ *   (K == 0 or alpha == 0) and beta == 1   -> FG_OK, nothing enqueued
+ *   (K == 0 or alpha == 0) otherwise       -> C = beta * C
+ * When beta == 0, C is not read: NaN or Inf in C does not reach the result.
+ */
+fg_status fg_sgemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                   float alpha, const float* A, int64_t lda,
+                   const float* B, int64_t ldb, float beta,
+                   float* C, int64_t ldc, hipStream_t stream);
+
+/*
+ * fg_sgemm_ex: fg_sgemm with the tile configuration forced.
+ * config_id = -1 selects automatically (same as fg_sgemm); otherwise it must
+ * be a valid table index (else FG_ERR_INVALID_ARG, bad argument 15).
+ */
+fg_status fg_sgemm_ex(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                      float alpha, const float* A, int64_t lda,
+                      const float* B, int64_t ldb, float beta,
+                      float* C, int64_t ldc, hipStream_t stream,
+                      int32_t config_id);
+
+/* Size of the tile-configuration table. Host only; no GPU needed. */
+int32_t fg_num_configs(void);
+
+/* Copy table entry `id` to *out. FG_ERR_INVALID_ARG if id is out of range or
+ * out is NULL. Host only. */
+fg_status fg_get_config(int32_t id, fg_config* out);
+
+/*
+ * The configuration fg_sgemm would use for this call (shape, layouts and the
+ * 16-byte alignment of the pointers and leading dimensions), without
+ * launching anything. Pointers are only inspected, never dereferenced; they
+ * may be NULL (then treated as 16-byte aligned). Same validation as fg_sgemm.
+ * Host only.
+ */
+fg_status fg_select_config(fg_op transA, fg_op transB, int64_t M, int64_t N,
+                           int64_t K, const float* A, int64_t lda,
+                           const float* B, int64_t ldb, const float* C,
+                           int64_t ldc, fg_config* out);
+
+/* 1-based BLAS position of the first invalid argument of the last failing
+ * call on this thread, or 0. */
+int32_t fg_last_bad_arg(void);
+
+/* Message for the last failure on this thread ("" if none). */
+const char* fg_last_error(void);
+
+/* Static name of a status code. */
+const char* fg_status_string(fg_status status);
+
+/* Version of this interface (incremented on incompatible changes). */
+int32_t fg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP32GEMM_H */

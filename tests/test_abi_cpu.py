@@ -1,0 +1,117 @@
+"""The C-ABI library on the host: it loads, exports what the header declares,
+validates arguments and takes the quick returns without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp32_gemm_tile_amd as fg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp32gemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fg_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fg.load_library()
+    names = declared_functions()
+    assert "fg_sgemm" in names and "fg_sgemm_ex" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+
+
+def test_abi_version_and_status_strings():
+    assert fg.fg_abi_version() == 1
+    assert fg.fg_status_string(0) == "FG_OK"
+    assert fg.fg_status_string(1) == "FG_ERR_INVALID_ARG"
+    assert fg.fg_status_string(2) == "FG_ERR_HIP"
+    assert fg.fg_status_string(3) == "FG_ERR_UNSUPPORTED"
+
+
+def _call(ta=0, tb=0, M=4, N=4, K=4, alpha=1.0, A=16, lda=None, B=16, ldb=None,
+          beta=0.0, C=16, ldc=None, cfg=-1):
+    lda = lda if lda is not None else max(1, K if ta == 0 else M)
+    ldb = ldb if ldb is not None else max(1, N if tb == 0 else K)
+    ldc = ldc if ldc is not None else max(1, N)
+    return fg.fg_sgemm_ex(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, 0, cfg)
+
+
+@pytest.mark.parametrize("kw,bad", [
+    (dict(ta=2), 1), (dict(tb=-1), 2), (dict(M=-1), 3), (dict(N=-1), 4), (dict(K=-1), 5),
+    (dict(lda=3), 8), (dict(ta=1, M=6, lda=5), 8), (dict(ldb=3), 10),
+    (dict(tb=1, K=7, ldb=6), 10), (dict(ldc=3), 13), (dict(A=0), 7), (dict(B=0), 9),
+    (dict(C=0), 12), (dict(cfg=99), 15), (dict(cfg=-2), 15),
+    (dict(M=0, lda=0), 8), (dict(N=0, ldc=0), 13),
+])
+def test_invalid_arguments_are_rejected_before_any_gpu_work(kw, bad):
+    st = _call(**kw)
+    assert st == fg.FG_ERR_INVALID_ARG
+    assert fg.fg_last_bad_arg() == bad
+    assert fg.fg_last_error()
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=0), dict(N=0), dict(M=0, N=0, K=0, C=0),
+    dict(K=0, beta=1.0, A=0, B=0), dict(alpha=0.0, beta=1.0, A=0, B=0),
+    dict(M=0, A=0, B=0, C=0),
+])
+def test_quick_returns_need_no_gpu(kw):
+    # These must succeed without launching (there is no GPU here).
+    assert _call(**kw) == fg.FG_OK
+    assert fg.fg_last_bad_arg() == 0
+
+
+def test_unsupported_leading_dimension():
+    st = _call(lda=fg.FG_MAX_LD + 4)
+    assert st == fg.FG_ERR_UNSUPPORTED
+
+
+def test_config_table():
+    n = fg.fg_num_configs()
+    assert n >= 2
+    cfgs = fg.configs()
+    assert [c["id"] for c in cfgs] == list(range(n))
+    kinds = {c["kind"] for c in cfgs}
+    assert kinds == {fg.FG_KIND_MFMA, fg.FG_KIND_VALU}
+    for c in cfgs:
+        assert c["bm"] > 0 and c["bn"] > 0 and c["bk"] > 0 and c["threads"] % 64 == 0
+        assert c["lds_bytes"] <= 160 * 1024
+        if c["kind"] == fg.FG_KIND_MFMA:
+            assert c["wm"] % 32 == 0 and c["wn"] % 32 == 0
+            assert (c["bm"] // c["wm"]) * (c["bn"] // c["wn"]) * 64 == c["threads"]
+    with pytest.raises(fg.FgError):
+        fg.fg_get_config(n)
+
+
+def test_selection_is_mfma_and_scales_with_shape():
+    big = fg.fg_select_config("N", "N", 8192, 8192, 8192)
+    assert big["kind"] == fg.FG_KIND_MFMA and big["bm"] * big["bn"] >= 256 * 128
+    small = fg.fg_select_config("N", "N", 256, 256, 256)
+    assert small["kind"] == fg.FG_KIND_MFMA
+    assert small["bm"] * small["bn"] < big["bm"] * big["bn"]
+    ragged = fg.fg_select_config("T", "N", 3001, 2047, 1025, lda=3001, ldb=2047, ldc=2047)
+    assert ragged["kind"] == fg.FG_KIND_MFMA
+    with pytest.raises(fg.FgError) as e:
+        fg.fg_select_config("N", "N", 4, 4, 4, lda=2)
+    assert e.value.bad_arg == 8
+
+
+def test_header_is_plain_c():
+    """The header compiles as C99 with no HIP or torch headers."""
+    import shutil
+    import subprocess
+    import tempfile
+    if shutil.which("gcc") is None:
+        pytest.skip("needs gcc")
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        with open(src, "w") as f:
+            f.write('#include "fp32gemm.h"\nint main(void){return fg_abi_version()==0;}\n')
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
+                        "-I", os.path.dirname(HEADER), src], check=True)

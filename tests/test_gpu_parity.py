@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerance (stated acceptance bound): per element
+|C - C_ref| <= 8*max(K,1)*2^-24*(|alpha|*S + |beta|*|C_in|) + 1e-6 with
+S = sum_k |a_ik b_kj|, and relative Frobenius error <= 1e-5. Integer-valued
+inputs must match bit for bit (every partial sum is exact in binary32).
+"""
+import numpy as np
+import pytest
+
+import fp32_gemm_tile_amd as fg
+from fp32_gemm_tile_amd import workloads as wl
+import oracle
+
+from gpu_util import check_full, check_sampled, log, run_fg
+
+pytestmark = pytest.mark.gpu
+
+OPS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fg.load_library()
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def _configs():
+    try:
+        return fg.configs()
+    except OSError:  # library missing: the tests below then fail loudly
+        return [{"id": i, "kind": fg.FG_KIND_MFMA} for i in range(7)]
+
+
+def mfma_ids():
+    return [c["id"] for c in _configs() if c["kind"] == fg.FG_KIND_MFMA]
+
+
+def all_ids():
+    return [c["id"] for c in _configs()]
+
+
+# --- the workloads the metric and the parity cases are quoted on ----------
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3"])
+def test_workload_full_oracle(name):
+    w = wl.WORKLOADS[name]
+    A, B, C = wl.make_inputs(w)
+    out, _ = run_fg(w, A, B, C)
+    info = check_full(w, A, B, C, out)
+    log(f"  {name}: max err/tol {info['max_err_over_tol']:.3g}, frob_rel {info.get('frob_rel')}")
+
+
+@pytest.mark.parametrize("name", ["C4", "C5a", "C5b", "C6"])
+def test_workload_sampled_oracle(name):
+    w = wl.WORKLOADS[name]
+    A, B, C = wl.make_inputs(w)
+    out, _ = run_fg(w, A, B, C)
+    assert np.all(np.isfinite(out))
+    info = check_sampled(w, A, B, C, out)
+    log(f"  {name}: sampled max err/tol {info['max_err_over_tol']:.3g}")
+
+
+# --- exactness on integer-valued inputs: catches layout/predication bugs ---
+
+@pytest.mark.parametrize("cfg", all_ids())
+@pytest.mark.parametrize("ta,tb", OPS)
+def test_integer_bit_exact_every_config(cfg, ta, tb):
+    rng_shapes = [(97, 131, 45), (256, 128, 32), (33, 257, 17), (1, 1, 1), (300, 5, 70)]
+    for (M, N, K) in rng_shapes:
+        for alpha, beta in [(1.0, 0.0), (-1.0, 2.0), (0.5, -1.0)]:
+            w = wl.custom(M, N, K, ta, tb, alpha, beta, dist="int8", seed=M + N + K)
+            A, B, C = wl.make_inputs(w)
+            out, _ = run_fg(w, A, B, C, config=cfg)
+            cref, _ = oracle.gemm(ta, tb, M, N, K, alpha, A, w.LDA, B, w.LDB, beta, C, w.LDC)
+            bad = np.argwhere(out.astype(np.float64) != cref)
+            assert bad.size == 0, (cfg, ta, tb, M, N, K, alpha, beta, bad[:5].tolist(),
+                                   [(out[i, j], cref[i, j]) for i, j in bad[:3]])
+
+
+@pytest.mark.parametrize("cfg", mfma_ids())
+def test_identity_and_one_hot_layout(cfg):
+    """A = I gives C = B exactly and B = I gives C = A exactly: any mix-up of
+    rows, columns or k inside the kernel shows as a misplaced value."""
+    rng = np.random.default_rng(1)
+    for ta, tb in OPS:
+        n = 160
+        B = rng.standard_normal((n, 96)).astype(np.float32)
+        w = wl.custom(n, 96, n, ta, tb)
+        I = np.eye(n, dtype=np.float32)
+        Bs = B.T.copy() if tb == "T" else B
+        out, _ = run_fg(w, I, Bs, config=cfg)
+        assert np.array_equal(out, B), (cfg, ta, tb)
+        A = rng.standard_normal((96, n)).astype(np.float32)
+        w2 = wl.custom(96, n, n, ta, tb)
+        As = A.T.copy() if ta == "T" else A
+        out, _ = run_fg(w2, As, I, config=cfg)
+        assert np.array_equal(out, A), (cfg, ta, tb)
+
+
+# --- ragged shapes, odd leading dimensions, misaligned bases ---------------
+
+RAGGED = [(1, 1, 1), (7, 5, 3), (33, 65, 17), (129, 257, 31), (255, 129, 16),
+          (300, 200, 100), (513, 97, 1025)]
+
+
+@pytest.mark.parametrize("cfg", all_ids())
+@pytest.mark.parametrize("ta,tb", OPS)
+def test_ragged_float_every_config(cfg, ta, tb):
+    for i, (M, N, K) in enumerate(RAGGED):
+        w = wl.custom(M, N, K, ta, tb, alpha=1.25, beta=-0.5, dist="normal", seed=i)
+        A, B, C = wl.make_inputs(w)
+        out, _ = run_fg(w, A, B, C, config=cfg)
+        check_full(w, A, B, C, out)
+
+
+@pytest.mark.parametrize("ta,tb", OPS)
+def test_padded_and_misaligned(ta, tb):
+    """Leading dimensions larger than the rows (odd and multiple-of-4) and
+    base pointers 1 float off 16-byte alignment; the padding of C is a guard
+    band that must stay untouched."""
+    for (M, N, K, pad, off) in [(130, 70, 50, 3, (1, 2, 3)), (128, 128, 64, 4, (0, 0, 0)),
+                                (64, 256, 33, 5, (3, 0, 1))]:
+        w0 = wl.custom(M, N, K, ta, tb)
+        w = wl.custom(M, N, K, ta, tb, alpha=0.75, beta=1.5, dist="normal", seed=M,
+                      lda=w0.LDA + pad, ldb=w0.LDB + pad, ldc=w0.LDC + pad)
+        A, B, C = wl.make_inputs(w)
+        C[:, N:] = 12345.0  # guard band
+        out, full = run_fg(w, A, B, C, offsets=off)
+        check_full(w, A, B, C, out)
+        assert np.all(full[:, N:] == 12345.0), "C padding was written"
+
+
+def test_guard_rows_outside_c():
+    """Nothing is written past the last row of C (the buffer continues)."""
+    import torch
+    M, N, K = 100, 96, 40
+    w = wl.custom(M, N, K, dist="normal", seed=3)
+    A, B, _ = wl.make_inputs(w)
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    buf = torch.full((M + 8, N), 777.0, device="cuda")
+    st = fg.fg_sgemm("N", "N", M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0,
+                     buf.data_ptr(), N, 0)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.all(buf[M:] == 777.0)
+
+
+# --- semantics --------------------------------------------------------------
+
+def test_beta_zero_ignores_nan_in_c():
+    w = wl.custom(200, 300, 64, alpha=2.0, beta=0.0, seed=4)
+    A, B, _ = wl.make_inputs(w)
+    C = np.full((w.M, w.LDC), np.nan, dtype=np.float32)
+    out, _ = run_fg(w, A, B, C)
+    assert np.all(np.isfinite(out))
+    check_full(w, A, B, None, out)
+
+
+def test_nan_in_a_row_propagates():
+    w = wl.custom(64, 64, 64, seed=5)
+    A, B, _ = wl.make_inputs(w)
+    A[7, 3] = np.nan
+    out, _ = run_fg(w, A, B)
+    assert np.all(np.isnan(out[7])) and np.all(np.isfinite(np.delete(out, 7, axis=0)))
+
+
+@pytest.mark.parametrize("alpha,beta,K", [(0.0, 0.5, 32), (1.0, -2.0, 0), (0.0, 0.0, 16),
+                                          (1.0, 0.0, 0), (0.0, 1.0, 8)])
+def test_scale_only_paths(alpha, beta, K):
+    """K == 0 or alpha == 0: C = beta*C, A and B never read (NaN there is fine)."""
+    M, N = 50, 70
+    w = wl.custom(M, N, K, alpha=alpha, beta=beta, dist="normal", seed=6)
+    A = np.full((M, max(K, 1)), np.nan, dtype=np.float32)
+    B = np.full((max(K, 1), N), np.nan, dtype=np.float32)
+    C = np.random.default_rng(0).standard_normal((M, N)).astype(np.float32)
+    out, _ = run_fg(w, A, B, C.copy())
+    want = C if beta == 1.0 else (np.zeros_like(C) if beta == 0 else (beta * C.astype(np.float64)).astype(np.float32))
+    assert np.array_equal(out, want)
+
+
+def test_repeat_runs_bit_identical():
+    w = wl.WORKLOADS["C2"]
+    A, B, _ = wl.make_inputs(w)
+    o1, _ = run_fg(w, A, B)
+    o2, _ = run_fg(w, A, B)
+    assert np.array_equal(o1, o2)
+
+
+def test_runs_on_caller_stream():
+    import torch
+    s = torch.cuda.Stream()
+    w = wl.custom(512, 384, 256, dist="normal", seed=8)
+    A, B, _ = wl.make_inputs(w)
+    with torch.cuda.stream(s):
+        out, _ = run_fg(w, A, B, stream=s)
+    check_full(w, A, B, None, out)
+
+
+def test_torch_convenience_wrapper():
+    import torch
+    g = torch.Generator().manual_seed(0)
+    A = torch.randn(300, 200, generator=g)
+    B = torch.randn(200, 100, generator=g)
+    C = torch.zeros(300, 100, device="cuda")
+    fg.sgemm(A.cuda(), B.cuda(), C)
+    torch.cuda.synchronize()
+    cref, s = oracle.gemm("N", "N", 300, 100, 200, 1.0, A.numpy(), 200, B.numpy(), 100, 0.0)
+    ok, info = oracle.compare.check(C.cpu().numpy(), cref, s, 200)
+    assert ok, info
+    # a transposed view goes through transA = T on the same storage
+    At = A.t().contiguous().cuda()  # 200 x 300 storage of A^T
+    C2 = torch.zeros(300, 100, device="cuda")
+    fg.sgemm(At, B.cuda(), C2, transA="T")
+    torch.cuda.synchronize()
+    ok, info = oracle.compare.check(C2.cpu().numpy(), cref, s, 200)
+    assert ok, info
+    with pytest.raises(fg.FgError):
+        fg.sgemm(A.cuda(), B.cuda(), C, config=1000)
+
+
+def test_error_statistics_are_fp32_scale():
+    """For uniform[-1,1) inputs the relative Frobenius error should be at
+    binary32 rounding scale (~sqrt(K)*2^-24), far inside 1e-5; a precision
+    downcast anywhere would show up as ~1e-3."""
+    w = wl.custom(1024, 1024, 2048, seed=9)
+    A, B, _ = wl.make_inputs(w)
+    out, _ = run_fg(w, A, B)
+    info = check_full(w, A, B, None, out)
+    assert info["frob_rel"] < 2e-6, info
