@@ -61,6 +61,14 @@ def load_library(path: str = LIB_PATH):
         raise ImportError(
             f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
             " (there is no non-HIP fallback)")
+    # One HIP runtime per process: PyTorch ships its own libamdhip64 (same
+    # SONAME as the system one). Importing torch first makes the dynamic
+    # loader bind this library to that copy, so torch's streams and device
+    # pointers are the ones the library's runtime knows.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
     gemm_args = [i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, vp]

@@ -115,3 +115,13 @@ def test_header_is_plain_c():
             f.write('#include "fp32gemm.h"\nint main(void){return fg_abi_version()==0;}\n')
         subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
                         "-I", os.path.dirname(HEADER), src], check=True)
+
+
+def test_single_hip_runtime_in_process():
+    """The library must bind to the HIP runtime torch already loaded (two
+    runtimes in one process do not share streams)."""
+    pytest.importorskip("torch")
+    fg.load_library()
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {l.split()[-1] for l in maps if "libamdhip64" in l}
+    assert len(hip) == 1, hip
