@@ -118,6 +118,19 @@ def cpu_baseline(w, target_s=15.0):
             "sample": f"{rows} of {w.M} output rows of {w.name} (binary64 oracle), {dt:.1f} s"}
 
 
+def copy_probe(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size: it reads and writes
+    nbytes each, the reference for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy_probe: {reps} copies of {nbytes} bytes", file=sys.stderr, flush=True)
+
+
 def run_one(name, steps, warmup, with_cpu, config=-1):
     from fp32_gemm_tile_amd import workloads as wl
     w = wl.WORKLOADS[name]
@@ -162,6 +175,11 @@ def main():
     ap.add_argument("--suite", action="store_true",
                     help="one line per workload C1..C6 (no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run a plain device copy of 1 GiB three times "
+                         "(reference for scaling HBM traffic counters)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="time every table entry on every workload (one line each)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -176,10 +194,15 @@ def main():
     import fp32_gemm_tile_amd as fg
     fg.load_library()
 
-    if args.suite:
+    if args.suite or args.calibrate:
+        ids = range(fg.fg_num_configs()) if args.calibrate else [args.config]
         for name in ("C1", "C2", "C3", "C4", "C5a", "C5b", "C6"):
-            r = run_one(name, args.steps, args.warmup, False, args.config)
-            print(json.dumps(r), flush=True)
+            for cid in ids:
+                r = run_one(name, args.steps, args.warmup, False, cid)
+                print(json.dumps({"workload": name, "config": r["config"]["kernel_config"],
+                                  "forced": cid, "tflops": r["value"],
+                                  "ms": r["ms_per_step"], "pct": r["pct_of_fp32_peak"]}),
+                      flush=True)
         return
 
     r = run_one(args.workload, args.steps, args.warmup, False, args.config)
@@ -192,6 +215,8 @@ def main():
     if not args.no_cpu:
         from fp32_gemm_tile_amd import workloads as wl
         r["cpu_baseline"] = cpu_baseline(wl.WORKLOADS[args.workload])
+    if args.copy_probe:
+        copy_probe()
     print(json.dumps(r), flush=True)
 
 

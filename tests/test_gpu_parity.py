@@ -234,3 +234,14 @@ def test_error_statistics_are_fp32_scale():
     out, _ = run_fg(w, A, B)
     info = check_full(w, A, B, None, out)
     assert info["frob_rel"] < 2e-6, info
+
+
+@pytest.mark.parametrize("cfg", all_ids())
+def test_every_config_at_4096_cubed_sampled(cfg):
+    """Every table entry, forced, on the 4096^3 workload (sampled oracle):
+    the comparison paths must compute the whole product too."""
+    w = wl.WORKLOADS["C6"]
+    A, B, C = wl.make_inputs(w)
+    out, _ = run_fg(w, A, B, C, config=cfg)
+    assert np.all(np.isfinite(out))
+    check_sampled(w, A, B, C, out, n=3000, seed=cfg, rows=(0, 4095, 2049))
