@@ -52,16 +52,19 @@ void clear_error() {
 // SIMD to itself; it only ranks the candidates.
 struct Entry {
     fg_config cfg;
-    int variant;  // index inside the kernel family's launcher
-    int wps;      // resident waves per SIMD
-    double eff;   // relative efficiency for the cost model
+    int variant;   // index inside the kernel family's launcher
+    int wps;       // resident waves per SIMD
+    double eff;    // relative efficiency for the cost model
+    int fallback;  // entry used instead when A or B rows are not 16-byte
+                   // aligned (direct-to-LDS entries only; -1 = none needed)
 };
 
 constexpr int kNumCUs = 256;
 constexpr int kSimdsPerCU = 4;
 
 Entry make_entry(int id, fg_kind kind, int variant, int bm, int bn, int bk, int wm, int wn,
-                 int threads, int stages, int wps, double eff, const char* name) {
+                 int threads, int stages, int wps, double eff, const char* name,
+                 int fallback = -1) {
     Entry e;
     memset(&e, 0, sizeof e);
     e.cfg.id = id;
@@ -78,23 +81,29 @@ Entry make_entry(int id, fg_kind kind, int variant, int bm, int bn, int bk, int 
     e.variant = variant;
     e.wps = wps;
     e.eff = eff;
+    e.fallback = fallback;
     return e;
 }
 
 const Entry* table() {
     static const Entry t[] = {
-        make_entry(0, FG_KIND_MFMA, 0, 256, 256, 16, 128, 128, 256, 2, 1, 0.85, "mfma_256x256x16_w2x2"),
-        make_entry(1, FG_KIND_MFMA, 1, 256, 128, 16, 128, 128, 128, 2, 1, 0.80, "mfma_256x128x16_w2x1"),
-        make_entry(2, FG_KIND_MFMA, 2, 128, 128, 16, 128, 128, 64, 2, 1, 0.75, "mfma_128x128x16_w1x1"),
-        make_entry(3, FG_KIND_MFMA, 3, 64, 128, 16, 64, 128, 64, 2, 1, 0.55, "mfma_64x128x16_w1x1"),
-        make_entry(4, FG_KIND_MFMA, 4, 32, 128, 16, 32, 128, 64, 2, 2, 0.35, "mfma_32x128x16_w1x1"),
+        make_entry(0, FG_KIND_MFMA, 0, 256, 256, 16, 128, 128, 256, 2, 1, 0.86, "mfma_256x256x16_w2x2"),
+        make_entry(1, FG_KIND_MFMA, 1, 256, 128, 16, 128, 128, 128, 2, 1, 0.86, "mfma_256x128x16_w2x1"),
+        make_entry(2, FG_KIND_MFMA, 2, 128, 128, 16, 128, 128, 64, 2, 1, 0.85, "mfma_128x128x16_w1x1"),
+        make_entry(3, FG_KIND_MFMA, 3, 64, 128, 16, 64, 128, 64, 2, 1, 0.78, "mfma_64x128x16_w1x1"),
+        make_entry(4, FG_KIND_MFMA, 4, 32, 128, 16, 32, 128, 64, 2, 2, 0.70, "mfma_32x128x16_w1x1"),
         // VALU rows: wm x wn is the per-thread tile.
-        make_entry(5, FG_KIND_VALU, 0, 128, 128, 8, 8, 8, 256, 2, 2, 0.40, "valu_128x128x8_t8x8"),
-        make_entry(6, FG_KIND_VALU, 1, 64, 64, 8, 4, 4, 256, 2, 4, 0.25, "valu_64x64x8_t4x4"),
+        make_entry(5, FG_KIND_VALU, 0, 128, 128, 8, 8, 8, 256, 2, 2, 0.53, "valu_128x128x8_t8x8"),
+        make_entry(6, FG_KIND_VALU, 1, 64, 64, 8, 4, 4, 256, 2, 4, 0.42, "valu_64x64x8_t4x4"),
+        // MFMA rows fed by direct-to-LDS loads (rows of A and B 16-byte
+        // aligned; otherwise the named 2-stage entry runs).
+        make_entry(7, FG_KIND_MFMA, 5, 256, 256, 16, 128, 128, 256, 4, 1, 0.93, "mfma_256x256x16_w2x2_s4", 0),
+        make_entry(8, FG_KIND_MFMA, 6, 256, 128, 16, 128, 128, 128, 3, 1, 0.90, "mfma_256x128x16_w2x1_s3", 1),
+        make_entry(9, FG_KIND_MFMA, 7, 128, 128, 16, 64, 64, 256, 4, 2, 0.85, "mfma_128x128x16_w2x2_s4", 2),
     };
     return t;
 }
-constexpr int kNumEntries = 7;
+constexpr int kNumEntries = 10;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -112,12 +121,13 @@ double cost(const Entry& e, int64_t M, int64_t N, int64_t K) {
     return (double)rounds * e.cfg.wm * e.cfg.wn * kpad * (double)share / e.eff;
 }
 
-int select_entry(int64_t M, int64_t N, int64_t K) {
+int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned) {
     int best = -1;
     double best_cost = 0;
     for (int i = 0; i < kNumEntries; ++i) {
         const Entry& e = table()[i];
         if (e.cfg.kind != FG_KIND_MFMA) continue;
+        if (e.fallback >= 0 && !ab_aligned) continue;
         const double c = cost(e, M, N, K);
         if (best < 0 || c < best_cost) {
             best = i;
@@ -201,6 +211,7 @@ int32_t build_flags(const float* A, int64_t lda, const float* B, int64_t ldb, co
     if (aligned16(A) && lda % 4 == 0) f |= fg::FLAG_VEC_A;
     if (aligned16(B) && ldb % 4 == 0) f |= fg::FLAG_VEC_B;
     if (aligned16(C) && ldc % 4 == 0) f |= fg::FLAG_VEC_C;
+    if (((uintptr_t)C & 7u) == 0 && ldc % 2 == 0) f |= fg::FLAG_VEC2_C;
     if (beta == 0.0f) f |= fg::FLAG_BETA0;
     return f;
 }
@@ -242,7 +253,9 @@ fg_status fg_select_config(fg_op transA, fg_op transB, int64_t M, int64_t N, int
     fg_status s = validate(transA, transB, M, N, K, 1.0f, A, lda, B, ldb, C, ldc, false);
     if (s != FG_OK) return s;
     if (!out) return fail(FG_ERR_INVALID_ARG, 12, "out is NULL");
-    *out = table()[select_entry(M, N, K)].cfg;
+    const int32_t f = build_flags(A, lda, B, ldb, C, ldc, 0.0f);
+    const bool ab_aligned = (f & fg::FLAG_VEC_A) && (f & fg::FLAG_VEC_B);
+    *out = table()[select_entry(M, N, K, ab_aligned)].cfg;
     return FG_OK;
 }
 
@@ -288,7 +301,9 @@ fg_status fg_sgemm_ex(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t 
     if (no_product) {
         e = fg::launch_scale(p, stream);
     } else {
-        const int idx = config_id >= 0 ? config_id : select_entry(M, N, K);
+        const bool ab_aligned = (p.flags & fg::FLAG_VEC_A) && (p.flags & fg::FLAG_VEC_B);
+        int idx = config_id >= 0 ? config_id : select_entry(M, N, K, ab_aligned);
+        if (table()[idx].fallback >= 0 && !ab_aligned) idx = table()[idx].fallback;
         const Entry& en = table()[idx];
         p.tiles_m = (int32_t)cdiv(M, en.cfg.bm);
         p.tiles_n = (int32_t)cdiv(N, en.cfg.bn);

@@ -42,6 +42,12 @@ __device__ __forceinline__ void st4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
 __device__ __forceinline__ void st1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
 }
+__device__ __forceinline__ f2 ld2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void st2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 0);
+}
 
 // Four consecutive floats starting at element `e` of a row whose valid length
 // is `len` (elements at or past `len` read as 0). `off` is the byte offset of

@@ -30,6 +30,7 @@ enum : int32_t {
     FLAG_VEC_C = 4,    // C rows start 16-byte aligned: 128-bit loads/stores
     FLAG_BETA0 = 8,    // beta == 0: C is written, never read
     FLAG_XCD_REMAP = 16,  // remap workgroup ids so each XCD gets a contiguous tile range
+    FLAG_VEC2_C = 32,  // C rows start 8-byte aligned: 64-bit loads/stores
 };
 
 // Launchers: enqueue one kernel on `stream`; return the HIP launch status.

@@ -157,25 +157,127 @@ struct Operand {
     }
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int TA, int TB>
+// One operand's k-tile filled by direct-to-LDS buffer loads: each
+// buffer_load_dwordx4 ... lds writes 64 lanes x 16 bytes to 1 KiB of
+// consecutive LDS (lane L at base + 16 L), so instruction j of a stage covers
+// LDS floats [256 j, 256 j + 256) and each lane fetches the global chunk that
+// belongs at its slot in the layout read_frags() expects. This is the
+// gfx950 counterpart of the asynchronous global-to-shared copy of "Matmul II",
+// section 7 (t3) and "CuTe-ly writing an SM86 SGEMM", section "mainloop": the
+// data bypasses registers and the wave keeps issuing MFMAs.
+template <int BX, int WX, int XB, bool MN, int NW>
+struct DmaOperand {
+    using Op = Operand<BX, WX, XB, MN, 64 * NW>;
+    static constexpr int kInst = Op::kStage / 256;  // 1 KiB instructions per stage
+    static constexpr int kPerWave = kInst / NW;
+    static_assert(kInst % NW == 0, "stage must split evenly over the waves");
+
+    uint32_t voff[kPerWave];
+
+    __device__ void init(int wave, int lane, int ld) {
+#pragma unroll
+        for (int q = 0; q < kPerWave; ++q) {
+            const int j = wave + NW * q;
+            const int pos = j * 256 + 4 * lane;  // float offset inside the stage
+            if constexpr (MN) {
+                const int k = pos / BX, col = pos % BX;
+                voff[q] = (uint32_t)(k * ld + col) * 4u;
+            } else {
+                const int pr = pos / kBK, slot = (pos % kBK) / 4;
+                const int c = slot ^ Op::swz(pr);
+                const int x = Op::phys_to_logical(pr);
+                voff[q] = (uint32_t)(x * ld + 4 * c) * 4u;
+            }
+        }
+    }
+
+    __device__ void issue(__amdgpu_buffer_rsrc_t r, float* stage, int wave) const {
+        // Device pass only: in clang's host pass the LDS address-space cast
+        // makes it drop the launch stubs of later template instances.
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+        for (int q = 0; q < kPerWave; ++q) {
+            const int j = wave + NW * q;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)(stage + j * 256), 16, voff[q], 0, 0, 0);
+        }
+#else
+        (void)r, (void)stage, (void)wave;
+#endif
+    }
+};
+
+// s_waitcnt that waits until at most VM vector-memory operations of this wave
+// are outstanding and all of its LDS operations have completed (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at its maximum,
+// lgkmcnt 11:8 = 0).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lds() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would make the compiler wait for every outstanding direct-to-LDS load,
+// including the ones meant to stay in flight across the barrier. The caller
+// orders memory itself with wait_vm_lds<>() first; the "memory" clobber keeps
+// the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// LDS read instructions read_frags() issues for one operand per k-tile.
+template <int XB, bool MN>
+constexpr int read_count() {
+    return MN ? (kBK / 2) * (XB == 8 ? 2 : 1) : 2 * XB;
+}
+
+template <int MB, int NB>
+__device__ __forceinline__ void mfma_kstep(f16v (&acc)[MB][NB], const float (&fa)[kBK / 2][MB],
+                                           const float (&fb)[kBK / 2][NB], int s) {
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s][a], fb[s][b], acc[a][b], 0, 0, 0);
+}
+
+template <int MB, int NB>
+__device__ __forceinline__ void mfma_ktile(f16v (&acc)[MB][NB], const float (&fa)[kBK / 2][MB],
+                                           const float (&fb)[kBK / 2][NB]) {
+#pragma unroll
+    for (int s = 0; s < kBK / 2; ++s) mfma_kstep<MB, NB>(acc, fa, fb, s);
+}
+
+// STAGES == 2: register-staged loop (any alignment, any edges).
+// STAGES >= 3: direct-to-LDS loop over a STAGES-deep ring, with the next
+// k-tile's fragments read during the current k-tile's MFMAs. It needs the rows
+// of A and B to start 16-byte aligned (the dispatcher checks). Tiles that
+// cross M or N take the same loop: a row of op(A) past M (a column of op(B)
+// past N) only feeds elements of C that are never stored, and the bounded
+// buffer resources return 0 past the end of each matrix. A partial last
+// k-tile (K not a multiple of 16) must read as exact zeros past K, so it goes
+// through the guarded register path once after the loop.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int TA, int TB, int STAGES>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 sgemm_mfma_kernel(GemmParams p) {
-    constexpr int NT = 64 * WAVES_M * WAVES_N;
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int NT = 64 * NW;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int MB = WM / 32, NB = WN / 32;
     constexpr bool A_MN = (TA == 1);  // A stored K x M
     constexpr bool B_MN = (TB == 0);  // B stored K x N
+    constexpr int NS = STAGES < 2 ? 2 : STAGES;
     using OpA = Operand<BM, WM, MB, A_MN, NT>;
     using OpB = Operand<BN, WN, NB, B_MN, NT>;
 
-    __shared__ f4 smem[(2 * OpA::kStage + 2 * OpB::kStage) / 4];
+    __shared__ f4 smem[NS * (OpA::kStage + OpB::kStage) / 4];
     float* sA = reinterpret_cast<float*>(smem);
-    float* sB = sA + 2 * OpA::kStage;
+    float* sB = sA + NS * OpA::kStage;
 
     int tm, tn;
     map_tile(blockIdx.x, gridDim.x, p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep in SGPRs
     const int wave_m = wave / WAVES_N, wave_n = wave % WAVES_N;
     const int li = lane & 31, lh = lane >> 5;
 
@@ -190,14 +292,16 @@ sgemm_mfma_kernel(GemmParams p) {
     const int64_t b_org = B_MN ? (int64_t)n0 : (int64_t)n0 * p.ldb;
     const int64_t b_kstep = B_MN ? (int64_t)kBK * p.ldb : (int64_t)kBK;
 
-    OpA opa;
-    OpB opb;
-    opa.init(tid, p.lda);
-    opb.init(tid, p.ldb);
+    f16v acc[MB][NB];
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    const int nk = (p.K + kBK - 1) / kBK;
-
-    auto load_tiles = [&](int kt) {
+    // Guarded register-path load of k-tile kt (zero past M, N and K).
+    auto load_tiles = [&](OpA& opa, OpB& opb, int kt) {
         const int k0 = kt * kBK;
         const int64_t ao = a_org + kt * a_kstep, bo = b_org + kt * b_kstep;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + ao, p.a_extent - ao);
@@ -214,43 +318,127 @@ sgemm_mfma_kernel(GemmParams p) {
             opb.load(rb, vec_b && k_in && b_rows_in, vec_b, p.N - n0, k_left);
     };
 
-    f16v acc[MB][NB];
+    if constexpr (STAGES >= 3) {
+        using DA = DmaOperand<BM, WM, MB, A_MN, NW>;
+        using DB = DmaOperand<BN, WN, NB, B_MN, NW>;
+        constexpr int NI = DA::kPerWave + DB::kPerWave;  // DMA ops per wave per k-tile
+        const int nk = p.K / kBK;                         // full k-tiles
+        DA da;
+        DB db;
+        da.init(wave, lane, p.lda);
+        db.init(wave, lane, p.ldb);
+        // DMA of k-tile kt into buffer kt % NS. A k-tile past the last one
+        // (kt >= nk) gets an empty buffer resource: its loads read nothing
+        // from memory and write zeros into a buffer no one reads, which keeps
+        // the loop below free of branches.
+        auto issue = [&](int kt) {
+            const int st = kt % NS;
+            const bool live = kt < nk;
+            const int64_t ao = a_org + kt * a_kstep, bo = b_org + kt * b_kstep;
+            da.issue(make_rsrc(p.A + ao, live ? p.a_extent - ao : 0), sA + st * OpA::kStage, wave);
+            db.issue(make_rsrc(p.B + bo, live ? p.b_extent - bo : 0), sB + st * OpB::kStage, wave);
+        };
+        // Prologue: k-tiles 0 .. NS-2 in flight; tiles 0 and 1 must have
+        // landed before the first iteration (it reads tile 1's fragments).
 #pragma unroll
-    for (int a = 0; a < MB; ++a)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+        for (int j = 0; j < NS - 1; ++j) issue(j);
+        wait_vm_lds<(NS - 3) * NI>();
+        barrier_no_fence();
 
-    if (nk > 0) {
-        load_tiles(0);
-        opa.store_lds(sA);
-        opb.store_lds(sB);
-        if (nk > 1) load_tiles(1);
-        __syncthreads();
-    }
+        float f0a[kBK / 2][MB], f0b[kBK / 2][NB], f1a[kBK / 2][MB], f1b[kBK / 2][NB];
+        OpA::read_frags(sA, wave_m * WM, li, lh, f0a);
+        OpB::read_frags(sB, wave_n * WN, li, lh, f0b);
 
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const float* bufA = sA + cur * OpA::kStage;
-        const float* bufB = sB + cur * OpB::kStage;
-        float fa[kBK / 2][MB], fb[kBK / 2][NB];
-        OpA::read_frags(bufA, wave_m * WM, li, lh, fa);
-        OpB::read_frags(bufB, wave_n * WN, li, lh, fb);
+        // k-tile t, branch free: its MFMAs run from registers; after the first
+        // k-step the DMA of k-tile t+NS-1 goes into buffer (t+NS-1)%NS, and
+        // after the second the fragments of k-tile t+1 are read. Buffer
+        // (t+NS-1)%NS last held k-tile t-1, whose fragments were read in
+        // iteration t-2: the barriers closing iterations t-2 and t-1 separate
+        // those reads from this DMA. The closing wait leaves k-tile t+NS-1's
+        // DMA in flight and completes k-tile t+2 (read in iteration t+1).
+        auto step = [&](int t, float (&ca)[kBK / 2][MB], float (&cb)[kBK / 2][NB],
+                        float (&na)[kBK / 2][MB], float (&nb)[kBK / 2][NB]) {
+            const int st = (t + 1) % NS;
+            mfma_kstep<MB, NB>(acc, ca, cb, 0);
+            issue(t + NS - 1);
+            mfma_kstep<MB, NB>(acc, ca, cb, 1);
+            OpA::read_frags(sA + st * OpA::kStage, wave_m * WM, li, lh, na);
+            OpB::read_frags(sB + st * OpB::kStage, wave_n * WN, li, lh, nb);
 #pragma unroll
-        for (int s = 0; s < kBK / 2; ++s)
+            for (int s = 2; s < kBK / 2; ++s) mfma_kstep<MB, NB>(acc, ca, cb, s);
+            // Issue order for the scheduler: the DMA loads spread over the
+            // first MFMAs, then the fragment reads one per MFMA, then the rest
+            // of the MFMAs, so that the reads have landed long before the
+            // closing wait and the matrix core never waits on memory.
+            constexpr int kMfma = (kBK / 2) * MB * NB;
+            constexpr int kReads = read_count<MB, A_MN>() + read_count<NB, B_MN>();
 #pragma unroll
-            for (int a = 0; a < MB; ++a)
+            for (int i = 0; i < NI; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM (DMA)
+            }
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s][a], fb[s][b],
-                                                                     acc[a][b], 0, 0, 0);
-        if (kt + 1 < nk) {
-            opa.store_lds(sA + (cur ^ 1) * OpA::kStage);
-            opb.store_lds(sB + (cur ^ 1) * OpB::kStage);
-            if (kt + 2 < nk) load_tiles(kt + 2);
+            for (int i = 0; i < kReads; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kMfma - NI - kReads, 0);
+            wait_vm_lds<(NS - 3) * NI>();
+            barrier_no_fence();
+        };
+        int t = 0;
+        for (; t + 1 < nk; t += 2) {
+            step(t, f0a, f0b, f1a, f1b);
+            step(t + 1, f1a, f1b, f0a, f0b);
         }
-        __syncthreads();
+        if (t < nk) step(t, f0a, f0b, f1a, f1b);
+        wait_vm_lds<0>();  // no DMA (not even an empty one) outlives the loop
+
+        if (p.K % kBK) {
+            // Partial last k-tile: every wave has finished its DMA and LDS reads
+            // (waited above); the barrier makes that true for all of them
+            // before buffer 0 is rewritten.
+            __syncthreads();
+            OpA opa;
+            OpB opb;
+            opa.init(tid, p.lda);
+            opb.init(tid, p.ldb);
+            load_tiles(opa, opb, nk);
+            opa.store_lds(sA);
+            opb.store_lds(sB);
+            __syncthreads();
+            OpA::read_frags(sA, wave_m * WM, li, lh, f0a);
+            OpB::read_frags(sB, wave_n * WN, li, lh, f0b);
+            mfma_ktile<MB, NB>(acc, f0a, f0b);
+        }
+    } else {
+        const int nk = (p.K + kBK - 1) / kBK;
+        OpA opa;
+        OpB opb;
+        opa.init(tid, p.lda);
+        opb.init(tid, p.ldb);
+
+        if (nk > 0) {
+            load_tiles(opa, opb, 0);
+            opa.store_lds(sA);
+            opb.store_lds(sB);
+            if (nk > 1) load_tiles(opa, opb, 1);
+            __syncthreads();
+        }
+
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            float fa[kBK / 2][MB], fb[kBK / 2][NB];
+            OpA::read_frags(sA + cur * OpA::kStage, wave_m * WM, li, lh, fa);
+            OpB::read_frags(sB + cur * OpB::kStage, wave_n * WN, li, lh, fb);
+            mfma_ktile<MB, NB>(acc, fa, fb);
+            if (kt + 1 < nk) {
+                opa.store_lds(sA + (cur ^ 1) * OpA::kStage);
+                opb.store_lds(sB + (cur ^ 1) * OpB::kStage);
+                if (kt + 2 < nk) load_tiles(opa, opb, kt + 2);
+            }
+            __syncthreads();
+        }
     }
 
     // Epilogue: C = alpha * acc + beta * C, 128-bit where possible.
@@ -259,10 +447,14 @@ sgemm_mfma_kernel(GemmParams p) {
     const int64_t c_org = (int64_t)m0 * p.ldc + n0;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c_org, p.c_extent - c_org);
     const bool beta0 = p.flags & FLAG_BETA0;
-    const bool vec_c = (p.flags & FLAG_VEC_C) && NB == 4;
+    // A lane's NB columns are one 128-bit (NB = 4) or 64-bit (NB = 2) access
+    // when C's rows are aligned for it and all NB columns are inside N.
+    const bool vec_c = NB == 4 ? (p.flags & FLAG_VEC_C) != 0
+                               : (NB == 2 ? (p.flags & FLAG_VEC2_C) != 0 : false);
     const float alpha = p.alpha, beta = p.beta;
     const int col0 = wave_n * WN + NB * li;  // first of this lane's NB columns
     const int cols_left = p.N - n0 - col0;
+    const bool full_vec = vec_c && cols_left >= NB;
 #pragma unroll
     for (int a = 0; a < MB; ++a) {
 #pragma unroll
@@ -274,56 +466,69 @@ sgemm_mfma_kernel(GemmParams p) {
             float v[NB];
 #pragma unroll
             for (int b = 0; b < NB; ++b) v[b] = alpha * acc[a][b][r];
-            if (vec_c && mn_interior) {
-                f4 o = {v[0], v[1], v[2], v[3]};
-                if (!beta0) {
-                    f4 c = ld4(rc, off);
-                    o = o + beta * c;
+            if constexpr (NB == 4) {
+                if (full_vec) {
+                    f4 o = {v[0], v[1], v[2], v[3]};
+                    if (!beta0) o = o + beta * ld4(rc, off);
+                    st4(rc, off, o);
+                    continue;
                 }
-                st4(rc, off, o);
-            } else {
+            } else if constexpr (NB == 2) {
+                if (full_vec) {
+                    f2 o = {v[0], v[1]};
+                    if (!beta0) o = o + beta * ld2(rc, off);
+                    st2(rc, off, o);
+                    continue;
+                }
+            }
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (b < cols_left) {
-                        float o = v[b];
-                        if (!beta0) o += beta * ld1(rc, off + 4 * b);
-                        st1(rc, off + 4 * b, o);
-                    }
+            for (int b = 0; b < NB; ++b) {
+                if (b < cols_left) {
+                    float o = v[b];
+                    if (!beta0) o += beta * ld1(rc, off + 4 * b);
+                    st1(rc, off + 4 * b, o);
                 }
             }
         }
     }
+    (void)mn_interior;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 hipError_t launch_shape(int ta, int tb, const GemmParams& p, hipStream_t s) {
     const dim3 grid(p.tiles_m * p.tiles_n), block(64 * WAVES_M * WAVES_N);
     if (ta == 0 && tb == 0)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 0>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 0, STAGES>), grid, block, 0, s, p);
     else if (ta == 0 && tb == 1)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 1>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 1, STAGES>), grid, block, 0, s, p);
     else if (ta == 1 && tb == 0)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 0>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 0, STAGES>), grid, block, 0, s, p);
     else
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 1>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 1, STAGES>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 // Variants (must match the MFMA rows of the configuration table):
-//   0: 256 x 256, 2 x 2 waves of 128 x 128
-//   1: 256 x 128, 2 x 1 waves of 128 x 128
-//   2: 128 x 128, 1 wave  of 128 x 128
-//   3:  64 x 128, 1 wave  of  64 x 128
-//   4:  32 x 128, 1 wave  of  32 x 128
+//   0: 256 x 256, 2 x 2 waves of 128 x 128, 2 stages (register staged)
+//   1: 256 x 128, 2 x 1 waves of 128 x 128, 2 stages
+//   2: 128 x 128, 1 wave  of 128 x 128,     2 stages
+//   3:  64 x 128, 1 wave  of  64 x 128,     2 stages
+//   4:  32 x 128, 1 wave  of  32 x 128,     2 stages
+//   5: 256 x 256, 2 x 2 waves of 128 x 128, 4-stage direct-to-LDS ring
+//   6: 256 x 128, 2 x 1 waves of 128 x 128, 3-stage direct-to-LDS ring
+//   7: 128 x 128, 2 x 2 waves of  64 x  64, 4-stage direct-to-LDS ring
 hipError_t launch_mfma(int variant, int ta, int tb, const GemmParams& p, hipStream_t s) {
     switch (variant) {
-        case 0: return launch_shape<256, 256, 2, 2>(ta, tb, p, s);
-        case 1: return launch_shape<256, 128, 2, 1>(ta, tb, p, s);
-        case 2: return launch_shape<128, 128, 1, 1>(ta, tb, p, s);
-        case 3: return launch_shape<64, 128, 1, 1>(ta, tb, p, s);
-        case 4: return launch_shape<32, 128, 1, 1>(ta, tb, p, s);
+        case 0: return launch_shape<256, 256, 2, 2, 2>(ta, tb, p, s);
+        case 1: return launch_shape<256, 128, 2, 1, 2>(ta, tb, p, s);
+        case 2: return launch_shape<128, 128, 1, 1, 2>(ta, tb, p, s);
+        case 3: return launch_shape<64, 128, 1, 1, 2>(ta, tb, p, s);
+        case 4: return launch_shape<32, 128, 1, 1, 2>(ta, tb, p, s);
+        case 5: return launch_shape<256, 256, 2, 2, 4>(ta, tb, p, s);
+        case 6: return launch_shape<256, 128, 2, 1, 3>(ta, tb, p, s);
+        case 7: return launch_shape<128, 128, 2, 2, 4>(ta, tb, p, s);
         default: return hipErrorInvalidValue;
     }
 }

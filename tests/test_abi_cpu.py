@@ -97,6 +97,9 @@ def test_selection_is_mfma_and_scales_with_shape():
     assert small["bm"] * small["bn"] < big["bm"] * big["bn"]
     ragged = fg.fg_select_config("T", "N", 3001, 2047, 1025, lda=3001, ldb=2047, ldc=2047)
     assert ragged["kind"] == fg.FG_KIND_MFMA
+    # direct-to-LDS entries (stages > 2) need 16-byte aligned rows of A and B
+    assert ragged["stages"] == 2
+    assert fg.fg_select_config("N", "N", 8192, 8192, 8192, A=16 + 4)["stages"] == 2
     with pytest.raises(fg.FgError) as e:
         fg.fg_select_config("N", "N", 4, 4, 4, lda=2)
     assert e.value.bad_arg == 8
@@ -125,3 +128,17 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read().splitlines()
     hip = {l.split()[-1] for l in maps if "libamdhip64" in l}
     assert len(hip) == 1, hip
+
+
+def test_every_kernel_instance_is_linked():
+    """Every kernel the launchers reference has its host launch stub in the
+    library (clang once dropped some silently; the load then failed)."""
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("needs nm")
+    out = subprocess.run(["nm", "-C", fg.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    undefined = [l for l in out.splitlines() if " U " in l and "device_stub" in l]
+    assert not undefined, undefined[:5]
+    assert sum(1 for l in out.splitlines() if "device_stub" in l and "sgemm_mfma" in l) >= 32

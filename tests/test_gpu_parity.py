@@ -119,6 +119,31 @@ def test_ragged_float_every_config(cfg, ta, tb):
         check_full(w, A, B, C, out)
 
 
+def _pad4(n):
+    return (n + 3) // 4 * 4
+
+
+@pytest.mark.parametrize("cfg", all_ids())
+@pytest.mark.parametrize("ta,tb", OPS)
+def test_ragged_aligned_rows_every_config(cfg, ta, tb):
+    """Ragged M, N and K with 16-byte aligned rows (leading dimensions padded
+    to a multiple of 4, padding filled with NaN): the direct-to-LDS kernels
+    take these, including tiles that cross M or N and a partial last
+    k-tile. NaN padding must not reach C."""
+    for i, (M, N, K) in enumerate([(97, 131, 45), (300, 257, 100), (513, 190, 1025),
+                                   (256, 256, 17), (31, 500, 3), (640, 384, 64)]):
+        w0 = wl.custom(M, N, K, ta, tb)
+        w = wl.custom(M, N, K, ta, tb, alpha=-0.75, beta=0.25, dist="normal", seed=40 + i,
+                      lda=_pad4(w0.LDA), ldb=_pad4(w0.LDB), ldc=_pad4(w0.LDC))
+        A, B, C = wl.make_inputs(w)
+        A[:, w0.LDA:] = np.nan
+        B[:, w0.LDB:] = np.nan
+        C[:, N:] = 4321.0
+        out, full = run_fg(w, A, B, C, config=cfg)
+        check_full(w, A, B, C, out)
+        assert np.all(full[:, N:] == 4321.0)
+
+
 @pytest.mark.parametrize("ta,tb", OPS)
 def test_padded_and_misaligned(ta, tb):
     """Leading dimensions larger than the rows (odd and multiple-of-4) and
