@@ -56,7 +56,8 @@ struct Entry {
     int wps;       // resident waves per SIMD
     double eff;    // relative efficiency for the cost model
     int fallback;  // entry used instead when A or B rows are not 16-byte
-                   // aligned (direct-to-LDS entries only; -1 = none needed)
+                   // aligned (entries with 16-byte direct-to-LDS loads only;
+                   // -1 = any alignment is fine)
 };
 
 constexpr int kNumCUs = 256;
@@ -87,23 +88,27 @@ Entry make_entry(int id, fg_kind kind, int variant, int bm, int bn, int bk, int 
 
 const Entry* table() {
     static const Entry t[] = {
-        make_entry(0, FG_KIND_MFMA, 0, 256, 256, 16, 128, 128, 256, 2, 1, 0.86, "mfma_256x256x16_w2x2"),
-        make_entry(1, FG_KIND_MFMA, 1, 256, 128, 16, 128, 128, 128, 2, 1, 0.86, "mfma_256x128x16_w2x1"),
-        make_entry(2, FG_KIND_MFMA, 2, 128, 128, 16, 128, 128, 64, 2, 1, 0.85, "mfma_128x128x16_w1x1"),
-        make_entry(3, FG_KIND_MFMA, 3, 64, 128, 16, 64, 128, 64, 2, 1, 0.78, "mfma_64x128x16_w1x1"),
-        make_entry(4, FG_KIND_MFMA, 4, 32, 128, 16, 32, 128, 64, 2, 2, 0.70, "mfma_32x128x16_w1x1"),
-        // VALU rows: wm x wn is the per-thread tile.
-        make_entry(5, FG_KIND_VALU, 0, 128, 128, 8, 8, 8, 256, 2, 2, 0.53, "valu_128x128x8_t8x8"),
-        make_entry(6, FG_KIND_VALU, 1, 64, 64, 8, 4, 4, 256, 2, 4, 0.42, "valu_64x64x8_t4x4"),
-        // MFMA rows fed by direct-to-LDS loads (rows of A and B 16-byte
-        // aligned; otherwise the named 2-stage entry runs).
-        make_entry(7, FG_KIND_MFMA, 5, 256, 256, 16, 128, 128, 256, 4, 1, 0.93, "mfma_256x256x16_w2x2_s4", 0),
-        make_entry(8, FG_KIND_MFMA, 6, 256, 128, 16, 128, 128, 128, 3, 1, 0.90, "mfma_256x128x16_w2x1_s3", 1),
-        make_entry(9, FG_KIND_MFMA, 7, 128, 128, 16, 64, 64, 256, 4, 2, 0.85, "mfma_128x128x16_w2x2_s4", 2),
+        // eff: fraction of the fp32 matrix peak measured at 8192^3 NN with
+        // the SIMDs full (bench.py --calibrate, profiles/calibration_*.md).
+        make_entry(0, FG_KIND_MFMA, 0, 256, 256, 16, 128, 128, 256, 2, 1, 0.857, "mfma_256x256x16_w2x2"),
+        make_entry(1, FG_KIND_MFMA, 1, 256, 128, 16, 128, 128, 128, 2, 1, 0.866, "mfma_256x128x16_w2x1"),
+        make_entry(2, FG_KIND_MFMA, 2, 128, 128, 16, 128, 128, 64, 2, 1, 0.850, "mfma_128x128x16_w1x1"),
+        make_entry(3, FG_KIND_MFMA, 3, 64, 128, 16, 64, 128, 64, 2, 1, 0.786, "mfma_64x128x16_w1x1"),
+        make_entry(4, FG_KIND_MFMA, 4, 32, 128, 16, 32, 128, 64, 2, 2, 0.737, "mfma_32x128x16_w1x1"),
+        // VALU rows: wm x wn is the per-thread tile; never auto-selected.
+        make_entry(5, FG_KIND_VALU, 0, 128, 128, 8, 8, 8, 256, 2, 2, 0.55, "valu_128x128x8_t8x8"),
+        make_entry(6, FG_KIND_VALU, 1, 64, 64, 8, 4, 4, 256, 2, 4, 0.44, "valu_64x64x8_t4x4"),
+        // MFMA rows fed by direct-to-LDS loads. The 16-byte form needs rows
+        // of A and B 16-byte aligned (otherwise the named entry runs); the
+        // 4-byte form (_dw) takes any rows.
+        make_entry(7, FG_KIND_MFMA, 5, 256, 256, 16, 128, 128, 256, 4, 1, 0.931, "mfma_256x256x16_w2x2_s4", 0),
+        make_entry(8, FG_KIND_MFMA, 6, 256, 128, 16, 128, 128, 128, 3, 1, 0.921, "mfma_256x128x16_w2x1_s3", 1),
+        make_entry(9, FG_KIND_MFMA, 7, 128, 128, 16, 64, 64, 256, 4, 2, 0.899, "mfma_128x128x16_w2x2_s4", 10),
+        make_entry(10, FG_KIND_MFMA, 8, 128, 128, 16, 64, 64, 256, 4, 2, 0.881, "mfma_128x128x16_w2x2_s4_dw"),
     };
     return t;
 }
-constexpr int kNumEntries = 10;
+constexpr int kNumEntries = 11;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

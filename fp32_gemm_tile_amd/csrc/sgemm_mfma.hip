@@ -31,8 +31,8 @@
 //   * k-contiguous (A stored M x K, or B^T stored N x K): LDS row = one m (or
 //     n), 16 floats. Rows are placed in "physical" order so that the 32 rows
 //     read by one instruction are consecutive, and the four 16-byte chunks of
-//     a row are XOR-swizzled with bits 1-2 of the physical row, so eight
-//     consecutive rows' chunk c land in eight distinct 16-byte bank groups
+//     a row are XOR-swizzled with bits 2-3 of the physical row, so sixteen
+//     consecutive rows' chunk c land in sixteen distinct 16-byte bank groups
 //     (the XOR swizzle of "CuTe-ly writing an SM86 SGEMM", section "swizzles
 //     & shared memory", at 16-byte granularity).
 //
@@ -78,7 +78,11 @@ struct Operand {
         const int a = within / 32, i = within % 32;
         return w * WX + i * XB + a;
     }
-    __device__ static int swz(int pr) { return (pr >> 1) & 3; }
+    // 16-byte chunk swizzle of a k-contiguous row: an ds_read_b128 is served
+    // 16 lanes (256 bytes) at a time, and 16 consecutive physical rows hold
+    // chunk c at 16 distinct 16-byte slots of a 256-byte window when the
+    // chunk index is XORed with bits 2-3 of the row.
+    __device__ static int swz(int pr) { return (pr >> 2) & 3; }
 
     __device__ void init(int tid, int ld) {
 #pragma unroll
@@ -157,19 +161,24 @@ struct Operand {
     }
 };
 
-// One operand's k-tile filled by direct-to-LDS buffer loads: each
+// One operand's k-tile filled by direct-to-LDS buffer loads. A
 // buffer_load_dwordx4 ... lds writes 64 lanes x 16 bytes to 1 KiB of
-// consecutive LDS (lane L at base + 16 L), so instruction j of a stage covers
-// LDS floats [256 j, 256 j + 256) and each lane fetches the global chunk that
-// belongs at its slot in the layout read_frags() expects. This is the
-// gfx950 counterpart of the asynchronous global-to-shared copy of "Matmul II",
-// section 7 (t3) and "CuTe-ly writing an SM86 SGEMM", section "mainloop": the
-// data bypasses registers and the wave keeps issuing MFMAs.
-template <int BX, int WX, int XB, bool MN, int NW>
+// consecutive LDS (lane L at base + 16 L); buffer_load_dword ... lds writes
+// 64 x 4 bytes (lane L at base + 4 L). Instruction j of a stage therefore
+// covers LDS floats [j * 64 * W, (j + 1) * 64 * W) for W = BYTES / 4 floats per
+// lane, and each lane fetches the global element(s) that belong at its slot
+// of the layout read_frags() expects. The 4-byte form needs no alignment of
+// the matrix rows. This is the gfx950 counterpart of the asynchronous
+// global-to-shared copy of "Matmul II", section 7 (t3) and "CuTe-ly writing
+// an SM86 SGEMM", section "mainloop": the data bypasses registers and the
+// wave keeps issuing MFMAs.
+template <int BX, int WX, int XB, bool MN, int NW, int BYTES>
 struct DmaOperand {
     using Op = Operand<BX, WX, XB, MN, 64 * NW>;
-    static constexpr int kInst = Op::kStage / 256;  // 1 KiB instructions per stage
+    static constexpr int kW = BYTES / 4;                    // floats per lane
+    static constexpr int kInst = Op::kStage / (64 * kW);    // instructions per stage
     static constexpr int kPerWave = kInst / NW;
+    static_assert(BYTES == 4 || BYTES == 16, "dword or dwordx4");
     static_assert(kInst % NW == 0, "stage must split evenly over the waves");
 
     uint32_t voff[kPerWave];
@@ -178,15 +187,15 @@ struct DmaOperand {
 #pragma unroll
         for (int q = 0; q < kPerWave; ++q) {
             const int j = wave + NW * q;
-            const int pos = j * 256 + 4 * lane;  // float offset inside the stage
+            const int pos = j * 64 * kW + kW * lane;  // float offset inside the stage
             if constexpr (MN) {
                 const int k = pos / BX, col = pos % BX;
                 voff[q] = (uint32_t)(k * ld + col) * 4u;
             } else {
-                const int pr = pos / kBK, slot = (pos % kBK) / 4;
+                const int pr = pos / kBK, slot = (pos % kBK) / 4, e = pos % 4;
                 const int c = slot ^ Op::swz(pr);
                 const int x = Op::phys_to_logical(pr);
-                voff[q] = (uint32_t)(x * ld + 4 * c) * 4u;
+                voff[q] = (uint32_t)(x * ld + 4 * c + e) * 4u;
             }
         }
     }
@@ -199,7 +208,8 @@ struct DmaOperand {
         for (int q = 0; q < kPerWave; ++q) {
             const int j = wave + NW * q;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void*)(stage + j * 256), 16, voff[q], 0, 0, 0);
+                r, (__attribute__((address_space(3))) void*)(stage + j * 64 * kW), BYTES, voff[q],
+                0, 0, 0);
         }
 #else
         (void)r, (void)stage, (void)wave;
@@ -249,14 +259,15 @@ __device__ __forceinline__ void mfma_ktile(f16v (&acc)[MB][NB], const float (&fa
 
 // STAGES == 2: register-staged loop (any alignment, any edges).
 // STAGES >= 3: direct-to-LDS loop over a STAGES-deep ring, with the next
-// k-tile's fragments read during the current k-tile's MFMAs. It needs the rows
-// of A and B to start 16-byte aligned (the dispatcher checks). Tiles that
+// k-tile's fragments read during the current k-tile's MFMAs. DMAB = 16 needs
+// the rows of A and B to start 16-byte aligned (the dispatcher checks);
+// DMAB = 4 takes any rows. Tiles that
 // cross M or N take the same loop: a row of op(A) past M (a column of op(B)
 // past N) only feeds elements of C that are never stored, and the bounded
 // buffer resources return 0 past the end of each matrix. A partial last
 // k-tile (K not a multiple of 16) must read as exact zeros past K, so it goes
 // through the guarded register path once after the loop.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int TA, int TB, int STAGES>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int TA, int TB, int STAGES, int DMAB>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 sgemm_mfma_kernel(GemmParams p) {
     constexpr int NW = WAVES_M * WAVES_N;
@@ -319,8 +330,8 @@ sgemm_mfma_kernel(GemmParams p) {
     };
 
     if constexpr (STAGES >= 3) {
-        using DA = DmaOperand<BM, WM, MB, A_MN, NW>;
-        using DB = DmaOperand<BN, WN, NB, B_MN, NW>;
+        using DA = DmaOperand<BM, WM, MB, A_MN, NW, DMAB>;
+        using DB = DmaOperand<BN, WN, NB, B_MN, NW, DMAB>;
         constexpr int NI = DA::kPerWave + DB::kPerWave;  // DMA ops per wave per k-tile
         const int nk = p.K / kBK;                         // full k-tiles
         DA da;
@@ -494,17 +505,17 @@ sgemm_mfma_kernel(GemmParams p) {
     (void)mn_interior;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int DMAB = 16>
 hipError_t launch_shape(int ta, int tb, const GemmParams& p, hipStream_t s) {
     const dim3 grid(p.tiles_m * p.tiles_n), block(64 * WAVES_M * WAVES_N);
     if (ta == 0 && tb == 0)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 0, STAGES>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 0, STAGES, DMAB>), grid, block, 0, s, p);
     else if (ta == 0 && tb == 1)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 1, STAGES>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 1, STAGES, DMAB>), grid, block, 0, s, p);
     else if (ta == 1 && tb == 0)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 0, STAGES>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 0, STAGES, DMAB>), grid, block, 0, s, p);
     else
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 1, STAGES>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 1, STAGES, DMAB>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 
@@ -519,6 +530,7 @@ hipError_t launch_shape(int ta, int tb, const GemmParams& p, hipStream_t s) {
 //   5: 256 x 256, 2 x 2 waves of 128 x 128, 4-stage direct-to-LDS ring
 //   6: 256 x 128, 2 x 1 waves of 128 x 128, 3-stage direct-to-LDS ring
 //   7: 128 x 128, 2 x 2 waves of  64 x  64, 4-stage direct-to-LDS ring
+//   8: as 7 with 4-byte direct-to-LDS loads (rows of any alignment)
 hipError_t launch_mfma(int variant, int ta, int tb, const GemmParams& p, hipStream_t s) {
     switch (variant) {
         case 0: return launch_shape<256, 256, 2, 2, 2>(ta, tb, p, s);
@@ -529,6 +541,7 @@ hipError_t launch_mfma(int variant, int ta, int tb, const GemmParams& p, hipStre
         case 5: return launch_shape<256, 256, 2, 2, 4>(ta, tb, p, s);
         case 6: return launch_shape<256, 128, 2, 1, 3>(ta, tb, p, s);
         case 7: return launch_shape<128, 128, 2, 2, 4>(ta, tb, p, s);
+        case 8: return launch_shape<128, 128, 2, 2, 4, 4>(ta, tb, p, s);
         default: return hipErrorInvalidValue;
     }
 }
