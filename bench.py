@@ -52,7 +52,7 @@ def load_traffic(workload):
     return t.get("bytes_per_launch")
 
 
-def time_gpu(w, steps, warmup, config=-1):
+def time_gpu(w, steps, warmup, config=-1, splitk=False):
     import torch
     import fp32_gemm_tile_amd as fg
     from fp32_gemm_tile_amd import workloads as wl
@@ -64,11 +64,17 @@ def time_gpu(w, steps, warmup, config=-1):
         (w.M, w.LDC), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
+    ws = torch.empty(64 << 20, dtype=torch.float32, device="cuda") if splitk else None
 
     def step():
-        st = fg.fg_sgemm_ex(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
-                            w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
-                            sp, config)
+        if splitk:
+            st = fg.fg_sgemm_splitk(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
+                                    w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
+                                    0, ws.data_ptr(), ws.numel() * 4, sp)
+        else:
+            st = fg.fg_sgemm_ex(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
+                                w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
+                                sp, config)
         if st != 0:
             raise fg.FgError(st, fg.fg_last_bad_arg(), fg.fg_last_error())
 
@@ -131,10 +137,10 @@ def copy_probe(nbytes=1 << 30, reps=3):
     print(f"copy_probe: {reps} copies of {nbytes} bytes", file=sys.stderr, flush=True)
 
 
-def run_one(name, steps, warmup, with_cpu, config=-1):
+def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False):
     from fp32_gemm_tile_amd import workloads as wl
     w = wl.WORKLOADS[name]
-    g = time_gpu(w, steps, warmup, config)
+    g = time_gpu(w, steps, warmup, config, splitk)
     tflops = w.flops / (g["ms_per_launch"] * 1e-3) / 1e12
     traffic = load_traffic(name)
     out = {
@@ -180,6 +186,9 @@ def main():
                          "(reference for scaling HBM traffic counters)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time every table entry on every workload (one line each)")
+    ap.add_argument("--splitk", action="store_true",
+                    help="with --suite: time fg_sgemm_splitk (library-chosen split, "
+                         "256 MiB workspace) instead of fg_sgemm")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -198,9 +207,9 @@ def main():
         ids = range(fg.fg_num_configs()) if args.calibrate else [args.config]
         for name in ("C1", "C2", "C3", "C4", "C5a", "C5b", "C6"):
             for cid in ids:
-                r = run_one(name, args.steps, args.warmup, False, cid)
+                r = run_one(name, args.steps, args.warmup, False, cid, args.splitk)
                 print(json.dumps({"workload": name, "config": r["config"]["kernel_config"],
-                                  "forced": cid, "tflops": r["value"],
+                                  "forced": cid, "splitk": args.splitk, "tflops": r["value"],
                                   "ms": r["ms_per_step"], "pct": r["pct_of_fp32_peak"]}),
                       flush=True)
         return

@@ -9,6 +9,7 @@ importing the binding's functions raises.
 
 Entry points (same names as the C ABI):
   fg_sgemm(...), fg_sgemm_ex(...)      raw pointers and sizes
+  fg_sgemm_splitk(...), fg_sgemm_splitk_workspace_size(M, N, S)
   fg_num_configs(), fg_get_config(i), fg_select_config(...)
   fg_last_bad_arg(), fg_last_error(), fg_status_string(s), fg_abi_version()
 Convenience:
@@ -76,6 +77,10 @@ def load_library(path: str = LIB_PATH):
     lib.fg_sgemm.restype = i32
     lib.fg_sgemm_ex.argtypes = gemm_args + [i32]
     lib.fg_sgemm_ex.restype = i32
+    lib.fg_sgemm_splitk.argtypes = gemm_args[:13] + [i32, vp, ctypes.c_size_t, vp]
+    lib.fg_sgemm_splitk.restype = i32
+    lib.fg_sgemm_splitk_workspace_size.argtypes = [i64, i64, i32]
+    lib.fg_sgemm_splitk_workspace_size.restype = ctypes.c_size_t
     lib.fg_num_configs.argtypes = []
     lib.fg_num_configs.restype = i32
     lib.fg_get_config.argtypes = [i32, ctypes.POINTER(fg_config)]
@@ -125,6 +130,18 @@ def fg_sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, st
                 config_id=-1):
     return load_library().fg_sgemm_ex(_op(transA), _op(transB), M, N, K, alpha, A, lda,
                                       B, ldb, beta, C, ldc, stream or None, config_id)
+
+
+def fg_sgemm_splitk(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                    workspace, workspace_bytes, stream=0):
+    """Raw split-K call (see include/fp32gemm.h); workspace is a device address."""
+    return load_library().fg_sgemm_splitk(_op(transA), _op(transB), M, N, K, alpha, A, lda,
+                                          B, ldb, beta, C, ldc, splits, workspace or None,
+                                          workspace_bytes, stream or None)
+
+
+def fg_sgemm_splitk_workspace_size(M, N, splits) -> int:
+    return load_library().fg_sgemm_splitk_workspace_size(M, N, splits)
 
 
 def fg_num_configs() -> int:

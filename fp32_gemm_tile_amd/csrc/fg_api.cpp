@@ -112,31 +112,59 @@ constexpr int kNumEntries = 11;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Estimated time (arbitrary units) of the call with MFMA entry e: the number
-// of rounds of resident waves times the time of one wave tile, which grows
-// with the number of waves sharing a SIMD.
-double cost(const Entry& e, int64_t M, int64_t N, int64_t K) {
+// Estimated time in seconds of the call with MFMA entry e and `splits`
+// split-K slices: rounds of resident waves times the time of one wave tile
+// (which grows with the number of waves sharing a SIMD), plus, with split-K,
+// the partial slices written, read back and reduced at HBM speed.
+constexpr double kSimdFlops = 157.3e12 / (kNumCUs * kSimdsPerCU);  // fp32 MFMA per SIMD
+constexpr double kHbmBytes = 5.0e12;                              // sustained, not peak
+constexpr double kLaunch = 4e-6;                                  // one more kernel
+
+int64_t effective_splits(int64_t K, int64_t bk, int64_t splits, int64_t* kt_per_split) {
+    const int64_t kt_total = cdiv(K, bk);
+    if (splits < 1) splits = 1;
+    if (splits > kt_total) splits = kt_total;
+    const int64_t kps = cdiv(kt_total, splits);
+    *kt_per_split = kps;
+    return cdiv(kt_total, kps);
+}
+
+double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, bool beta0) {
+    int64_t kps = 0;
+    const int64_t s = effective_splits(K, e.cfg.bk, splits, &kps);
     const int64_t tiles = cdiv(M, e.cfg.bm) * cdiv(N, e.cfg.bn);
-    const int64_t waves = tiles * (e.cfg.threads / 64);
+    const int64_t waves = tiles * (e.cfg.threads / 64) * s;
     const int64_t simds = (int64_t)kNumCUs * kSimdsPerCU;
     const int64_t rounds = cdiv(waves, simds * e.wps);
     int64_t share = cdiv(waves, simds);
     if (share > e.wps) share = e.wps;
-    const double kpad = (double)cdiv(K, e.cfg.bk) * e.cfg.bk;
-    return (double)rounds * e.cfg.wm * e.cfg.wn * kpad * (double)share / e.eff;
+    const double kpad = (double)kps * e.cfg.bk;
+    double t = (double)rounds * 2.0 * e.cfg.wm * e.cfg.wn * kpad * (double)share /
+               (e.eff * kSimdFlops);
+    if (s > 1)
+        t += ((double)(2 * s + (beta0 ? 1 : 2)) * M * N * 4.0) / kHbmBytes + kLaunch;
+    return t;
 }
 
-int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned) {
+// Best MFMA entry (and split count, at most max_splits) for the call.
+int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_splits,
+                 bool beta0, int64_t* best_splits) {
+    static const int64_t kSplits[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
     int best = -1;
     double best_cost = 0;
+    *best_splits = 1;
     for (int i = 0; i < kNumEntries; ++i) {
         const Entry& e = table()[i];
         if (e.cfg.kind != FG_KIND_MFMA) continue;
         if (e.fallback >= 0 && !ab_aligned) continue;
-        const double c = cost(e, M, N, K);
-        if (best < 0 || c < best_cost) {
-            best = i;
-            best_cost = c;
+        for (int64_t sp : kSplits) {
+            if (sp > max_splits) break;
+            const double c = cost(e, M, N, K, sp, beta0);
+            if (best < 0 || c < best_cost) {
+                best = i;
+                best_cost = c;
+                *best_splits = sp;
+            }
         }
     }
     return best;
@@ -260,13 +288,21 @@ fg_status fg_select_config(fg_op transA, fg_op transB, int64_t M, int64_t N, int
     if (!out) return fail(FG_ERR_INVALID_ARG, 12, "out is NULL");
     const int32_t f = build_flags(A, lda, B, ldb, C, ldc, 0.0f);
     const bool ab_aligned = (f & fg::FLAG_VEC_A) && (f & fg::FLAG_VEC_B);
-    *out = table()[select_entry(M, N, K, ab_aligned)].cfg;
+    int64_t splits = 1;
+    *out = table()[select_entry(M, N, K, ab_aligned, 1, true, &splits)].cfg;
     return FG_OK;
 }
 
-fg_status fg_sgemm_ex(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, float alpha,
-                      const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
-                      float* C, int64_t ldc, hipStream_t stream, int32_t config_id) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of fg_sgemm_ex and fg_sgemm_splitk. splits: 1 = no split-K,
+// 0 = choose (bounded by the workspace), > 1 = requested.
+fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, float alpha,
+                   const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                   float* C, int64_t ldc, hipStream_t stream, int32_t config_id,
+                   int64_t splits, float* ws, size_t ws_bytes) {
     clear_error();
     fg_status s = validate(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
     if (s != FG_OK) return s;
@@ -277,9 +313,6 @@ fg_status fg_sgemm_ex(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t 
     if (M == 0 || N == 0) return FG_OK;
     const bool no_product = (K == 0 || alpha == 0.0f);
     if (no_product && beta == 1.0f) return FG_OK;
-
-    s = check_device();
-    if (s != FG_OK) return s;
 
     fg::GemmParams p;
     memset(&p, 0, sizeof p);
@@ -302,27 +335,104 @@ fg_status fg_sgemm_ex(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t 
     p.c_extent = (M - 1) * ldc + N;
     p.flags = build_flags(A, lda, B, ldb, C, ldc, beta);
 
-    hipError_t e;
     if (no_product) {
-        e = fg::launch_scale(p, stream);
+        s = check_device();
+        if (s != FG_OK) return s;
+        const hipError_t e = fg::launch_scale(p, stream);
+        if (e != hipSuccess) return fail(FG_ERR_HIP, 0, "kernel launch: %s", hipGetErrorString(e));
+        return FG_OK;
+    }
+
+    const bool ab_aligned = (p.flags & fg::FLAG_VEC_A) && (p.flags & fg::FLAG_VEC_B);
+    const int64_t slice = M * N;  // floats per split-K partial
+    // One slice needs no workspace, so at least one is always possible.
+    int64_t max_splits = ws ? (int64_t)(ws_bytes / (sizeof(float) * (size_t)slice)) : 1;
+    if (max_splits < 1) max_splits = 1;
+    int64_t want = splits;
+    int idx;
+    if (config_id >= 0) {
+        idx = config_id;
+        if (want == 0) want = 1;
     } else {
-        const bool ab_aligned = (p.flags & fg::FLAG_VEC_A) && (p.flags & fg::FLAG_VEC_B);
-        int idx = config_id >= 0 ? config_id : select_entry(M, N, K, ab_aligned);
-        if (table()[idx].fallback >= 0 && !ab_aligned) idx = table()[idx].fallback;
-        const Entry& en = table()[idx];
-        p.tiles_m = (int32_t)cdiv(M, en.cfg.bm);
-        p.tiles_n = (int32_t)cdiv(N, en.cfg.bn);
-        const int64_t nblocks = (int64_t)p.tiles_m * p.tiles_n;
-        if (nblocks > 0x7FFFFFFF) return fail(FG_ERR_UNSUPPORTED, 0, "too many tiles");
-        p.group_m = group_m_override() > 0 ? group_m_override() : 4;
-        if (p.group_m > p.tiles_m) p.group_m = p.tiles_m;
-        if (en.cfg.kind == FG_KIND_MFMA)
-            e = fg::launch_mfma(en.variant, transA, transB, p, stream);
-        else
-            e = fg::launch_valu(en.variant, transA, transB, p, stream);
+        int64_t auto_splits = 1;
+        idx = select_entry(M, N, K, ab_aligned, want == 0 ? max_splits : 1, beta == 0.0f,
+                           &auto_splits);
+        if (want == 0) want = auto_splits;
+    }
+    if (idx < 0 || idx >= kNumEntries)
+        return fail(FG_ERR_UNSUPPORTED, 0, "no table entry fits this call");
+    if (table()[idx].fallback >= 0 && !ab_aligned) idx = table()[idx].fallback;
+    const Entry& en = table()[idx];
+    if (en.cfg.kind != FG_KIND_MFMA) want = 1;  // split-K runs on the MFMA kernels
+
+    int64_t kps = 0;
+    const int64_t nsplit = effective_splits(K, en.cfg.bk, want, &kps);
+    if (nsplit > 1 && nsplit > max_splits)
+        return fail(FG_ERR_INVALID_ARG, 16, "workspace of %zu bytes holds %lld splits, need %lld",
+                    ws_bytes, (long long)max_splits, (long long)nsplit);
+
+    s = check_device();
+    if (s != FG_OK) return s;
+
+    p.tiles_m = (int32_t)cdiv(M, en.cfg.bm);
+    p.tiles_n = (int32_t)cdiv(N, en.cfg.bn);
+    const int64_t nblocks = (int64_t)p.tiles_m * p.tiles_n;
+    if (nblocks > 0x7FFFFFFF) return fail(FG_ERR_UNSUPPORTED, 0, "too many tiles");
+    p.group_m = group_m_override() > 0 ? group_m_override() : 4;
+    if (p.group_m > p.tiles_m) p.group_m = p.tiles_m;
+    p.kt_per_split = (int32_t)kps;
+    p.c_split_stride = 0;
+
+    hipError_t e;
+    if (nsplit > 1) {
+        // Partial products (alpha = 1, beta = 0) into dense M x N slices of
+        // the workspace, then C = alpha * sum + beta * C.
+        fg::GemmParams q = p;
+        q.C = ws;
+        q.ldc = (int32_t)N;
+        q.c_extent = slice;
+        q.c_split_stride = slice;
+        q.alpha = 1.0f;
+        q.beta = 0.0f;
+        q.flags = build_flags(A, lda, B, ldb, ws, N, 0.0f);
+        e = fg::launch_mfma(en.variant, transA, transB, q, stream);
+        if (e == hipSuccess) e = fg::launch_splitk_reduce(ws, (int32_t)nsplit, p, stream);
+    } else if (en.cfg.kind == FG_KIND_MFMA) {
+        e = fg::launch_mfma(en.variant, transA, transB, p, stream);
+    } else {
+        e = fg::launch_valu(en.variant, transA, transB, p, stream);
     }
     if (e != hipSuccess) return fail(FG_ERR_HIP, 0, "kernel launch: %s", hipGetErrorString(e));
     return FG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fg_status fg_sgemm_ex(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, float alpha,
+                      const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                      float* C, int64_t ldc, hipStream_t stream, int32_t config_id) {
+    return run_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                    config_id, 1, nullptr, 0);
+}
+
+size_t fg_sgemm_splitk_workspace_size(int64_t M, int64_t N, int32_t splits) {
+    if (M <= 0 || N <= 0 || splits <= 1) return 0;
+    return (size_t)M * (size_t)N * (size_t)splits * sizeof(float);
+}
+
+fg_status fg_sgemm_splitk(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                          float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                          float beta, float* C, int64_t ldc, int32_t splits, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    clear_error();
+    if (splits < 0) return fail(FG_ERR_INVALID_ARG, 14, "splits < 0");
+    if (splits > 1 && !workspace) return fail(FG_ERR_INVALID_ARG, 15, "workspace is NULL");
+    if (workspace && ((uintptr_t)workspace & 3u))
+        return fail(FG_ERR_INVALID_ARG, 15, "workspace is not 4-byte aligned");
+    return run_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1,
+                    splits, (float*)workspace, workspace ? workspace_bytes : 0);
 }
 
 fg_status fg_sgemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, float alpha,

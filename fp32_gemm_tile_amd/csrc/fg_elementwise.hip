@@ -1,0 +1,82 @@
+// The two memory-bound kernels around the GEMM proper:
+//   * scale: C = beta * C (C = 0 without reading C when beta == 0), the
+//     whole result when K == 0 or alpha == 0;
+//   * split-K reduction: C = alpha * (W_0 + W_1 + ... + W_{S-1}) + beta * C,
+//     summing the per-split partial products in ascending split order, so
+//     the result does not depend on scheduling.
+// Both walk the M x N window with a grid-stride loop; every index is inside
+// the caller's buffers by construction, so plain global accesses are used.
+#include "fg_device.h"
+
+namespace fg {
+namespace {
+
+__global__ void __launch_bounds__(256) scale_kernel(GemmParams p) {
+    const int64_t total = (int64_t)p.M * p.N;
+    const bool beta0 = p.flags & FLAG_BETA0;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = t / p.N, j = t - i * p.N;
+        float* c = p.C + i * p.ldc + j;
+        *c = beta0 ? 0.f : p.beta * *c;
+    }
+}
+
+// VEC: N % 4 == 0, W 16-byte aligned and C rows 16-byte aligned, so each
+// thread handles four consecutive columns with 128-bit accesses.
+template <bool VEC>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ W,
+                                                            int splits, GemmParams p) {
+    const int64_t mn = (int64_t)p.M * p.N;
+    const bool beta0 = p.flags & FLAG_BETA0;
+    constexpr int V = VEC ? 4 : 1;
+    const int64_t units = mn / V;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units;
+         u += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = u * V;  // first element (row-major in the dense slices)
+        const int64_t i = e / p.N, j = e - i * p.N;
+        float* c = p.C + i * p.ldc + j;
+        if constexpr (VEC) {
+            f4 acc = *reinterpret_cast<const f4*>(W + e);
+            for (int s = 1; s < splits; ++s) acc = acc + *reinterpret_cast<const f4*>(W + s * mn + e);
+            f4 out = p.alpha * acc;
+            if (!beta0) out = out + p.beta * *reinterpret_cast<const f4*>(c);
+            *reinterpret_cast<f4*>(c) = out;
+        } else {
+            float acc = W[e];
+            for (int s = 1; s < splits; ++s) acc += W[s * mn + e];
+            float out = p.alpha * acc;
+            if (!beta0) out += p.beta * *c;
+            *c = out;
+        }
+    }
+}
+
+unsigned grid_for(int64_t units) {
+    int64_t blocks = (units + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    return (unsigned)blocks;
+}
+
+}  // namespace
+
+hipError_t launch_scale(const GemmParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(scale_kernel, dim3(grid_for((int64_t)p.M * p.N)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float* W, int32_t splits, const GemmParams& p,
+                                hipStream_t s) {
+    const int64_t mn = (int64_t)p.M * p.N;
+    const bool vec = (p.N % 4 == 0) && (((uintptr_t)W & 15u) == 0) && (p.flags & FLAG_VEC_C);
+    if (vec)
+        hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(grid_for(mn / 4)), dim3(256), 0, s,
+                           W, splits, p);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(grid_for(mn)), dim3(256), 0, s, W,
+                           splits, p);
+    return hipGetLastError();
+}
+
+}  // namespace fg

@@ -22,6 +22,12 @@ struct GemmParams {
     int32_t tiles_m, tiles_n;
     int32_t group_m;   // tile rows per raster group
     int32_t flags;     // FLAG_* below
+    // Split-K: workgroup (tile, blockIdx.y = s) sums k-tiles
+    // [s * kt_per_split, (s + 1) * kt_per_split) and writes its result to
+    // C + s * c_split_stride. One split: kt_per_split covers all of K and
+    // c_split_stride is 0.
+    int32_t kt_per_split;
+    int64_t c_split_stride;
 };
 
 enum : int32_t {
@@ -42,5 +48,9 @@ hipError_t launch_valu(int variant, int trans_a, int trans_b, const GemmParams& 
                        hipStream_t stream);
 // C = beta * C (beta == 0: C = 0 without reading it); for K == 0 or alpha == 0.
 hipError_t launch_scale(const GemmParams& p, hipStream_t stream);
+// Split-K reduction: C = alpha * sum_{s < splits} W_s + beta * C, where W_s is
+// the dense M x N slice W + s * M * N; the sum runs in ascending s.
+hipError_t launch_splitk_reduce(const float* W, int32_t splits, const GemmParams& p,
+                                hipStream_t stream);
 
 }  // namespace fg

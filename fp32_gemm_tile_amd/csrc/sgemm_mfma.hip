@@ -296,12 +296,17 @@ sgemm_mfma_kernel(GemmParams p) {
     const bool mn_interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
     const bool a_rows_in = m0 + BM <= p.M, b_rows_in = n0 + BN <= p.N;
 
-    // Element offset of the tile origin (row m0 / column n0, k = 0) and of
-    // one k-tile step, per operand.
-    const int64_t a_org = A_MN ? (int64_t)m0 : (int64_t)m0 * p.lda;
+    // This workgroup's k range: k-tiles [kt0, kt0 + kt_per_split) of K, i.e.
+    // Kp elements of k starting at kt0 * 16 (all of K without split-K).
+    const int kt0 = (int)blockIdx.y * p.kt_per_split;
+    const int Kp = min(p.K - kt0 * kBK, p.kt_per_split * kBK);
+
+    // Element offset of the tile origin (row m0 / column n0, first k of the
+    // range) and of one k-tile step, per operand.
     const int64_t a_kstep = A_MN ? (int64_t)kBK * p.lda : (int64_t)kBK;
-    const int64_t b_org = B_MN ? (int64_t)n0 : (int64_t)n0 * p.ldb;
     const int64_t b_kstep = B_MN ? (int64_t)kBK * p.ldb : (int64_t)kBK;
+    const int64_t a_org = (A_MN ? (int64_t)m0 : (int64_t)m0 * p.lda) + kt0 * a_kstep;
+    const int64_t b_org = (B_MN ? (int64_t)n0 : (int64_t)n0 * p.ldb) + kt0 * b_kstep;
 
     f16v acc[MB][NB];
 #pragma unroll
@@ -311,14 +316,15 @@ sgemm_mfma_kernel(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    // Guarded register-path load of k-tile kt (zero past M, N and K).
+    // Guarded register-path load of k-tile kt of the range (zero past M, N
+    // and the end of the range).
     auto load_tiles = [&](OpA& opa, OpB& opb, int kt) {
         const int k0 = kt * kBK;
         const int64_t ao = a_org + kt * a_kstep, bo = b_org + kt * b_kstep;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + ao, p.a_extent - ao);
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + bo, p.b_extent - bo);
-        const bool k_in = k0 + kBK <= p.K;
-        const int k_left = p.K - k0;
+        const bool k_in = k0 + kBK <= Kp;
+        const int k_left = Kp - k0;
         if constexpr (A_MN)
             opa.load(ra, vec_a && k_in && a_rows_in, vec_a, k_left, p.M - m0);
         else
@@ -333,7 +339,7 @@ sgemm_mfma_kernel(GemmParams p) {
         using DA = DmaOperand<BM, WM, MB, A_MN, NW, DMAB>;
         using DB = DmaOperand<BN, WN, NB, B_MN, NW, DMAB>;
         constexpr int NI = DA::kPerWave + DB::kPerWave;  // DMA ops per wave per k-tile
-        const int nk = p.K / kBK;                         // full k-tiles
+        const int nk = Kp / kBK;                          // full k-tiles
         DA da;
         DB db;
         da.init(wave, lane, p.lda);
@@ -405,7 +411,7 @@ sgemm_mfma_kernel(GemmParams p) {
         if (t < nk) step(t, f0a, f0b, f1a, f1b);
         wait_vm_lds<0>();  // no DMA (not even an empty one) outlives the loop
 
-        if (p.K % kBK) {
+        if (Kp % kBK) {
             // Partial last k-tile: every wave has finished its DMA and LDS reads
             // (waited above); the barrier makes that true for all of them
             // before buffer 0 is rewritten.
@@ -423,7 +429,7 @@ sgemm_mfma_kernel(GemmParams p) {
             mfma_ktile<MB, NB>(acc, f0a, f0b);
         }
     } else {
-        const int nk = (p.K + kBK - 1) / kBK;
+        const int nk = (Kp + kBK - 1) / kBK;
         OpA opa;
         OpB opb;
         opa.init(tid, p.lda);
@@ -456,7 +462,8 @@ sgemm_mfma_kernel(GemmParams p) {
     // Accumulator register r of a 32x32 block, lane (i = lane%32, h = lane/32),
     // holds block row 8*(r/4) + 4*h + r%4 and block column i.
     const int64_t c_org = (int64_t)m0 * p.ldc + n0;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c_org, p.c_extent - c_org);
+    float* const Cs = p.C + (int64_t)blockIdx.y * p.c_split_stride;  // this split's C
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cs + c_org, p.c_extent - c_org);
     const bool beta0 = p.flags & FLAG_BETA0;
     // A lane's NB columns are one 128-bit (NB = 4) or 64-bit (NB = 2) access
     // when C's rows are aligned for it and all NB columns are inside N.
@@ -507,7 +514,8 @@ sgemm_mfma_kernel(GemmParams p) {
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int DMAB = 16>
 hipError_t launch_shape(int ta, int tb, const GemmParams& p, hipStream_t s) {
-    const dim3 grid(p.tiles_m * p.tiles_n), block(64 * WAVES_M * WAVES_N);
+    const dim3 grid(p.tiles_m * p.tiles_n, (p.K + kBK * p.kt_per_split - 1) / (kBK * p.kt_per_split)),
+        block(64 * WAVES_M * WAVES_N);
     if (ta == 0 && tb == 0)
         hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 0, STAGES, DMAB>), grid, block, 0, s, p);
     else if (ta == 0 && tb == 1)

@@ -209,19 +209,6 @@ hipError_t launch_valu_shape(int ta, int tb, const GemmParams& p, hipStream_t s)
     return hipGetLastError();
 }
 
-// C = beta * C over the M x N window (beta == 0: C = 0, C not read).
-// Every index is inside the window, so plain global accesses suffice.
-__global__ void __launch_bounds__(256) scale_kernel(GemmParams p) {
-    const int64_t total = (int64_t)p.M * p.N;
-    const bool beta0 = p.flags & FLAG_BETA0;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-         t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t i = t / p.N, j = t - i * p.N;
-        float* c = p.C + i * p.ldc + j;
-        *c = beta0 ? 0.f : p.beta * *c;
-    }
-}
-
 }  // namespace
 
 // Variants (must match the VALU rows of the configuration table):
@@ -233,15 +220,6 @@ hipError_t launch_valu(int variant, int ta, int tb, const GemmParams& p, hipStre
         case 1: return launch_valu_shape<64, 64, 4, 4>(ta, tb, p, s);
         default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_scale(const GemmParams& p, hipStream_t s) {
-    const int64_t total = (int64_t)p.M * p.N;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(scale_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
-    return hipGetLastError();
 }
 
 }  // namespace fg

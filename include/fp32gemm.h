@@ -24,7 +24,8 @@
  *
  * Ownership: the caller owns every buffer. A, B and C are device pointers
  * (e.g. from hipMalloc or a framework's allocator). The library allocates,
- * frees and copies nothing and keeps no workspace. C must not overlap A or B.
+ * frees and copies nothing and keeps no workspace of its own (split-K takes
+ * one from the caller). C must not overlap A or B.
  *
  * Streams: work is enqueued on `stream` (NULL = the null stream) and the call
  * returns without synchronising; C is complete once the stream reaches that
@@ -38,6 +39,7 @@
 #ifndef FP32GEMM_H
 #define FP32GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -117,6 +119,42 @@ fg_status fg_sgemm_ex(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t 
                       const float* B, int64_t ldb, float beta,
                       float* C, int64_t ldc, hipStream_t stream,
                       int32_t config_id);
+
+/*
+ * fg_sgemm_splitk: fg_sgemm with the K dimension split across workgroups,
+ * for shapes whose M x N grid of output tiles is too small to fill the GPU
+ * (split-K as described in "Matmul II: register blocking, warp tiling,
+ * tensor cores", section 8: several blocks share one output tile and their
+ * partial sums are added).
+ *
+ * Each of S slices sums a contiguous range of k into a dense M x N binary32
+ * partial in `workspace` (slice s at workspace + s*M*N floats); a second
+ * kernel then writes C = alpha * (P_0 + P_1 + ... + P_{S-1}) + beta * C,
+ * adding the slices in ascending order, so repeated calls give identical
+ * bits. Both kernels run on `stream`.
+ *
+ * Arguments 1-13 as for fg_sgemm, then:
+ *   14 splits          : 0 = choose (at most what the workspace holds),
+ *                        1 = no split (same as fg_sgemm), S > 1 = S slices
+ *                        (capped at the number of 16-deep k-tiles)
+ *   15 workspace       : device memory owned by the caller, 4-byte aligned
+ *                        (16-byte alignment enables 128-bit accesses); may be
+ *                        NULL when splits == 1 (or splits == 0: then no split)
+ *   16 workspace_bytes : at least fg_sgemm_splitk_workspace_size(M, N, S) for
+ *                        the S actually used, else FG_ERR_INVALID_ARG
+ *   17 stream
+ * The workspace must not overlap A, B or C and must not be used by another
+ * call that may run at the same time.
+ */
+fg_status fg_sgemm_splitk(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                          float alpha, const float* A, int64_t lda,
+                          const float* B, int64_t ldb, float beta,
+                          float* C, int64_t ldc, int32_t splits,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace fg_sgemm_splitk needs for `splits` slices of an M x N
+ * result (0 when splits <= 1 or the result is empty). Host only. */
+size_t fg_sgemm_splitk_workspace_size(int64_t M, int64_t N, int32_t splits);
 
 /* Size of the tile-configuration table. Host only; no GPU needed. */
 int32_t fg_num_configs(void);

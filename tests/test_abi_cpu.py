@@ -159,3 +159,34 @@ def test_auto_selection_matches_measured_best():
         measured = cal["tflops"][name]
         # the pick must be the best, or within 3% of it
         assert measured[str(got["id"])] >= 0.97 * measured[str(best)], (name, got["name"], best)
+
+
+def test_splitk_workspace_size_and_validation():
+    assert fg.fg_sgemm_splitk_workspace_size(100, 60, 1) == 0
+    assert fg.fg_sgemm_splitk_workspace_size(100, 60, 0) == 0
+    assert fg.fg_sgemm_splitk_workspace_size(0, 60, 4) == 0
+    assert fg.fg_sgemm_splitk_workspace_size(100, 60, 4) == 100 * 60 * 4 * 4
+
+    def call(splits=4, ws=4096, ws_bytes=1 << 30, M=64, N=64, K=1024):
+        return fg.fg_sgemm_splitk(0, 0, M, N, K, 1.0, 16, K, 16, N, 0.0, 16, N, splits, ws,
+                                  ws_bytes, 0)
+    assert call(splits=-1) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 14
+    assert call(ws=0) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 15
+    assert call(ws=4098) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 15
+    # 4 slices of 64 x 64 floats need 65536 bytes
+    assert call(ws_bytes=65535) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 16
+    # the usual argument checks still apply, with fg_sgemm's numbering
+    assert fg.fg_sgemm_splitk(0, 0, 4, 4, 4, 1.0, 16, 3, 16, 4, 0.0, 16, 4, 2, 4096, 1 << 20,
+                              0) == fg.FG_ERR_INVALID_ARG
+    assert fg.fg_last_bad_arg() == 8
+    # quick return: nothing to do, no GPU needed
+    assert call(M=0) == fg.FG_OK
+
+
+def test_splitk_auto_with_workspace_too_small_for_any_split():
+    """splits = 0 with a workspace smaller than one M x N slice must plan a
+    single pass (it once planned nothing and divided by zero). Without a GPU
+    the call then stops at the device check."""
+    st = fg.fg_sgemm_splitk(0, 0, 4096, 4096, 256, 1.0, 16, 256, 16, 4096, 0.0, 16, 4096, 0,
+                            4096, 1024, 0)
+    assert st in (fg.FG_ERR_HIP, fg.FG_ERR_UNSUPPORTED, fg.FG_OK)
