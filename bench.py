@@ -31,16 +31,18 @@ METRIC = "fp32 SGEMM TFLOP/s and % of MI355X fp32 peak at 4096^3 and 8192^3"
 
 
 def kernel_source_sha():
+    """Hash of the sources that define the matrix-core kernel and its launch."""
     h = hashlib.sha256()
-    for f in ("sgemm_mfma.hip", "fg_device.h", "fg_kernels.h", "fg_api.cpp"):
+    for f in ("sgemm_mfma.hip", "fg_device.h", "fg_kernels.h"):
         with open(os.path.join(ROOT, "fp32_gemm_tile_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
+def load_traffic(workload, kernel_config):
     """Measured HBM traffic per launch from committed rocprofv3 counter runs,
-    if they were taken on the current kernel sources; else None."""
+    if they were taken on the current kernel sources with the same table
+    entry; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     try:
         with open(path) as f:
@@ -48,6 +50,8 @@ def load_traffic(workload):
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    if t.get("kernel_config") not in (None, kernel_config):
         return None
     return t.get("bytes_per_launch")
 
@@ -142,7 +146,7 @@ def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False):
     w = wl.WORKLOADS[name]
     g = time_gpu(w, steps, warmup, config, splitk)
     tflops = w.flops / (g["ms_per_launch"] * 1e-3) / 1e12
-    traffic = load_traffic(name)
+    traffic = load_traffic(name, g["config"])
     out = {
         "metric": METRIC,
         "value": round(tflops, 3),

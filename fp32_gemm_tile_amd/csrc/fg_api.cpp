@@ -105,10 +105,12 @@ const Entry* table() {
         make_entry(8, FG_KIND_MFMA, 6, 256, 128, 16, 128, 128, 128, 3, 1, 0.921, "mfma_256x128x16_w2x1_s3", 1),
         make_entry(9, FG_KIND_MFMA, 7, 128, 128, 16, 64, 64, 256, 4, 2, 0.899, "mfma_128x128x16_w2x2_s4", 10),
         make_entry(10, FG_KIND_MFMA, 8, 128, 128, 16, 64, 64, 256, 4, 2, 0.881, "mfma_128x128x16_w2x2_s4_dw"),
+        make_entry(11, FG_KIND_MFMA, 9, 256, 256, 16, 64, 128, 512, 4, 2, 0.90, "mfma_256x256x16_w4x2_s4", 0),
+        make_entry(12, FG_KIND_MFMA, 10, 256, 128, 16, 128, 64, 256, 3, 2, 0.90, "mfma_256x128x16_w2x2_s3", 1),
     };
     return t;
 }
-constexpr int kNumEntries = 11;
+constexpr int kNumEntries = 13;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -267,8 +267,10 @@ __device__ __forceinline__ void mfma_ktile(f16v (&acc)[MB][NB], const float (&fa
 // buffer resources return 0 past the end of each matrix. A partial last
 // k-tile (K not a multiple of 16) must read as exact zeros past K, so it goes
 // through the guarded register path once after the loop.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int TA, int TB, int STAGES, int DMAB>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+// OCC: waves per SIMD the register allocation must allow (1 lets a wave use
+// all 512 registers of a lane; 2 caps it at 256 so two workgroups share a CU).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int TA, int TB, int STAGES, int DMAB, int OCC>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 sgemm_mfma_kernel(GemmParams p) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int NT = 64 * NW;
@@ -512,18 +514,18 @@ sgemm_mfma_kernel(GemmParams p) {
     (void)mn_interior;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int DMAB = 16>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int DMAB = 16, int OCC = 1>
 hipError_t launch_shape(int ta, int tb, const GemmParams& p, hipStream_t s) {
     const dim3 grid(p.tiles_m * p.tiles_n, (p.K + kBK * p.kt_per_split - 1) / (kBK * p.kt_per_split)),
         block(64 * WAVES_M * WAVES_N);
     if (ta == 0 && tb == 0)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 0, STAGES, DMAB>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 0, STAGES, DMAB, OCC>), grid, block, 0, s, p);
     else if (ta == 0 && tb == 1)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 1, STAGES, DMAB>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 1, STAGES, DMAB, OCC>), grid, block, 0, s, p);
     else if (ta == 1 && tb == 0)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 0, STAGES, DMAB>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 0, STAGES, DMAB, OCC>), grid, block, 0, s, p);
     else
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 1, STAGES, DMAB>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 1, STAGES, DMAB, OCC>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 
@@ -539,6 +541,10 @@ hipError_t launch_shape(int ta, int tb, const GemmParams& p, hipStream_t s) {
 //   6: 256 x 128, 2 x 1 waves of 128 x 128, 3-stage direct-to-LDS ring
 //   7: 128 x 128, 2 x 2 waves of  64 x  64, 4-stage direct-to-LDS ring
 //   8: as 7 with 4-byte direct-to-LDS loads (rows of any alignment)
+//   9: 256 x 256, 4 x 2 waves of  64 x 128, 4-stage direct-to-LDS ring
+//      (two waves per SIMD)
+//  10: 256 x 128, 2 x 2 waves of 128 x  64, 3-stage direct-to-LDS ring
+//      (two workgroups per CU)
 hipError_t launch_mfma(int variant, int ta, int tb, const GemmParams& p, hipStream_t s) {
     switch (variant) {
         case 0: return launch_shape<256, 256, 2, 2, 2>(ta, tb, p, s);
@@ -550,6 +556,8 @@ hipError_t launch_mfma(int variant, int ta, int tb, const GemmParams& p, hipStre
         case 6: return launch_shape<256, 128, 2, 1, 3>(ta, tb, p, s);
         case 7: return launch_shape<128, 128, 2, 2, 4>(ta, tb, p, s);
         case 8: return launch_shape<128, 128, 2, 2, 4, 4>(ta, tb, p, s);
+        case 9: return launch_shape<256, 256, 4, 2, 4>(ta, tb, p, s);
+        case 10: return launch_shape<256, 128, 2, 2, 3, 16, 2>(ta, tb, p, s);
         default: return hipErrorInvalidValue;
     }
 }
