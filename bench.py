@@ -69,12 +69,13 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False):
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     ws = torch.empty(64 << 20, dtype=torch.float32, device="cuda") if splitk else None
+    nsplit = int(splitk) if splitk and not isinstance(splitk, bool) else 0
 
     def step():
         if splitk:
             st = fg.fg_sgemm_splitk(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
                                     w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
-                                    0, ws.data_ptr(), ws.numel() * 4, sp)
+                                    nsplit, ws.data_ptr(), ws.numel() * 4, sp)
         else:
             st = fg.fg_sgemm_ex(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
                                 w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
@@ -146,7 +147,17 @@ def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False):
     w = wl.WORKLOADS[name]
     g = time_gpu(w, steps, warmup, config, splitk)
     tflops = w.flops / (g["ms_per_launch"] * 1e-3) / 1e12
+    gbs = w.compulsory_bytes / (g["ms_per_launch"] * 1e-3) / 1e9
     traffic = load_traffic(name, g["config"])
+    # Bound: the matrix core above the ridge point, HBM below it.
+    hbm_bound = w.flops / w.compulsory_bytes < PEAK_FP32_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP32_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_TFLOPS, 4),
+                "traffic": traffic}
     out = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -165,14 +176,20 @@ def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False):
                    "alpha": w.alpha, "beta": w.beta, "inputs": f"{w.dist} seed {w.seed}",
                    "kernel_config": g["config"]},
         "pct_of_fp32_peak": round(100 * tflops / PEAK_FP32_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
-                     "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_FP32_TFLOPS, 4),
-                     "traffic": traffic},
+        "hbm_gbs_compulsory": round(gbs, 1),
+        "roofline": roof,
     }
     if with_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     return out
+
+
+def _splitk_arg(args):
+    """False: fg_sgemm; True: fg_sgemm_splitk with a library-chosen split;
+    an int > 0: that many splits."""
+    if args.splitk is None:
+        return False
+    return True if args.splitk < 0 else args.splitk
 
 
 def main():
@@ -190,9 +207,9 @@ def main():
                          "(reference for scaling HBM traffic counters)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time every table entry on every workload (one line each)")
-    ap.add_argument("--splitk", action="store_true",
-                    help="with --suite: time fg_sgemm_splitk (library-chosen split, "
-                         "256 MiB workspace) instead of fg_sgemm")
+    ap.add_argument("--splitk", type=int, nargs="?", const=-1, default=None,
+                    help="time fg_sgemm_splitk (256 MiB workspace) instead of fg_sgemm; "
+                         "optional value = split count (default: library-chosen)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -209,16 +226,18 @@ def main():
 
     if args.suite or args.calibrate:
         ids = range(fg.fg_num_configs()) if args.calibrate else [args.config]
-        for name in ("C1", "C2", "C3", "C4", "C5a", "C5b", "C6"):
+        names = ("C1", "C2", "C3", "C4", "C5a", "C5b", "C6") + (("G1", "G1T", "G8") if args.suite else ())
+        for name in names:
             for cid in ids:
-                r = run_one(name, args.steps, args.warmup, False, cid, args.splitk)
+                r = run_one(name, args.steps, args.warmup, False, cid, _splitk_arg(args))
                 print(json.dumps({"workload": name, "config": r["config"]["kernel_config"],
-                                  "forced": cid, "splitk": args.splitk, "tflops": r["value"],
-                                  "ms": r["ms_per_step"], "pct": r["pct_of_fp32_peak"]}),
+                                  "forced": cid, "splitk": _splitk_arg(args), "tflops": r["value"],
+                                  "ms": r["ms_per_step"], "pct": r["pct_of_fp32_peak"],
+                                  "roofline": r["roofline"]}),
                       flush=True)
         return
 
-    r = run_one(args.workload, args.steps, args.warmup, False, args.config)
+    r = run_one(args.workload, args.steps, args.warmup, False, args.config, _splitk_arg(args))
     # The 4096^3 shape of the metric, timed in the same run.
     if args.workload == "C5a":
         r2 = run_one("C6", args.steps, args.warmup, False, args.config)

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libfp32gemm.so")
 
 FG_OP_N, FG_OP_T = 0, 1
 FG_OK, FG_ERR_INVALID_ARG, FG_ERR_HIP, FG_ERR_UNSUPPORTED = 0, 1, 2, 3
-FG_KIND_MFMA, FG_KIND_VALU = 1, 2
+FG_KIND_MFMA, FG_KIND_VALU, FG_KIND_SKINNY = 1, 2, 3
 FG_MAX_LD = 2097152
 
 

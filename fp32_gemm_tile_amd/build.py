@@ -22,7 +22,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp32gemm.so")
-SOURCES = ["fg_api.cpp", "sgemm_mfma.hip", "sgemm_valu.hip", "fg_elementwise.hip"]
+SOURCES = ["fg_api.cpp", "sgemm_mfma.hip", "sgemm_valu.hip", "sgemm_skinny.hip",
+           "fg_elementwise.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

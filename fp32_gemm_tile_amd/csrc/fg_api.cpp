@@ -77,7 +77,7 @@ Entry make_entry(int id, fg_kind kind, int variant, int bm, int bn, int bk, int 
     e.cfg.wn = wn;
     e.cfg.threads = threads;
     e.cfg.stages = stages;
-    e.cfg.lds_bytes = stages * (bm + bn) * bk * 4;
+    e.cfg.lds_bytes = kind == FG_KIND_SKINNY ? 4 * bm * 32 * 4 : stages * (bm + bn) * bk * 4;
     snprintf(e.cfg.name, sizeof e.cfg.name, "%s", name);
     e.variant = variant;
     e.wps = wps;
@@ -107,10 +107,13 @@ const Entry* table() {
         make_entry(10, FG_KIND_MFMA, 8, 128, 128, 16, 64, 64, 256, 4, 2, 0.881, "mfma_128x128x16_w2x2_s4_dw"),
         make_entry(11, FG_KIND_MFMA, 9, 256, 256, 16, 64, 128, 512, 4, 2, 0.90, "mfma_256x256x16_w4x2_s4", 0),
         make_entry(12, FG_KIND_MFMA, 10, 256, 128, 16, 128, 64, 256, 3, 2, 0.90, "mfma_256x128x16_w2x2_s3", 1),
+        // Few-row kernel: bm = rows per block (up to 8), bn = columns per
+        // workgroup for B stored K x N; memory-bound, costed separately.
+        make_entry(13, FG_KIND_SKINNY, 0, 8, 32, 0, 8, 4, 256, 0, 2, 1.0, "valu_skinny_m8"),
     };
     return t;
 }
-constexpr int kNumEntries = 13;
+constexpr int kNumEntries = 14;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -141,14 +144,25 @@ double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, boo
     int64_t share = cdiv(waves, simds);
     if (share > e.wps) share = e.wps;
     const double kpad = (double)kps * e.cfg.bk;
-    double t = (double)rounds * 2.0 * e.cfg.wm * e.cfg.wn * kpad * (double)share /
+    double t = kLaunch + (double)rounds * 2.0 * e.cfg.wm * e.cfg.wn * kpad * (double)share /
                (e.eff * kSimdFlops);
     if (s > 1)
         t += ((double)(2 * s + (beta0 ? 1 : 2)) * M * N * 4.0) / kHbmBytes + kLaunch;
     return t;
 }
 
-// Best MFMA entry (and split count, at most max_splits) for the call.
+// Few-row kernel: op(B) streamed once per block of 8 rows (a pessimistic
+// count when B stays in cache), or its vector-ALU flops, whichever is longer.
+constexpr double kValuFlops = 60e12;
+double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0) {
+    const double blocks = (double)cdiv(M, 8);
+    const double bytes = 4.0 * (blocks * K * N + (double)M * K + (double)M * N * (beta0 ? 1 : 2));
+    const double flops = 2.0 * M * N * K;
+    const double t = bytes / kHbmBytes > flops / kValuFlops ? bytes / kHbmBytes : flops / kValuFlops;
+    return kLaunch + t;
+}
+
+// Best MFMA or few-row entry (and split count, at most max_splits).
 int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_splits,
                  bool beta0, int64_t* best_splits) {
     static const int64_t kSplits[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
@@ -157,6 +171,18 @@ int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_s
     *best_splits = 1;
     for (int i = 0; i < kNumEntries; ++i) {
         const Entry& e = table()[i];
+        if (e.cfg.kind == FG_KIND_SKINNY) {
+            // Automatic use only for the few-row shapes it is built for; any
+            // M runs when forced.
+            if (M > 2 * e.cfg.bm) continue;
+            const double c = skinny_cost(M, N, K, beta0);
+            if (best < 0 || c < best_cost) {
+                best = i;
+                best_cost = c;
+                *best_splits = 1;
+            }
+            continue;
+        }
         if (e.cfg.kind != FG_KIND_MFMA) continue;
         if (e.fallback >= 0 && !ab_aligned) continue;
         for (int64_t sp : kSplits) {
@@ -170,6 +196,17 @@ int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_s
         }
     }
     return best;
+}
+
+// Tuning overrides (environment, read once): FG_FORCE_CONFIG=<id> forces a
+// table entry in calls that do not name one; FG_GROUP_M=<n> sets the raster
+// band height. For measurements only.
+int force_config_override() {
+    static int v = [] {
+        const char* s = getenv("FG_FORCE_CONFIG");
+        return s ? atoi(s) : -1;
+    }();
+    return v;
 }
 
 int group_m_override() {
@@ -352,6 +389,8 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
     if (max_splits < 1) max_splits = 1;
     int64_t want = splits;
     int idx;
+    if (config_id < 0 && force_config_override() >= 0 && force_config_override() < kNumEntries)
+        config_id = force_config_override();
     if (config_id >= 0) {
         idx = config_id;
         if (want == 0) want = 1;
@@ -368,7 +407,9 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
     if (en.cfg.kind != FG_KIND_MFMA) want = 1;  // split-K runs on the MFMA kernels
 
     int64_t kps = 0;
-    const int64_t nsplit = effective_splits(K, en.cfg.bk, want, &kps);
+    // k-tile depth of the MFMA kernels; the other kinds ignore the split.
+    const int64_t split_bk = en.cfg.kind == FG_KIND_MFMA ? en.cfg.bk : 16;
+    const int64_t nsplit = effective_splits(K, split_bk, want, &kps);
     if (nsplit > 1 && nsplit > max_splits)
         return fail(FG_ERR_INVALID_ARG, 16, "workspace of %zu bytes holds %lld splits, need %lld",
                     ws_bytes, (long long)max_splits, (long long)nsplit);
@@ -401,6 +442,8 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
         if (e == hipSuccess) e = fg::launch_splitk_reduce(ws, (int32_t)nsplit, p, stream);
     } else if (en.cfg.kind == FG_KIND_MFMA) {
         e = fg::launch_mfma(en.variant, transA, transB, p, stream);
+    } else if (en.cfg.kind == FG_KIND_SKINNY) {
+        e = fg::launch_skinny(transA, transB, p, stream);
     } else {
         e = fg::launch_valu(en.variant, transA, transB, p, stream);
     }

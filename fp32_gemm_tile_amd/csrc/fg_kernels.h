@@ -46,6 +46,9 @@ hipError_t launch_mfma(int variant, int trans_a, int trans_b, const GemmParams& 
                        hipStream_t stream);
 hipError_t launch_valu(int variant, int trans_a, int trans_b, const GemmParams& p,
                        hipStream_t stream);
+// Few-row GEMM (memory-bound): blocks of up to 8 rows of C, op(B) streamed
+// once per block.
+hipError_t launch_skinny(int trans_a, int trans_b, const GemmParams& p, hipStream_t stream);
 // C = beta * C (beta == 0: C = 0 without reading it); for K == 0 or alpha == 0.
 hipError_t launch_scale(const GemmParams& p, hipStream_t stream);
 // Split-K reduction: C = alpha * sum_{s < splits} W_s + beta * C, where W_s is

@@ -1,0 +1,258 @@
+// SGEMM for few rows of C (M small: the decode shape of "Matmul II: register
+// blocking, warp tiling, tensor cores", section 8, where the kernel is a
+// memory-bound GEMV and the game is bytes).
+//
+// With M <= 8 the product reads every element of op(B) once and does only
+// 2*M flops per element, so the bound is HBM bandwidth, not the matrix
+// cores: this kernel streams op(B) with coalesced 128-bit loads, keeps MR
+// (1, 2, 4 or 8) rows of results per thread in registers, and reduces the
+// per-thread partial sums in a fixed order (deterministic results). Larger M
+// runs as ceil(M / MR) row blocks (blockIdx.y), each streaming op(B) again.
+//
+// Two layouts of op(B):
+//   * B stored K x N (n contiguous): a workgroup owns 32 columns; lane
+//     (g = lane % 8) loads columns 4g..4g+3 of one k row, the 32 lane-rows
+//     of the workgroup (8 per wave) step through k together, so each wave
+//     load covers 8 rows x 128 contiguous bytes. Partial sums over the 32
+//     k classes are reduced with lane shuffles, then across waves in LDS.
+//   * B stored N x K (k contiguous): a wave owns 4 columns and its 64 lanes
+//     read 256 consecutive k of each (one 1 KiB load per column); the 64
+//     lane partials of every (row, column) are reduced with shuffles.
+// op(A) is read with ordinary (cached) loads: it is M x K, small next to B.
+// Every global access goes through a buffer resource bounded by the matrix.
+#include "fg_device.h"
+
+namespace fg {
+namespace {
+
+constexpr int kSkinnyThreads = 256;
+constexpr int kUnrollMN = 8;  // k steps in flight per lane (B stored K x N)
+constexpr int kUnrollK = 2;   // 256-deep k blocks in flight per column (B stored N x K)
+
+// op(A)(i, k) for the rows of this block; rows past M read as 0.
+template <int MR, bool TA>
+__device__ __forceinline__ void load_a(__amdgpu_buffer_rsrc_t ra, int lda, int rows_left, int k,
+                                       float (&a)[MR]) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const uint32_t off = (uint32_t)(TA ? k * lda + m : m * lda + k) * 4u;
+        a[m] = m < rows_left ? ld1(ra, off) : 0.f;
+    }
+}
+
+// Sum of v over the lanes whose index differs only in the bits of `mask`
+// (xor butterfly; every lane of a group ends with the same value).
+template <int MASK>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+        if (MASK & o) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+template <int MR, int TA, bool VEC>
+__global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p) {
+    // B stored K x N. Workgroup: columns [n0, n0 + 32), rows [m0, m0 + MR).
+    constexpr int NW = kSkinnyThreads / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane & 7;                 // column group: 4 columns
+    const int rcls = (lane >> 3) + 8 * wave;  // k class 0..31
+    const int n0 = blockIdx.x * 32, m0 = blockIdx.y * MR;
+    const int rows_left = p.M - m0, cols_left = p.N - n0 - 4 * g;
+
+    float acc[MR][4];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[m][j] = 0.f;
+
+    for (int kb = 0; kb < p.K; kb += 32 * kUnrollMN) {
+        // Buffer resources based at this k block keep the 32-bit offsets small.
+        const int64_t a_org = TA ? (int64_t)kb * p.lda + m0 : (int64_t)m0 * p.lda + kb;
+        const int64_t b_org = (int64_t)kb * p.ldb + n0;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_org, p.b_extent - b_org);
+        f4 b[kUnrollMN];
+#pragma unroll
+        for (int u = 0; u < kUnrollMN; ++u) {
+            const int kk = rcls + 32 * u;  // k - kb
+            const uint32_t off = (uint32_t)(kk * p.ldb + 4 * g) * 4u;
+            const f4 z = {0.f, 0.f, 0.f, 0.f};
+            b[u] = kb + kk < p.K ? ld4_guard(rb, off, 4 * g, p.N - n0, VEC) : z;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnrollMN; ++u) {
+            const int kk = rcls + 32 * u;
+            float a[MR];
+            if (kb + kk < p.K) {
+                load_a<MR, TA>(ra, p.lda, rows_left, kk, a);
+            } else {
+#pragma unroll
+                for (int m = 0; m < MR; ++m) a[m] = 0.f;
+            }
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[m][j] = __builtin_fmaf(a[m], b[u][j], acc[m][j]);
+        }
+    }
+
+    // Reduce over the 8 k classes of a wave (lane bits 3-5), then over the
+    // waves through LDS, always in the same order.
+    __shared__ float red[NW][MR][32];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float s = group_sum<0x38>(acc[m][j]);
+            if (lane < 8) red[wave][m][4 * g + j] = s;
+        }
+    __syncthreads();
+    if (wave == 0 && lane < 8) {
+        const int64_t c_org = (int64_t)m0 * p.ldc + n0;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c_org, p.c_extent - c_org);
+        const bool beta0 = p.flags & FLAG_BETA0;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            if (m >= rows_left) break;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j >= cols_left) break;
+                float s = red[0][m][4 * g + j];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) s += red[w][m][4 * g + j];
+                const uint32_t off = (uint32_t)(m * p.ldc + 4 * g + j) * 4u;
+                float o = p.alpha * s;
+                if (!beta0) o += p.beta * ld1(rc, off);
+                st1(rc, off, o);
+            }
+        }
+    }
+}
+
+template <int MR, int TA, bool VEC>
+__global__ void __launch_bounds__(kSkinnyThreads) skinny_k_kernel(GemmParams p) {
+    // B stored N x K. Wave w of the workgroup: columns n0 + 4w .. n0 + 4w + 3,
+    // rows [m0, m0 + MR); lane L reads k = kb + 4L .. 4L + 3 of each column.
+    constexpr int NW = kSkinnyThreads / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n0 = (blockIdx.x * NW + wave) * 4, m0 = blockIdx.y * MR;
+    const int rows_left = p.M - m0, cols_left = p.N - n0;
+
+    const bool vec_a = !TA && (p.flags & FLAG_VEC_A);
+    float acc[MR][4];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[m][c] = 0.f;
+
+    for (int kb = 0; kb < p.K; kb += 256 * kUnrollK) {
+        // Buffer resources based at this k block keep the 32-bit offsets small.
+        const int64_t a_org = TA ? (int64_t)kb * p.lda + m0 : (int64_t)m0 * p.lda + kb;
+        const int64_t b_org = (int64_t)n0 * p.ldb + kb;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_org, p.b_extent - b_org);
+        const int k_left = p.K - kb;
+        f4 b[kUnrollK][4];
+#pragma unroll
+        for (int u = 0; u < kUnrollK; ++u) {
+            const int kk = 256 * u + 4 * lane;  // k - kb
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const f4 z = {0.f, 0.f, 0.f, 0.f};
+                const uint32_t off = (uint32_t)(c * p.ldb + kk) * 4u;
+                b[u][c] = c < cols_left ? ld4_guard(rb, off, kk, k_left, VEC) : z;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnrollK; ++u) {
+            const int kk = 256 * u + 4 * lane;
+            f4 a[MR];
+            if (vec_a) {
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    const f4 z = {0.f, 0.f, 0.f, 0.f};
+                    a[m] = m < rows_left ? ld4_guard(ra, (uint32_t)(m * p.lda + kk) * 4u, kk,
+                                                     k_left, true)
+                                         : z;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float t[MR];
+                    if (kk + e < k_left) {
+                        load_a<MR, TA>(ra, p.lda, rows_left, kk + e, t);
+                    } else {
+#pragma unroll
+                        for (int m = 0; m < MR; ++m) t[m] = 0.f;
+                    }
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) a[m][e] = t[m];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[m][c] = __builtin_fmaf(a[m][e], b[u][c][e], acc[m][c]);
+        }
+    }
+
+    const int64_t c_org = (int64_t)m0 * p.ldc + n0;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c_org, p.c_extent - c_org);
+    const bool beta0 = p.flags & FLAG_BETA0;
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float s = group_sum<0x3F>(acc[m][c]);
+            if (lane == 0 && m < rows_left && c < cols_left) {
+                const uint32_t off = (uint32_t)(m * p.ldc + c) * 4u;
+                float o = p.alpha * s;
+                if (!beta0) o += p.beta * ld1(rc, off);
+                st1(rc, off, o);
+            }
+        }
+}
+
+template <int MR>
+hipError_t launch_mr(int ta, int tb, const GemmParams& p, hipStream_t s) {
+    const bool vec_b = p.flags & FLAG_VEC_B;
+    const int rblocks = (p.M + MR - 1) / MR;
+    const dim3 block(kSkinnyThreads);
+    if (tb == 0) {  // B stored K x N
+        const dim3 grid((p.N + 31) / 32, rblocks);
+        if (ta == 0) {
+            if (vec_b) hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, true>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, false>), grid, block, 0, s, p);
+        } else {
+            if (vec_b) hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, true>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, false>), grid, block, 0, s, p);
+        }
+    } else {  // B stored N x K
+        const int cols_per_wg = 4 * (kSkinnyThreads / 64);
+        const dim3 grid((p.N + cols_per_wg - 1) / cols_per_wg, rblocks);
+        if (ta == 0) {
+            if (vec_b) hipLaunchKernelGGL((skinny_k_kernel<MR, 0, true>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((skinny_k_kernel<MR, 0, false>), grid, block, 0, s, p);
+        } else {
+            if (vec_b) hipLaunchKernelGGL((skinny_k_kernel<MR, 1, true>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((skinny_k_kernel<MR, 1, false>), grid, block, 0, s, p);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Rows per block: 1, 2, 4 or 8 (the smallest power of two >= M, capped at 8).
+hipError_t launch_skinny(int ta, int tb, const GemmParams& p, hipStream_t s) {
+    if (p.M <= 1) return launch_mr<1>(ta, tb, p, s);
+    if (p.M <= 2) return launch_mr<2>(ta, tb, p, s);
+    if (p.M <= 4) return launch_mr<4>(ta, tb, p, s);
+    return launch_mr<8>(ta, tb, p, s);
+}
+
+}  // namespace fg

@@ -99,6 +99,11 @@ WORKLOADS = {
                     note="8192^3 NT, same buffers as C5a"),
     "C6": Workload("C6", 4096, 4096, 4096, seed=5,
                    note="4096^3 NN (headline)"),
+    # Few-row (decode) shapes, memory-bound; seeds are this project's choice.
+    "G1": Workload("G1", 1, 8192, 8192, seed=6, note="GEMV: 1 x 8192 times 8192 x 8192"),
+    "G1T": Workload("G1T", 1, 8192, 8192, transB="T", seed=6,
+                    note="GEMV with B stored N x K"),
+    "G8": Workload("G8", 8, 8192, 8192, seed=7, note="8 rows times 8192 x 8192"),
 }
 
 

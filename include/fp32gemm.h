@@ -62,8 +62,10 @@ typedef enum fg_status {
 
 /* Kernel families. */
 typedef enum fg_kind {
-    FG_KIND_MFMA = 1, /* matrix-core contraction, v_mfma_f32_32x32x2_f32 */
-    FG_KIND_VALU = 2  /* vector-ALU v_fma_f32 outer products (comparison path) */
+    FG_KIND_MFMA = 1,  /* matrix-core contraction, v_mfma_f32_32x32x2_f32 */
+    FG_KIND_VALU = 2,  /* vector-ALU v_fma_f32 outer products (comparison path) */
+    FG_KIND_SKINNY = 3 /* few rows of C: streams op(B) once per block of up to 8
+                          rows, memory-bound (the GEMV shape) */
 } fg_kind;
 
 /* Largest leading dimension (elements) the kernels address with 32-bit
@@ -74,7 +76,8 @@ typedef enum fg_kind {
 typedef struct fg_config {
     int32_t id;        /* position in the table (0 .. fg_num_configs()-1) */
     int32_t kind;      /* fg_kind */
-    int32_t bm, bn;    /* output tile of one workgroup */
+    int32_t bm, bn;    /* output tile of one workgroup (FG_KIND_SKINNY: rows per
+                          block, and columns per workgroup when B is K x N) */
     int32_t bk;        /* depth of one k-tile staged in LDS */
     int32_t wm, wn;    /* output tile of one wavefront (MFMA) or thread (VALU) */
     int32_t threads;   /* work-items per workgroup */

@@ -78,9 +78,10 @@ def test_config_table():
     cfgs = fg.configs()
     assert [c["id"] for c in cfgs] == list(range(n))
     kinds = {c["kind"] for c in cfgs}
-    assert kinds == {fg.FG_KIND_MFMA, fg.FG_KIND_VALU}
+    assert kinds == {fg.FG_KIND_MFMA, fg.FG_KIND_VALU, fg.FG_KIND_SKINNY}
     for c in cfgs:
-        assert c["bm"] > 0 and c["bn"] > 0 and c["bk"] > 0 and c["threads"] % 64 == 0
+        assert c["bm"] > 0 and c["bn"] > 0 and c["threads"] % 64 == 0
+        assert c["bk"] > 0 or c["kind"] == fg.FG_KIND_SKINNY
         assert c["lds_bytes"] <= 160 * 1024
         if c["kind"] == fg.FG_KIND_MFMA:
             assert c["wm"] % 32 == 0 and c["wn"] % 32 == 0
@@ -89,10 +90,19 @@ def test_config_table():
         fg.fg_get_config(n)
 
 
+def test_few_rows_select_the_memory_bound_kernel():
+    for M in (1, 2, 8):
+        c = fg.fg_select_config("N", "N", M, 8192, 8192)
+        assert c["kind"] == fg.FG_KIND_SKINNY, (M, c)
+        c = fg.fg_select_config("N", "T", M, 8192, 8192)
+        assert c["kind"] == fg.FG_KIND_SKINNY, (M, c)
+    assert fg.fg_select_config("N", "N", 4096, 4096, 4096)["kind"] == fg.FG_KIND_MFMA
+
+
 def test_selection_is_mfma_and_scales_with_shape():
     big = fg.fg_select_config("N", "N", 8192, 8192, 8192)
     assert big["kind"] == fg.FG_KIND_MFMA and big["bm"] * big["bn"] >= 256 * 128
-    small = fg.fg_select_config("N", "N", 256, 256, 256)
+    small = fg.fg_select_config("N", "N", 512, 512, 512)
     assert small["kind"] == fg.FG_KIND_MFMA
     assert small["bm"] * small["bn"] < big["bm"] * big["bn"]
     ragged = fg.fg_select_config("T", "N", 3001, 2047, 1025, lda=3001, ldb=2047, ldc=2047)
@@ -190,3 +200,31 @@ def test_splitk_auto_with_workspace_too_small_for_any_split():
     st = fg.fg_sgemm_splitk(0, 0, 4096, 4096, 256, 1.0, 16, 256, 16, 4096, 0.0, 16, 4096, 0,
                             4096, 1024, 0)
     assert st in (fg.FG_ERR_HIP, fg.FG_ERR_UNSUPPORTED, fg.FG_OK)
+
+
+@pytest.mark.parametrize("splits", [None, 0, 3])
+def test_host_planner_handles_every_entry(splits):
+    """Every table entry, forced, and split-K planning run through the host
+    planner without crashing; without a GPU each call stops at the device
+    check (FG_ERR_HIP or FG_ERR_UNSUPPORTED)."""
+    import subprocess
+    import sys
+    code = f"""
+import sys; sys.path.insert(0, {ROOT!r})
+import fp32_gemm_tile_amd as fg
+ok = (fg.FG_ERR_HIP, fg.FG_ERR_UNSUPPORTED, fg.FG_OK)
+for cid in range(fg.fg_num_configs()):
+    for (M, N, K) in [(1, 1, 1), (8, 8192, 8192), (300, 257, 1025), (4096, 4096, 4096)]:
+        st = fg.fg_sgemm_ex(0, 1, M, N, K, 1.0, 16, K, 16, K, 0.0, 16, N, 0, cid)
+        assert st in ok, (cid, M, N, K, st)
+for (M, N, K) in [(1, 1, 1), (8, 8192, 8192), (256, 256, 256), (300, 257, 1025)]:
+    s = {splits!r}
+    if s is None:
+        st = fg.fg_sgemm(0, 0, M, N, K, 1.0, 16, K, 16, N, 0.5, 16, N, 0)
+    else:
+        st = fg.fg_sgemm_splitk(0, 0, M, N, K, 1.0, 16, K, 16, N, 0.5, 16, N, s, 4096, 1 << 30, 0)
+    assert st in ok, (M, N, K, st)
+print("ok")
+"""
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "ok" in r.stdout, (r.returncode, r.stderr[-1500:])
