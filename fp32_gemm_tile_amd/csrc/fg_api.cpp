@@ -153,7 +153,7 @@ double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, boo
 
 // Few-row kernel: op(B) streamed once per block of 8 rows (a pessimistic
 // count when B stays in cache), or its vector-ALU flops, whichever is longer.
-constexpr double kValuFlops = 60e12;
+constexpr double kValuFlops = 35e12;  // measured rate with 8-row blocks
 double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0) {
     const double blocks = (double)cdiv(M, 8);
     const double bytes = 4.0 * (blocks * K * N + (double)M * K + (double)M * N * (beta0 ? 1 : 2));
@@ -162,9 +162,10 @@ double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0) {
     return kLaunch + t;
 }
 
-// Best MFMA or few-row entry (and split count, at most max_splits).
+// Best MFMA or few-row entry (and split count, at most max_splits). With
+// mfma_only (the caller asked for a split), only the MFMA kernels compete.
 int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_splits,
-                 bool beta0, int64_t* best_splits) {
+                 bool beta0, int64_t* best_splits, bool mfma_only = false) {
     static const int64_t kSplits[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
     int best = -1;
     double best_cost = 0;
@@ -172,9 +173,7 @@ int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_s
     for (int i = 0; i < kNumEntries; ++i) {
         const Entry& e = table()[i];
         if (e.cfg.kind == FG_KIND_SKINNY) {
-            // Automatic use only for the few-row shapes it is built for; any
-            // M runs when forced.
-            if (M > 2 * e.cfg.bm) continue;
+            if (mfma_only) continue;
             const double c = skinny_cost(M, N, K, beta0);
             if (best < 0 || c < best_cost) {
                 best = i;
@@ -396,8 +395,8 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
         if (want == 0) want = 1;
     } else {
         int64_t auto_splits = 1;
-        idx = select_entry(M, N, K, ab_aligned, want == 0 ? max_splits : 1, beta == 0.0f,
-                           &auto_splits);
+        idx = select_entry(M, N, K, ab_aligned, want == 0 ? max_splits : want, beta == 0.0f,
+                           &auto_splits, want > 1);
         if (want == 0) want = auto_splits;
     }
     if (idx < 0 || idx >= kNumEntries)

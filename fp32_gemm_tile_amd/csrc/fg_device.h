@@ -64,6 +64,14 @@ __device__ __forceinline__ f4 ld4_guard(__amdgpu_buffer_rsrc_t r, uint32_t off,
     return v;
 }
 
+// Barrier after this wave's LDS writes have completed, without the memory
+// fence of __syncthreads() (which would also wait for every outstanding global
+// load). gfx9 s_waitcnt encoding: lgkmcnt = 0, vmcnt and expcnt at maximum.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // Workgroup id -> (tile_m, tile_n).
 //
 // 1. XCD remap: consecutive workgroup ids are handed to the 8 XCDs in turn,

@@ -66,12 +66,33 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[m][j] = 0.f;
 
-    for (int kb = 0; kb < p.K; kb += 32 * kUnrollMN) {
+    // With several rows, the block's op(A) values go through LDS: thread t
+    // loads k = kb + t of every row once (coalesced for A stored M x K) and
+    // each lane then reads the MR values of its k with 128-bit LDS reads,
+    // instead of MR scattered global loads per k. Two buffers: one barrier
+    // per k block.
+    constexpr int KB = 32 * kUnrollMN;  // k per block
+    constexpr bool STAGE_A = MR > 1;
+    __shared__ __attribute__((aligned(16))) float sa[STAGE_A ? 2 : 1][KB][MR];
+
+    int it = 0;
+    for (int kb = 0; kb < p.K; kb += KB, ++it) {
         // Buffer resources based at this k block keep the 32-bit offsets small.
         const int64_t a_org = TA ? (int64_t)kb * p.lda + m0 : (int64_t)m0 * p.lda + kb;
         const int64_t b_org = (int64_t)kb * p.ldb + n0;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_org, p.b_extent - b_org);
+        float astage[MR];
+        if constexpr (STAGE_A) {
+            // Issued before the B loads so waiting for them leaves B in flight.
+            const int kk = threadIdx.x;
+            if (kb + kk < p.K) {
+                load_a<MR, TA>(ra, p.lda, rows_left, kk, astage);
+            } else {
+#pragma unroll
+                for (int m = 0; m < MR; ++m) astage[m] = 0.f;
+            }
+        }
         f4 b[kUnrollMN];
 #pragma unroll
         for (int u = 0; u < kUnrollMN; ++u) {
@@ -80,11 +101,29 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
             const f4 z = {0.f, 0.f, 0.f, 0.f};
             b[u] = kb + kk < p.K ? ld4_guard(rb, off, 4 * g, p.N - n0, VEC) : z;
         }
+        if constexpr (STAGE_A) {
+            float* dst = &sa[it & 1][threadIdx.x][0];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) dst[m] = astage[m];
+            lds_barrier();
+        }
 #pragma unroll
         for (int u = 0; u < kUnrollMN; ++u) {
             const int kk = rcls + 32 * u;
             float a[MR];
-            if (kb + kk < p.K) {
+            if constexpr (STAGE_A) {
+                const float* src = &sa[it & 1][kk][0];
+#pragma unroll
+                for (int m = 0; m < MR; m += 4) {
+                    if constexpr (MR >= 4) {
+                        const f4 v = *reinterpret_cast<const f4*>(src + m);
+                        a[m] = v[0]; a[m + 1] = v[1]; a[m + 2] = v[2]; a[m + 3] = v[3];
+                    } else {
+                        const f2 v = *reinterpret_cast<const f2*>(src);
+                        a[0] = v[0]; a[1] = v[1];
+                    }
+                }
+            } else if (kb + kk < p.K) {
                 load_a<MR, TA>(ra, p.lda, rows_left, kk, a);
             } else {
 #pragma unroll
@@ -100,6 +139,7 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
     // Reduce over the 8 k classes of a wave (lane bits 3-5), then over the
     // waves through LDS, always in the same order.
     __shared__ float red[NW][MR][32];
+    static_assert(KB == kSkinnyThreads, "one staged k per thread");
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll

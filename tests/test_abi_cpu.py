@@ -102,9 +102,13 @@ def test_few_rows_select_the_memory_bound_kernel():
 def test_selection_is_mfma_and_scales_with_shape():
     big = fg.fg_select_config("N", "N", 8192, 8192, 8192)
     assert big["kind"] == fg.FG_KIND_MFMA and big["bm"] * big["bn"] >= 256 * 128
-    small = fg.fg_select_config("N", "N", 512, 512, 512)
-    assert small["kind"] == fg.FG_KIND_MFMA
-    assert small["bm"] * small["bn"] < big["bm"] * big["bn"]
+    mid = fg.fg_select_config("N", "N", 2048, 2048, 2048)
+    assert mid["kind"] == fg.FG_KIND_MFMA
+    assert mid["bm"] * mid["bn"] < big["bm"] * big["bn"]
+    # A few rows of C, or a grid of output tiles far too small for 256 CUs,
+    # go to the few-row kernel; the comparison kernel is never picked.
+    for shape in ((1, 8192, 8192), (8, 4096, 4096), (256, 256, 256), (512, 512, 512)):
+        assert fg.fg_select_config("N", "N", *shape)["kind"] == fg.FG_KIND_SKINNY, shape
     ragged = fg.fg_select_config("T", "N", 3001, 2047, 1025, lda=3001, ldb=2047, ldc=2047)
     assert ragged["kind"] == fg.FG_KIND_MFMA
     # entries with 16-byte direct-to-LDS loads need 16-byte aligned rows of A
