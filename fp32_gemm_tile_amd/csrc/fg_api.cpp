@@ -16,7 +16,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <mutex>
 
 #include "../../include/fp32gemm.h"
@@ -54,7 +56,8 @@ struct Entry {
     fg_config cfg;
     int variant;   // index inside the kernel family's launcher
     int wps;       // resident waves per SIMD
-    double eff;    // relative efficiency for the cost model
+    double eff;    // relative efficiency for the cost model, SIMD full
+    double eff1;   // the same with one wave per SIMD (small grids)
     int fallback;  // entry used instead when A or B rows are not 16-byte
                    // aligned (entries with 16-byte direct-to-LDS loads only;
                    // -1 = any alignment is fine)
@@ -65,7 +68,7 @@ constexpr int kSimdsPerCU = 4;
 
 Entry make_entry(int id, fg_kind kind, int variant, int bm, int bn, int bk, int wm, int wn,
                  int threads, int stages, int wps, double eff, const char* name,
-                 int fallback = -1) {
+                 int fallback = -1, double eff1 = 0) {
     Entry e;
     memset(&e, 0, sizeof e);
     e.cfg.id = id;
@@ -82,6 +85,7 @@ Entry make_entry(int id, fg_kind kind, int variant, int bm, int bn, int bk, int 
     e.variant = variant;
     e.wps = wps;
     e.eff = eff;
+    e.eff1 = eff1 > 0 ? eff1 : eff;
     e.fallback = fallback;
     return e;
 }
@@ -110,20 +114,25 @@ const Entry* table() {
         // Few-row kernel: bm = rows per block (up to 8), bn = columns per
         // workgroup for B stored K x N; memory-bound, costed separately.
         make_entry(13, FG_KIND_SKINNY, 0, 8, 32, 0, 8, 4, 256, 0, 2, 1.0, "valu_skinny_m8"),
+        // Small tiles for grids the entries above leave under-filled; several
+        // workgroups share a CU.
+        // eff1: measured with one workgroup per CU (M <= 256, N = K = 4096).
+        make_entry(14, FG_KIND_MFMA, 11, 64, 64, 16, 32, 32, 256, 4, 5, 0.75, "mfma_64x64x16_w2x2_s4", 15, 0.57),
+        make_entry(15, FG_KIND_MFMA, 12, 64, 64, 16, 32, 32, 256, 4, 5, 0.72, "mfma_64x64x16_w2x2_s4_dw", -1, 0.55),
+        make_entry(16, FG_KIND_MFMA, 13, 128, 64, 16, 64, 32, 256, 4, 3, 0.80, "mfma_128x64x16_w2x2_s4", 15, 0.74),
     };
     return t;
 }
-constexpr int kNumEntries = 14;
+constexpr int kNumEntries = 17;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Estimated time in seconds of the call with MFMA entry e and `splits`
-// split-K slices: rounds of resident waves times the time of one wave tile
-// (which grows with the number of waves sharing a SIMD), plus, with split-K,
-// the partial slices written, read back and reduced at HBM speed.
+// split-K slices: the rounds of resident waves the grid needs, plus, with
+// split-K, the partial slices written, read back and reduced at HBM speed.
 constexpr double kSimdFlops = 157.3e12 / (kNumCUs * kSimdsPerCU);  // fp32 MFMA per SIMD
 constexpr double kHbmBytes = 5.0e12;                              // sustained, not peak
-constexpr double kLaunch = 4e-6;                                  // one more kernel
+constexpr double kLaunch = 3e-6;                                  // one more kernel
 
 int64_t effective_splits(int64_t K, int64_t bk, int64_t splits, int64_t* kt_per_split) {
     const int64_t kt_total = cdiv(K, bk);
@@ -138,28 +147,44 @@ double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, boo
     int64_t kps = 0;
     const int64_t s = effective_splits(K, e.cfg.bk, splits, &kps);
     const int64_t tiles = cdiv(M, e.cfg.bm) * cdiv(N, e.cfg.bn);
-    const int64_t waves = tiles * (e.cfg.threads / 64) * s;
     const int64_t simds = (int64_t)kNumCUs * kSimdsPerCU;
-    const int64_t rounds = cdiv(waves, simds * e.wps);
-    int64_t share = cdiv(waves, simds);
-    if (share > e.wps) share = e.wps;
-    const double kpad = (double)kps * e.cfg.bk;
-    double t = kLaunch + (double)rounds * 2.0 * e.cfg.wm * e.cfg.wn * kpad * (double)share /
-               (e.eff * kSimdFlops);
+    const double wave_flops = 2.0 * e.cfg.wm * e.cfg.wn * (double)kps * e.cfg.bk;
+    // Rounds of resident waves: each round puts up to wps waves on every
+    // SIMD; the last round may hold fewer. A SIMD shared by `share` waves
+    // finishes them after share * wave_flops at an efficiency that grows
+    // from eff1 (one wave: little latency hiding) to eff (wps waves).
+    double t = kLaunch;
+    for (int64_t left = tiles * (e.cfg.threads / 64) * s; left > 0;) {
+        int64_t share = cdiv(left, simds);
+        if (share > e.wps) share = e.wps;
+        const double eff =
+            e.wps > 1 ? e.eff1 + (e.eff - e.eff1) * (double)(share - 1) / (e.wps - 1) : e.eff;
+        t += wave_flops * (double)share / (eff * kSimdFlops);
+        left -= share * simds;
+    }
     if (s > 1)
         t += ((double)(2 * s + (beta0 ? 1 : 2)) * M * N * 4.0) / kHbmBytes + kLaunch;
     return t;
 }
 
-// Few-row kernel: op(B) streamed once per block of 8 rows (a pessimistic
-// count when B stays in cache), or its vector-ALU flops, whichever is longer.
-constexpr double kValuFlops = 35e12;  // measured rate with 8-row blocks
+// Few-row kernel, fitted to measurements on one MI355X: a workgroup owns 32
+// columns of C for one block of up to 8 rows and walks K in steps of 32 rows
+// of op(B). One workgroup per CU is latency-bound (a step takes 0.17 us with
+// one row, 0.27 us with eight); with several per CU the CU's throughput
+// (0.1 us per workgroup-step) takes over. op(B) crosses HBM at least once.
+// The fixed cost covers the launch and the final cross-wave reduction.
+constexpr double kSkinnyFixed = 7e-6;
+constexpr double kHbmPeakish = 6.3e12;  // best streaming rate measured (GEMV)
 double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0) {
+    const int64_t rows = M < 8 ? M : 8;
     const double blocks = (double)cdiv(M, 8);
-    const double bytes = 4.0 * (blocks * K * N + (double)M * K + (double)M * N * (beta0 ? 1 : 2));
-    const double flops = 2.0 * M * N * K;
-    const double t = bytes / kHbmBytes > flops / kValuFlops ? bytes / kHbmBytes : flops / kValuFlops;
-    return kLaunch + t;
+    const double wgs = blocks * (double)cdiv(N, 32);
+    const double steps = (double)cdiv(K, 32);
+    const double per_cu = std::ceil(wgs / kNumCUs);
+    const double t_lat = steps * (0.17e-6 + (double)(rows - 1) * 0.0143e-6);
+    const double t_thr = per_cu * steps * 0.1e-6;
+    const double bytes = 4.0 * ((double)K * N + (double)M * K + (double)M * N * (beta0 ? 1 : 2));
+    return kSkinnyFixed + std::max(std::max(t_lat, t_thr), bytes / kHbmPeakish);
 }
 
 // Best MFMA or few-row entry (and split count, at most max_splits). With

@@ -389,19 +389,24 @@ sgemm_mfma_kernel(GemmParams p) {
             // first MFMAs, then the fragment reads one per MFMA, then the rest
             // of the MFMAs, so that the reads have landed long before the
             // closing wait and the matrix core never waits on memory.
+            // Small wave tiles (32 x 32) have fewer MFMAs than memory
+            // instructions per k-tile; there the compiler's order stands.
             constexpr int kMfma = (kBK / 2) * MB * NB;
             constexpr int kReads = read_count<MB, A_MN>() + read_count<NB, B_MN>();
+            if constexpr (NI + kReads <= kMfma) {
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM (DMA)
-            }
+                for (int i = 0; i < NI; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM (DMA)
+                }
 #pragma unroll
-            for (int i = 0; i < kReads; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                for (int i = 0; i < kReads; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                }
+                if constexpr (kMfma > NI + kReads)
+                    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - NI - kReads, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, kMfma - NI - kReads, 0);
             wait_vm_lds<(NS - 3) * NI>();
             barrier_no_fence();
         };
@@ -545,6 +550,10 @@ hipError_t launch_shape(int ta, int tb, const GemmParams& p, hipStream_t s) {
 //      (two waves per SIMD)
 //  10: 256 x 128, 2 x 2 waves of 128 x  64, 3-stage direct-to-LDS ring
 //      (two workgroups per CU)
+//  11:  64 x  64, 2 x 2 waves of  32 x  32, 4-stage direct-to-LDS ring
+//      (several workgroups per CU: grids too small for the large tiles)
+//  12: as 11 with 4-byte direct-to-LDS loads
+//  13: 128 x  64, 2 x 2 waves of  64 x  32, 4-stage direct-to-LDS ring
 hipError_t launch_mfma(int variant, int ta, int tb, const GemmParams& p, hipStream_t s) {
     switch (variant) {
         case 0: return launch_shape<256, 256, 2, 2, 2>(ta, tb, p, s);
@@ -558,6 +567,9 @@ hipError_t launch_mfma(int variant, int ta, int tb, const GemmParams& p, hipStre
         case 8: return launch_shape<128, 128, 2, 2, 4, 4>(ta, tb, p, s);
         case 9: return launch_shape<256, 256, 4, 2, 4>(ta, tb, p, s);
         case 10: return launch_shape<256, 128, 2, 2, 3, 16, 2>(ta, tb, p, s);
+        case 11: return launch_shape<64, 64, 2, 2, 4, 16, 2>(ta, tb, p, s);
+        case 12: return launch_shape<64, 64, 2, 2, 4, 4, 2>(ta, tb, p, s);
+        case 13: return launch_shape<128, 64, 2, 2, 4, 16, 2>(ta, tb, p, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -105,10 +105,13 @@ def test_selection_is_mfma_and_scales_with_shape():
     mid = fg.fg_select_config("N", "N", 2048, 2048, 2048)
     assert mid["kind"] == fg.FG_KIND_MFMA
     assert mid["bm"] * mid["bn"] < big["bm"] * big["bn"]
-    # A few rows of C, or a grid of output tiles far too small for 256 CUs,
-    # go to the few-row kernel; the comparison kernel is never picked.
-    for shape in ((1, 8192, 8192), (8, 4096, 4096), (256, 256, 256), (512, 512, 512)):
+    # A few rows of C go to the few-row kernel; a grid that the large tiles
+    # leave under-filled gets small MFMA tiles (measured on one MI355X:
+    # 1024^3 takes 29 us with 64 x 64 tiles, 71 us with 128 x 128).
+    for shape in ((1, 8192, 8192), (8, 4096, 4096), (32, 4096, 4096)):
         assert fg.fg_select_config("N", "N", *shape)["kind"] == fg.FG_KIND_SKINNY, shape
+    small = fg.fg_select_config("N", "N", 1024, 1024, 1024)
+    assert small["kind"] == fg.FG_KIND_MFMA and small["bm"] * small["bn"] <= 64 * 64
     ragged = fg.fg_select_config("T", "N", 3001, 2047, 1025, lda=3001, ldb=2047, ldc=2047)
     assert ragged["kind"] == fg.FG_KIND_MFMA
     # entries with 16-byte direct-to-LDS loads need 16-byte aligned rows of A
