@@ -10,8 +10,13 @@ Prints ONE JSON line (rank 0) with the metric, the roofline of the dominant
 kernel (timed with HIP events on the stream the kernel is launched on) and
 the CPU oracle timed on a bounded sample of the same workload.
 
+With the default workload it also times 4096^3 NN and the 1024 x 8192 x 8192
+row block one of eight GPUs would own, and measures the device's attainable
+MFMA and HBM-read rates with the library's probe kernels.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C5a]
-                       [--suite] [--no-cpu]
+                       [--suite] [--calibrate] [--splitk [S]] [--cold]
+                       [--no-cpu] [--no-probes] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -56,7 +61,13 @@ def load_traffic(workload, kernel_config):
     return t.get("bytes_per_launch")
 
 
-def time_gpu(w, steps, warmup, config=-1, splitk=False):
+def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock=False):
+    """Time `steps` calls on the current stream with a HIP event pair around
+    each call. Warm (default): the calls run back to back and the mean is the
+    whole range over `steps`. Cold: a 512 MiB device write runs before each
+    call (outside its event pair) so the operands start outside the caches."""
+    import statistics
+
     import torch
     import fp32_gemm_tile_amd as fg
     from fp32_gemm_tile_amd import workloads as wl
@@ -70,6 +81,7 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False):
     sp = stream.cuda_stream
     ws = torch.empty(64 << 20, dtype=torch.float32, device="cuda") if splitk else None
     nsplit = int(splitk) if splitk and not isinstance(splitk, bool) else 0
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda") if cold else None
 
     def step():
         if splitk:
@@ -86,20 +98,127 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(steps):
+    # Per-call event pairs (for the median and the minimum). Their records sit
+    # between the calls, so the warm mean comes from a second pass with one
+    # event pair around all `steps` calls.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        if cold:
+            flush.fill_(float(i))
+        starts[i].record(stream)
         step()
-    ev1.record(stream)
+        ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_events = ev0.elapsed_time(ev1)
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    if cold:
+        mean, wall = sum(per) / steps, None
+    else:
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        mean = ev0.elapsed_time(ev1) / steps
+    clock = None
+    if sample_clock:
+        # Outside the timed ranges: amd-smi samples the shader clock once a
+        # second while about five seconds of the same calls run.
+        watcher = start_clock_watch(seconds=4)
+        if watcher is not None:
+            time.sleep(1.0)
+            for _ in range(int(min(4000, max(10, 5000.0 / max(mean, 1e-3))))):
+                step()
+            torch.cuda.synchronize()
+            clock = finish_clock_watch(watcher)
     cfg = fg.fg_select_config(w.transA, w.transB, w.M, w.N, w.K, dA.data_ptr(), w.LDA,
                               dB.data_ptr(), w.LDB, dC.data_ptr(), w.LDC) if config < 0 \
         else fg.fg_get_config(config)
-    return {"ms_per_launch": ms_events / steps, "wall_s": wall, "config": cfg["name"]}
+    return {"ms_per_launch": mean, "ms_median": statistics.median(per), "ms_min": min(per),
+            "wall_s": wall, "config": cfg["name"], "clock_mhz": clock}
+
+
+def measured_peaks():
+    """The device's attainable fp32 MFMA rate and HBM read rate, from the
+    library's probe kernels (an MFMA-only loop; a 2 GiB streaming read, far
+    larger than the caches), best of five launches each."""
+    import torch
+    import fp32_gemm_tile_amd as fg
+
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    wgs, iters = 2048, 20000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    n = 1 << 29
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    rwgs = 512  # the best of 512 .. 16384 workgroups in a sweep on one MI355X
+    rout = torch.empty(rwgs * 4, dtype=torch.float32, device="cuda")
+
+    def best(launch):
+        launch()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        return min(times)
+
+    def mfma():
+        if fg.fg_probe_mfma(wgs, iters, out.data_ptr(), sp) != 0:
+            raise fg.FgError(fg.FG_ERR_HIP, 0, fg.fg_last_error())
+
+    def read():
+        if fg.fg_probe_read(x.data_ptr(), n, rwgs, rout.data_ptr(), sp) != 0:
+            raise fg.FgError(fg.FG_ERR_HIP, 0, fg.fg_last_error())
+
+    t_mfma = best(mfma)
+    t_read = best(read)
+    return {"mfma_tflops": round(fg.fg_probe_mfma_flops(wgs, iters) / t_mfma / 1e12, 2),
+            "hbm_read_gbs": round(4.0 * n / t_read / 1e9, 1),
+            "probes": "fg_probe_mfma 2048 WG x 20000 iterations; fg_probe_read of 2 GiB; "
+                      "best of 5"}
+
+
+def start_clock_watch(seconds):
+    """Start amd-smi sampling the clocks once a second for `seconds` seconds
+    (None if amd-smi cannot be started)."""
+    import subprocess
+    try:
+        return subprocess.Popen(["amd-smi", "metric", "--clock", "--json", "-w", "1",
+                                 "-W", str(seconds)], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+
+
+def finish_clock_watch(proc):
+    """Shader clock samples (MHz, mean over the XCDs of each sample) that
+    amd-smi printed: the median and the maximum, or None."""
+    import re
+    import statistics
+    import subprocess
+    try:
+        out, _ = proc.communicate(timeout=60)
+    except subprocess.TimeoutExpired:
+        proc.kill()
+        return None
+    vals = [float(v) for v in
+            re.findall(r'"gfx_\d+":\s*\{\s*"clk":\s*\{\s*"value":\s*(\d+(?:\.\d+)?)', out)]
+    if not vals:
+        return None
+    # eight XCDs per sample
+    per_sample = [sum(vals[i:i + 8]) / len(vals[i:i + 8]) for i in range(0, len(vals), 8)]
+    return {"median": round(statistics.median(per_sample), 1), "max": round(max(per_sample), 1),
+            "samples": len(per_sample), "source": "amd-smi metric --clock, 1 s interval"}
 
 
 def cpu_baseline(w, target_s=15.0):
@@ -126,7 +245,35 @@ def cpu_baseline(w, target_s=15.0):
     flops = 2.0 * rows * w.N * w.K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{rows} of {w.M} output rows of {w.name} (binary64 oracle), {dt:.1f} s"}
+            "sample": f"{rows} of {w.M} output rows of {w.name} (binary64 oracle), {dt:.1f} s",
+            "single_thread_256cubed_s": oracle_single_thread_small()}
+
+
+_ONE_THREAD_SNIPPET = """
+import sys, time
+sys.path.insert(0, sys.argv[1])
+import oracle
+from fp32_gemm_tile_amd import workloads as wl
+w = wl.WORKLOADS["C1"]
+A, B, C = wl.make_inputs(w)
+t0 = time.perf_counter()
+oracle.gemm(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A, w.LDA, B, w.LDB, w.beta, C, w.LDC)
+print(time.perf_counter() - t0, oracle.num_threads())
+"""
+
+
+def oracle_single_thread_small():
+    """Wall time of the whole 256^3 product on one host thread (the oracle in
+    a child process with OMP_NUM_THREADS=1), or None."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        r = subprocess.run([sys.executable, "-c", _ONE_THREAD_SNIPPET, ROOT], env=env,
+                           capture_output=True, text=True, timeout=120)
+        t, threads = r.stdout.split()
+        return round(float(t), 4) if int(threads) == 1 else None
+    except Exception:
+        return None
 
 
 def copy_probe(nbytes=1 << 30, reps=3):
@@ -142,10 +289,11 @@ def copy_probe(nbytes=1 << 30, reps=3):
     print(f"copy_probe: {reps} copies of {nbytes} bytes", file=sys.stderr, flush=True)
 
 
-def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False):
+def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False, cold=False,
+            sample_clock=False):
     from fp32_gemm_tile_amd import workloads as wl
     w = wl.WORKLOADS[name]
-    g = time_gpu(w, steps, warmup, config, splitk)
+    g = time_gpu(w, steps, warmup, config, splitk, cold, sample_clock)
     tflops = w.flops / (g["ms_per_launch"] * 1e-3) / 1e12
     gbs = w.compulsory_bytes / (g["ms_per_launch"] * 1e-3) / 1e9
     traffic = load_traffic(name, g["config"])
@@ -176,6 +324,11 @@ def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False):
                    "alpha": w.alpha, "beta": w.beta, "inputs": f"{w.dist} seed {w.seed}",
                    "kernel_config": g["config"]},
         "pct_of_fp32_peak": round(100 * tflops / PEAK_FP32_TFLOPS, 2),
+        "ms_median": round(g["ms_median"], 4),
+        "ms_min": round(g["ms_min"], 4),
+        "tflops_at_median": round(w.flops / (g["ms_median"] * 1e-3) / 1e12, 3),
+        "caches": "cold (512 MiB written before each call)" if cold else "warm",
+        "gpu_clock_mhz_under_load": g["clock_mhz"],
         "hbm_gbs_compulsory": round(gbs, 1),
         "roofline": roof,
     }
@@ -202,6 +355,10 @@ def main():
     ap.add_argument("--suite", action="store_true",
                     help="one line per workload C1..C6 (no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the measured MFMA-peak and HBM-read probes")
+    ap.add_argument("--cold", action="store_true",
+                    help="write 512 MiB before every timed call (operands out of cache)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run a plain device copy of 1 GiB three times "
                          "(reference for scaling HBM traffic counters)")
@@ -227,7 +384,7 @@ def main():
     if args.suite or args.calibrate:
         ids = range(fg.fg_num_configs()) if args.calibrate else [args.config]
         from fp32_gemm_tile_amd import workloads as wl
-        names = ("C1", "C2", "C3", "C4", "C5a", "C5b", "C6", "G1", "G1T", "G8")
+        names = ("C1", "C2", "C3", "C4", "C5a", "C5b", "C6", "S8", "G1", "G1T", "G8")
         for name in names:
             for cid in ids:
                 # The few-row kernel re-reads op(B) once per 8 rows of C: far
@@ -243,13 +400,22 @@ def main():
                       flush=True)
         return
 
-    r = run_one(args.workload, args.steps, args.warmup, False, args.config, _splitk_arg(args))
-    # The 4096^3 shape of the metric, timed in the same run.
+    r = run_one(args.workload, args.steps, args.warmup, False, args.config, _splitk_arg(args),
+                args.cold, sample_clock=True)
+    # The 4096^3 shape of the metric, and one GPU's row block of 8192^3 split
+    # over eight GPUs, timed in the same run.
     if args.workload == "C5a":
-        r2 = run_one("C6", args.steps, args.warmup, False, args.config)
-        r["also"] = {"sgemm_4096x4096x4096_nn": {"value": r2["value"], "unit": "TFLOP/s",
-                                                  "ms_per_step": r2["ms_per_step"],
-                                                  "pct_of_fp32_peak": r2["pct_of_fp32_peak"]}}
+        r["also"] = {}
+        for extra in ("C6", "S8"):
+            r2 = run_one(extra, args.steps, args.warmup, False, args.config, cold=args.cold)
+            r["also"][r2["config"]["workload"]] = {
+                k: r2[k] for k in ("value", "unit", "ms_per_step", "ms_median", "ms_min",
+                                   "pct_of_fp32_peak")}
+            r["also"][r2["config"]["workload"]]["kernel_config"] = r2["config"]["kernel_config"]
+    if not args.no_probes:
+        mp = measured_peaks()
+        mp["pct_of_measured_mfma"] = round(100 * r["value"] / mp["mfma_tflops"], 2)
+        r["measured_peaks"] = mp
     if not args.no_cpu:
         from fp32_gemm_tile_amd import workloads as wl
         r["cpu_baseline"] = cpu_baseline(wl.WORKLOADS[args.workload])

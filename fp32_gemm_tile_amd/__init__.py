@@ -96,6 +96,12 @@ def load_library(path: str = LIB_PATH):
     lib.fg_status_string.restype = ctypes.c_char_p
     lib.fg_abi_version.argtypes = []
     lib.fg_abi_version.restype = i32
+    lib.fg_probe_mfma.argtypes = [i32, i32, vp, vp]
+    lib.fg_probe_mfma.restype = i32
+    lib.fg_probe_mfma_flops.argtypes = [i32, i32]
+    lib.fg_probe_mfma_flops.restype = ctypes.c_double
+    lib.fg_probe_read.argtypes = [vp, i64, i32, vp, vp]
+    lib.fg_probe_read.restype = i32
     _lib = lib
     return lib
 
@@ -180,6 +186,20 @@ def fg_status_string(s: int) -> str:
 
 def fg_abi_version() -> int:
     return load_library().fg_abi_version()
+
+
+def fg_probe_mfma(workgroups, iterations, out, stream=0) -> int:
+    """MFMA-only loop (fp32gemm_probe.h); out: device pointer, workgroups*256 floats."""
+    return load_library().fg_probe_mfma(workgroups, iterations, out or None, stream or None)
+
+
+def fg_probe_mfma_flops(workgroups, iterations) -> float:
+    return load_library().fg_probe_mfma_flops(workgroups, iterations)
+
+
+def fg_probe_read(x, n, workgroups, out, stream=0) -> int:
+    """Streaming read of n floats (fp32gemm_probe.h); out: workgroups*4 floats."""
+    return load_library().fg_probe_read(x or None, n, workgroups, out or None, stream or None)
 
 
 def configs() -> list:

@@ -23,7 +23,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp32gemm.so")
 SOURCES = ["fg_api.cpp", "sgemm_mfma.hip", "sgemm_valu.hip", "sgemm_skinny.hip",
-           "fg_elementwise.hip"]
+           "fg_elementwise.hip", "fg_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -22,6 +22,7 @@
 #include <mutex>
 
 #include "../../include/fp32gemm.h"
+#include "../../include/fp32gemm_probe.h"
 #include "fg_kernels.h"
 
 namespace {
@@ -110,7 +111,7 @@ const Entry* table() {
         make_entry(9, FG_KIND_MFMA, 7, 128, 128, 16, 64, 64, 256, 4, 2, 0.899, "mfma_128x128x16_w2x2_s4", 10),
         make_entry(10, FG_KIND_MFMA, 8, 128, 128, 16, 64, 64, 256, 4, 2, 0.881, "mfma_128x128x16_w2x2_s4_dw"),
         make_entry(11, FG_KIND_MFMA, 9, 256, 256, 16, 64, 128, 512, 4, 2, 0.90, "mfma_256x256x16_w4x2_s4", 0),
-        make_entry(12, FG_KIND_MFMA, 10, 256, 128, 16, 128, 64, 256, 3, 2, 0.90, "mfma_256x128x16_w2x2_s3", 1),
+        make_entry(12, FG_KIND_MFMA, 10, 256, 128, 16, 128, 64, 256, 3, 2, 0.90, "mfma_256x128x16_w2x2_s3", 1, 0.86),
         // Few-row kernel: bm = rows per block (up to 8), bn = columns per
         // workgroup for B stored K x N; memory-bound, costed separately.
         make_entry(13, FG_KIND_SKINNY, 0, 8, 32, 0, 8, 4, 256, 0, 2, 1.0, "valu_skinny_m8"),
@@ -147,20 +148,22 @@ double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, boo
     int64_t kps = 0;
     const int64_t s = effective_splits(K, e.cfg.bk, splits, &kps);
     const int64_t tiles = cdiv(M, e.cfg.bm) * cdiv(N, e.cfg.bn);
-    const int64_t simds = (int64_t)kNumCUs * kSimdsPerCU;
     const double wave_flops = 2.0 * e.cfg.wm * e.cfg.wn * (double)kps * e.cfg.bk;
-    // Rounds of resident waves: each round puts up to wps waves on every
-    // SIMD; the last round may hold fewer. A SIMD shared by `share` waves
-    // finishes them after share * wave_flops at an efficiency that grows
-    // from eff1 (one wave: little latency hiding) to eff (wps waves).
+    // Rounds of resident workgroups: a workgroup's waves share one CU, and a
+    // CU holds up to `slots` workgroups (wps waves per SIMD); the last round
+    // may leave CUs idle. A SIMD shared by `share` waves finishes them after
+    // share * wave_flops at an efficiency that grows from eff1 (one wave:
+    // little latency hiding) to eff (wps waves).
+    const int64_t w = e.cfg.threads / 64;
+    const int64_t slots = std::max<int64_t>(1, (int64_t)e.wps * kSimdsPerCU / w);
     double t = kLaunch;
-    for (int64_t left = tiles * (e.cfg.threads / 64) * s; left > 0;) {
-        int64_t share = cdiv(left, simds);
-        if (share > e.wps) share = e.wps;
+    for (int64_t left = tiles * s; left > 0;) {
+        const int64_t per_cu = std::min<int64_t>(cdiv(left, kNumCUs), slots);
+        const int64_t share = std::max<int64_t>(1, cdiv(per_cu * w, kSimdsPerCU));
         const double eff =
             e.wps > 1 ? e.eff1 + (e.eff - e.eff1) * (double)(share - 1) / (e.wps - 1) : e.eff;
         t += wave_flops * (double)share / (eff * kSimdFlops);
-        left -= share * simds;
+        left -= per_cu * kNumCUs;
     }
     if (s > 1)
         t += ((double)(2 * s + (beta0 ? 1 : 2)) * M * N * 4.0) / kHbmBytes + kLaunch;
@@ -508,6 +511,42 @@ fg_status fg_sgemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
                    const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
                    float* C, int64_t ldc, hipStream_t stream) {
     return fg_sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1);
+}
+
+double fg_probe_mfma_flops(int32_t workgroups, int32_t iterations) {
+    if (workgroups <= 0 || iterations <= 0) return 0.0;
+    return (double)workgroups * 4.0 * (double)iterations * 4.0 * 4096.0;
+}
+
+fg_status fg_probe_mfma(int32_t workgroups, int32_t iterations, float* out, hipStream_t stream) {
+    clear_error();
+    if (workgroups < 1 || workgroups > 65536)
+        return fail(FG_ERR_INVALID_ARG, 1, "workgroups %d outside 1..65536", workgroups);
+    if (iterations < 1 || iterations > (1 << 24))
+        return fail(FG_ERR_INVALID_ARG, 2, "iterations %d outside 1..16777216", iterations);
+    if (!out) return fail(FG_ERR_INVALID_ARG, 3, "out is NULL");
+    fg_status s = check_device();
+    if (s != FG_OK) return s;
+    const hipError_t e = fg::launch_probe_mfma(workgroups, iterations, out, stream);
+    if (e != hipSuccess) return fail(FG_ERR_HIP, 0, "kernel launch: %s", hipGetErrorString(e));
+    return FG_OK;
+}
+
+fg_status fg_probe_read(const float* x, int64_t n, int32_t workgroups, float* out,
+                        hipStream_t stream) {
+    clear_error();
+    if (n < 0 || (n & 3)) return fail(FG_ERR_INVALID_ARG, 2, "n=%lld is not a multiple of 4 >= 0",
+                                      (long long)n);
+    if (n > 0 && !x) return fail(FG_ERR_INVALID_ARG, 1, "x is NULL");
+    if ((uintptr_t)x & 15u) return fail(FG_ERR_INVALID_ARG, 1, "x is not 16-byte aligned");
+    if (workgroups < 1 || workgroups > 65536)
+        return fail(FG_ERR_INVALID_ARG, 3, "workgroups %d outside 1..65536", workgroups);
+    if (!out) return fail(FG_ERR_INVALID_ARG, 4, "out is NULL");
+    fg_status s = check_device();
+    if (s != FG_OK) return s;
+    const hipError_t e = fg::launch_probe_read(x, n / 4, workgroups, out, stream);
+    if (e != hipSuccess) return fail(FG_ERR_HIP, 0, "kernel launch: %s", hipGetErrorString(e));
+    return FG_OK;
 }
 
 }  // extern "C"

@@ -55,5 +55,9 @@ hipError_t launch_scale(const GemmParams& p, hipStream_t stream);
 // the dense M x N slice W + s * M * N; the sum runs in ascending s.
 hipError_t launch_splitk_reduce(const float* W, int32_t splits, const GemmParams& p,
                                 hipStream_t stream);
+// Machine probes (fg_probe.hip): an MFMA-only loop and a streaming read.
+hipError_t launch_probe_mfma(int workgroups, int iters, float* out, hipStream_t stream);
+hipError_t launch_probe_read(const float* x, int64_t n4, int workgroups, float* out,
+                             hipStream_t stream);
 
 }  // namespace fg

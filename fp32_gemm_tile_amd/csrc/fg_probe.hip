@@ -1,0 +1,85 @@
+// Machine probes: the attainable fp32 matrix-core rate and HBM read rate of
+// the device, measured with kernels that do nothing else. A GEMM's fraction
+// of peak is quoted against both the published figures and these.
+//
+//   * mfma_probe_kernel: every wave runs `iters` rounds of four independent
+//     v_mfma_f32_32x32x2_f32 chains (4096 FLOP each) on register operands,
+//     with no memory traffic in the loop. One lane sum per thread is stored
+//     at the end so the chains cannot be removed.
+//   * read_probe_kernel: a grid-stride read of n floats with 128-bit loads,
+//     16 KiB per workgroup per pass, one partial sum per wave stored.
+#include "fg_device.h"
+
+namespace fg {
+namespace {
+
+constexpr int kProbeThreads = 256;
+
+__global__ void __launch_bounds__(kProbeThreads) mfma_probe_kernel(int iters, float* out) {
+    // Operands in (0, 1): each MFMA adds at most 2 to an accumulator, so the
+    // sums stay finite for any iteration count the host allows.
+    const float a = 0.25f + (threadIdx.x & 63) * (1.0f / 512.0f);
+    const float b = 0.75f - (threadIdx.x & 63) * (1.0f / 512.0f);
+    f16v acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[j], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += acc[j][r];
+    out[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
+}
+
+__global__ void __launch_bounds__(kProbeThreads) read_probe_kernel(const f4* __restrict__ x,
+                                                                   int64_t n4, float* out) {
+    // Each pass, a workgroup reads 4 x 256 consecutive 16-byte vectors (16 KiB,
+    // four loads in flight per thread); the grid then strides past them.
+    constexpr int kChunk = 4 * kProbeThreads;
+    const int64_t stride = (int64_t)gridDim.x * kChunk;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    int64_t base = (int64_t)blockIdx.x * kChunk;
+    for (; base + kChunk <= n4; base += stride) {
+        const f4* p = x + base + threadIdx.x;
+        const f4 v0 = p[0], v1 = p[kProbeThreads], v2 = p[2 * kProbeThreads], v3 = p[3 * kProbeThreads];
+        s0 += (v0[0] + v0[1]) + (v0[2] + v0[3]);
+        s1 += (v1[0] + v1[1]) + (v1[2] + v1[3]);
+        s2 += (v2[0] + v2[1]) + (v2[2] + v2[3]);
+        s3 += (v3[0] + v3[1]) + (v3[2] + v3[3]);
+    }
+    // At most one partial chunk is left, and only the workgroup whose turn it
+    // is reaches it (base < n4 < base + kChunk).
+    if (base < n4) {
+        for (int64_t i = base + threadIdx.x; i < n4; i += kProbeThreads) {
+            const f4 v = x[i];
+            s0 += (v[0] + v[1]) + (v[2] + v[3]);
+        }
+    }
+    float s = (s0 + s1) + (s2 + s3);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    if ((threadIdx.x & 63) == 0) out[(int64_t)blockIdx.x * (kProbeThreads / 64) + (threadIdx.x >> 6)] = s;
+}
+
+}  // namespace
+
+hipError_t launch_probe_mfma(int workgroups, int iters, float* out, hipStream_t stream) {
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(workgroups), dim3(kProbeThreads), 0, stream, iters,
+                       out);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const float* x, int64_t n4, int workgroups, float* out,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(workgroups), dim3(kProbeThreads), 0, stream,
+                       reinterpret_cast<const f4*>(x), n4, out);
+    return hipGetLastError();
+}
+
+}  // namespace fg

@@ -99,6 +99,10 @@ WORKLOADS = {
                     note="8192^3 NT, same buffers as C5a"),
     "C6": Workload("C6", 4096, 4096, 4096, seed=5,
                    note="4096^3 NN (headline)"),
+    # One GPU's share of 8192^3 split by row blocks over eight GPUs (each
+    # GPU holds 1024 rows of A and all of B); seed is this project's choice.
+    "S8": Workload("S8", 1024, 8192, 8192, seed=8,
+                   note="row block of 8192^3 over 8 GPUs: 1024 x 8192 x 8192 NN"),
     # Few-row (decode) shapes, memory-bound; seeds are this project's choice.
     "G1": Workload("G1", 1, 8192, 8192, seed=6, note="GEMV: 1 x 8192 times 8192 x 8192"),
     "G1T": Workload("G1T", 1, 8192, 8192, transB="T", seed=6,

@@ -1,0 +1,54 @@
+/*
+ * fp32gemm_probe -- machine probes that sit beside the GEMM in the same
+ * library: the attainable fp32 matrix-core rate and HBM read rate of the
+ * device, each measured by a kernel that does nothing else. A GEMM's
+ * fraction of peak can then be quoted against the published figures and
+ * against these measured ceilings. None of this is needed to call fg_sgemm.
+ *
+ * Same conventions as fp32gemm.h: device pointers owned by the caller, work
+ * enqueued on `stream` without synchronising, errors reported through
+ * fg_status / fg_last_bad_arg() / fg_last_error(), nothing enqueued when an
+ * argument is rejected.
+ */
+#ifndef FP32GEMM_PROBE_H
+#define FP32GEMM_PROBE_H
+
+#include "fp32gemm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * fg_probe_mfma: `workgroups` workgroups of four waves; every wave runs
+ * `iterations` rounds of four independent v_mfma_f32_32x32x2_f32 chains on
+ * register operands (no memory traffic), then each work-item stores one
+ * float to out[workgroup * 256 + work-item] (the sum of its accumulators).
+ *   1 workgroups : 1 .. 65536
+ *   2 iterations : 1 .. 16777216
+ *   3 out        : device memory for workgroups * 256 floats
+ *   4 stream
+ * Floating-point operations performed: fg_probe_mfma_flops(workgroups,
+ * iterations) = workgroups * 4 * iterations * 4 * 4096.
+ */
+fg_status fg_probe_mfma(int32_t workgroups, int32_t iterations, float* out, hipStream_t stream);
+double fg_probe_mfma_flops(int32_t workgroups, int32_t iterations);
+
+/*
+ * fg_probe_read: read n floats of x once with 128-bit loads (grid-stride over
+ * `workgroups` workgroups of four waves) and store one partial sum per wave
+ * to out[workgroup * 4 + wave]. Bytes read from memory: 4 * n.
+ *   1 x          : device memory, 16-byte aligned (may be NULL when n == 0)
+ *   2 n          : >= 0, a multiple of 4
+ *   3 workgroups : 1 .. 65536
+ *   4 out        : device memory for workgroups * 4 floats
+ *   5 stream
+ */
+fg_status fg_probe_read(const float* x, int64_t n, int32_t workgroups, float* out,
+                        hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP32GEMM_PROBE_H */

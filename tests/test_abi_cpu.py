@@ -1,6 +1,7 @@
 """The C-ABI library on the host: it loads, exports what the header declares,
 validates arguments and takes the quick returns without touching a GPU."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,18 +11,21 @@ import fp32_gemm_tile_amd as fg
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp32gemm.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fg_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(fg_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
     lib = fg.load_library()
     names = declared_functions()
-    assert "fg_sgemm" in names and "fg_sgemm_ex" in names
+    assert "fg_sgemm" in names and "fg_sgemm_ex" in names and "fg_probe_read" in names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
 
@@ -124,7 +128,7 @@ def test_selection_is_mfma_and_scales_with_shape():
 
 
 def test_header_is_plain_c():
-    """The header compiles as C99 with no HIP or torch headers."""
+    """The headers compile as C99 with no HIP or torch headers."""
     import shutil
     import subprocess
     import tempfile
@@ -133,7 +137,8 @@ def test_header_is_plain_c():
     with tempfile.TemporaryDirectory() as d:
         src = os.path.join(d, "t.c")
         with open(src, "w") as f:
-            f.write('#include "fp32gemm.h"\nint main(void){return fg_abi_version()==0;}\n')
+            f.write("".join(f'#include "{os.path.basename(h)}"\n' for h in HEADERS)
+                    + "int main(void){return fg_abi_version()==0;}\n")
         subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
                         "-I", os.path.dirname(HEADER), src], check=True)
 
@@ -235,3 +240,15 @@ print("ok")
 """
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and "ok" in r.stdout, (r.returncode, r.stderr[-1500:])
+
+
+def test_probe_validation_and_flop_count():
+    assert fg.fg_probe_mfma_flops(1024, 100) == 1024 * 4 * 100 * 4 * 4096
+    assert fg.fg_probe_mfma_flops(0, 100) == 0.0
+    assert fg.fg_probe_mfma(0, 10, 4096) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 1
+    assert fg.fg_probe_mfma(4, 0, 4096) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 2
+    assert fg.fg_probe_mfma(4, 10, 0) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 3
+    assert fg.fg_probe_read(4096, 6, 4, 4096) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 2
+    assert fg.fg_probe_read(4100, 8, 4, 4096) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 1
+    assert fg.fg_probe_read(4096, 8, 0, 4096) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 3
+    assert fg.fg_probe_read(4096, 8, 4, 0) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 4
