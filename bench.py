@@ -35,10 +35,17 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "fp32 SGEMM TFLOP/s and % of MI355X fp32 peak at 4096^3 and 8192^3"
 
 
-def kernel_source_sha():
-    """Hash of the sources that define the matrix-core kernel and its launch."""
+def kernel_source_sha(kernel_config="mfma_"):
+    """Hash of the sources that define the kernel family of a table entry
+    (matrix-core, few-row or vector-ALU kernel) and its launch."""
+    if kernel_config.startswith("valu_skinny"):
+        family = "sgemm_skinny.hip"
+    elif kernel_config.startswith("valu_"):
+        family = "sgemm_valu.hip"
+    else:
+        family = "sgemm_mfma.hip"
     h = hashlib.sha256()
-    for f in ("sgemm_mfma.hip", "fg_device.h", "fg_kernels.h"):
+    for f in (family, "fg_device.h", "fg_kernels.h"):
         with open(os.path.join(ROOT, "fp32_gemm_tile_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -54,7 +61,7 @@ def load_traffic(workload, kernel_config):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha") != kernel_source_sha():
+    if t.get("kernel_source_sha") != kernel_source_sha(kernel_config):
         return None
     if t.get("kernel_config") not in (None, kernel_config):
         return None
@@ -356,7 +363,8 @@ def main():
                     help="one line per workload C1..C6 (no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-probes", action="store_true",
-                    help="skip the measured MFMA-peak and HBM-read probes")
+                    help="skip the measured MFMA-peak and HBM-read probes and the "
+                         "clock sampling under load")
     ap.add_argument("--cold", action="store_true",
                     help="write 512 MiB before every timed call (operands out of cache)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -401,7 +409,7 @@ def main():
         return
 
     r = run_one(args.workload, args.steps, args.warmup, False, args.config, _splitk_arg(args),
-                args.cold, sample_clock=True)
+                args.cold, sample_clock=not args.no_probes)
     # The 4096^3 shape of the metric, and one GPU's row block of 8192^3 split
     # over eight GPUs, timed in the same run.
     if args.workload == "C5a":
