@@ -67,3 +67,67 @@ def check(c_gpu, c_ref, sabs, K, alpha=1.0, beta=0.0, cin=None, frob=True):
     info["ok_elem"] = ok_elem
     info["ok_frob"] = ok_frob
     return ok_elem and ok_frob, info
+
+
+def epilogue_tol(K, alpha, beta, sabs, cin, v_ref, row_scale=None, col_scale=None,
+                 row_bias=None, col_bias=None, act="none"):
+    """Per-element bound for the fused epilogue
+    D = act(alpha * r_i * c_j * s_ij + beta * C_ij + u_i + w_j).
+
+    The pre-activation value v carries the GEMM bound with every term of the
+    sum in place of |alpha| * S and |beta| * |C_in| (each extra binary32
+    rounding of the scale product and of the two bias additions is covered
+    by the 8 * max(K, 1) factor, as the alpha/beta roundings are):
+
+        tol_v = 8 * max(K, 1) * 2^-24 * (|alpha r_i c_j| S + |beta C_ij| + |u_i| + |w_j|) + 1e-6
+
+    The activation stretches that by at most its largest slope (1 for relu,
+    1.129 for gelu, 1.1 for silu) and its own binary32 evaluation adds at most
+    2^-20 * |v| (a few units in the last place of erf / exp and the products
+    around them)."""
+    from .epilogue import LIPSCHITZ
+    sabs = np.asarray(sabs, dtype=np.float64)
+    M, N = sabs.shape
+    r = np.ones(M) if row_scale is None else np.asarray(row_scale, np.float64).ravel()
+    c = np.ones(N) if col_scale is None else np.asarray(col_scale, np.float64).ravel()
+    t = np.abs(float(alpha) * r[:, None] * c[None, :]) * sabs
+    if beta != 0 and cin is not None:
+        t = t + abs(float(beta)) * np.abs(np.asarray(cin, dtype=np.float64))
+    if row_bias is not None:
+        t = t + np.abs(np.asarray(row_bias, np.float64).ravel())[:, None]
+    if col_bias is not None:
+        t = t + np.abs(np.asarray(col_bias, np.float64).ravel())[None, :]
+    tol_v = 8.0 * max(int(K), 1) * U32 * t + ABS_FLOOR
+    if act == "none":
+        return tol_v
+    return LIPSCHITZ[act] * tol_v + 2.0 ** -20 * np.abs(np.asarray(v_ref, dtype=np.float64))
+
+
+def check_epilogue(d_gpu, d_ref, v_ref, sabs, K, alpha, beta, cin=None, row_scale=None,
+                   col_scale=None, row_bias=None, col_bias=None, act="none", frob=True):
+    """(ok, info) for a fused-epilogue result, as check() for the plain GEMM:
+    every element within epilogue_tol and the relative Frobenius error of the
+    whole result at most 1e-5."""
+    d_gpu = np.asarray(d_gpu, dtype=np.float64)
+    d_ref = np.asarray(d_ref, dtype=np.float64)
+    if d_gpu.shape != d_ref.shape:
+        raise ValueError(f"shape mismatch {d_gpu.shape} vs {d_ref.shape}")
+    info = {"n": int(d_ref.size)}
+    if d_ref.size == 0:
+        return True, info
+    tol = epilogue_tol(K, alpha, beta, sabs, cin, v_ref, row_scale, col_scale, row_bias,
+                       col_bias, act)
+    err = np.abs(d_gpu - d_ref)
+    finite = np.isfinite(d_gpu)
+    ratio = np.where(finite, err / tol, np.inf)
+    worst = int(np.argmax(ratio))
+    info["max_err_over_tol"] = float(ratio.flat[worst])
+    info["worst_index"] = tuple(int(v) for v in np.unravel_index(worst, d_ref.shape))
+    info["n_bad"] = int((~(finite & (err <= tol))).sum())
+    ok = info["n_bad"] == 0
+    if frob:
+        dn = float(np.linalg.norm(np.where(finite, d_gpu - d_ref, np.inf)))
+        rn = float(np.linalg.norm(d_ref))
+        info["frob_rel"] = dn / rn if rn > 0 else dn
+        ok = ok and (dn <= FROB_REL * rn if rn > 0 else dn <= ABS_FLOOR * np.sqrt(d_ref.size))
+    return ok, info
