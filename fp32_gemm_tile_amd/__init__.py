@@ -50,6 +50,31 @@ class fg_config(ctypes.Structure):
         return d
 
 
+FG_ACT_NONE, FG_ACT_RELU, FG_ACT_GELU, FG_ACT_SILU = 0, 1, 2, 3
+_ACTS = {"none": FG_ACT_NONE, "relu": FG_ACT_RELU, "gelu": FG_ACT_GELU, "silu": FG_ACT_SILU}
+
+
+class fg_epilogue(ctypes.Structure):
+    _fields_ = [("row_scale", ctypes.c_void_p), ("col_scale", ctypes.c_void_p),
+                ("row_bias", ctypes.c_void_p), ("col_bias", ctypes.c_void_p),
+                ("activation", ctypes.c_int32)]
+
+
+def activation_code(act) -> int:
+    """fg_activation value of "none" / "relu" / "gelu" / "silu" (or an int)."""
+    if isinstance(act, str):
+        if act not in _ACTS:
+            raise ValueError(f"unknown activation {act!r}")
+        return _ACTS[act]
+    return int(act)
+
+
+def make_epilogue(row_scale=0, col_scale=0, row_bias=0, col_bias=0, activation="none"):
+    """fg_epilogue from device addresses (0 = not used) and an activation."""
+    return fg_epilogue(row_scale or None, col_scale or None, row_bias or None,
+                       col_bias or None, activation_code(activation))
+
+
 _lib = None
 
 
@@ -96,6 +121,8 @@ def load_library(path: str = LIB_PATH):
     lib.fg_status_string.restype = ctypes.c_char_p
     lib.fg_abi_version.argtypes = []
     lib.fg_abi_version.restype = i32
+    lib.fg_sgemm_fused.argtypes = gemm_args[:13] + [ctypes.POINTER(fg_epilogue), vp, i32]
+    lib.fg_sgemm_fused.restype = i32
     lib.fg_probe_mfma.argtypes = [i32, i32, vp, vp]
     lib.fg_probe_mfma.restype = i32
     lib.fg_probe_mfma_flops.argtypes = [i32, i32]
@@ -188,6 +215,14 @@ def fg_abi_version() -> int:
     return load_library().fg_abi_version()
 
 
+def fg_sgemm_fused(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                   epilogue=None, stream=0, config=-1):
+    """Raw call with a fused epilogue (an fg_epilogue, or None for none)."""
+    ep = ctypes.byref(epilogue) if epilogue is not None else None
+    return load_library().fg_sgemm_fused(_op(transA), _op(transB), M, N, K, alpha, A, lda,
+                                         B, ldb, beta, C, ldc, ep, stream or None, config)
+
+
 def fg_probe_mfma(workgroups, iterations, out, stream=0) -> int:
     """MFMA-only loop (fp32gemm_probe.h); out: device pointer, workgroups*256 floats."""
     return load_library().fg_probe_mfma(workgroups, iterations, out or None, stream or None)
@@ -216,10 +251,15 @@ def _ld(t, name):
     return t.stride(0) if t.size(0) > 1 else max(1, t.size(1))
 
 
-def sgemm(A, B, C, alpha=1.0, beta=0.0, transA="N", transB="N", config=-1, stream=None):
+def sgemm(A, B, C, alpha=1.0, beta=0.0, transA="N", transB="N", config=-1, stream=None,
+          row_scale=None, col_scale=None, row_bias=None, col_bias=None, activation="none"):
     """C <- alpha * op(A) @ op(B) + beta * C for float32 GPU tensors (row-major,
     unit inner stride; leading dimensions are taken from the row strides).
-    Returns C. Enqueued on ``stream`` (default: torch's current stream)."""
+    With any of row_scale / col_scale / row_bias / col_bias (contiguous float32
+    GPU vectors of length M or N) or an activation ("relu", "gelu", "silu"),
+    C <- act(alpha * r_i * c_j * (op(A) op(B))_ij + beta * C_ij + u_i + w_j)
+    through fg_sgemm_fused. Returns C. Enqueued on ``stream`` (default:
+    torch's current stream)."""
     import torch
     for name, t in (("A", A), ("B", B), ("C", C)):
         if t.dtype != torch.float32:
@@ -235,12 +275,26 @@ def sgemm(A, B, C, alpha=1.0, beta=0.0, transA="N", transB="N", config=-1, strea
         raise ValueError("op(B) rows != op(A) columns")
     if (B.shape[1] if tb == FG_OP_N else B.shape[0]) != N:
         raise ValueError("op(B) columns != C columns")
+    vecs = []
+    for name, v, n in (("row_scale", row_scale, M), ("col_scale", col_scale, N),
+                       ("row_bias", row_bias, M), ("col_bias", col_bias, N)):
+        if v is None:
+            vecs.append(0)
+            continue
+        if v.dtype != torch.float32 or not v.is_cuda or not v.is_contiguous() or v.numel() != n:
+            raise ValueError(f"{name} must be a contiguous float32 GPU vector of length {n}")
+        vecs.append(v.data_ptr())
     if stream is None:
         stream = torch.cuda.current_stream(C.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    st = fg_sgemm_ex(ta, tb, M, N, K, float(alpha), A.data_ptr(), _ld(A, "A"),
-                     B.data_ptr(), _ld(B, "B"), float(beta), C.data_ptr(), _ld(C, "C"),
-                     stream, config)
+    if any(vecs) or activation_code(activation) != FG_ACT_NONE:
+        st = fg_sgemm_fused(ta, tb, M, N, K, float(alpha), A.data_ptr(), _ld(A, "A"),
+                            B.data_ptr(), _ld(B, "B"), float(beta), C.data_ptr(), _ld(C, "C"),
+                            make_epilogue(*vecs, activation), stream, config)
+    else:
+        st = fg_sgemm_ex(ta, tb, M, N, K, float(alpha), A.data_ptr(), _ld(A, "A"),
+                         B.data_ptr(), _ld(B, "B"), float(beta), C.data_ptr(), _ld(C, "C"),
+                         stream, config)
     _raise_if(st)
     return C

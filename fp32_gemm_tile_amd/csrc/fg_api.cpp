@@ -368,17 +368,20 @@ namespace {
 fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, float alpha,
                    const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
                    float* C, int64_t ldc, hipStream_t stream, int32_t config_id,
-                   int64_t splits, float* ws, size_t ws_bytes) {
+                   int64_t splits, float* ws, size_t ws_bytes,
+                   const fg_epilogue* epi = nullptr, int config_arg = 15) {
     clear_error();
     fg_status s = validate(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
     if (s != FG_OK) return s;
     if (config_id < -1 || config_id >= kNumEntries)
-        return fail(FG_ERR_INVALID_ARG, 15, "config id %d out of range", config_id);
+        return fail(FG_ERR_INVALID_ARG, config_arg, "config id %d out of range", config_id);
+    const bool epi_on = epi && (epi->row_scale || epi->col_scale || epi->row_bias ||
+                                epi->col_bias || epi->activation != FG_ACT_NONE);
 
     // Quick returns.
     if (M == 0 || N == 0) return FG_OK;
     const bool no_product = (K == 0 || alpha == 0.0f);
-    if (no_product && beta == 1.0f) return FG_OK;
+    if (no_product && beta == 1.0f && !epi_on) return FG_OK;
 
     fg::GemmParams p;
     memset(&p, 0, sizeof p);
@@ -400,6 +403,14 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
     p.b_extent = b_rows > 0 && b_cols > 0 ? (b_rows - 1) * ldb + b_cols : 0;
     p.c_extent = (M - 1) * ldc + N;
     p.flags = build_flags(A, lda, B, ldb, C, ldc, beta);
+    if (epi_on) {
+        p.flags |= fg::FLAG_EPI;
+        p.row_scale = epi->row_scale;
+        p.col_scale = epi->col_scale;
+        p.row_bias = epi->row_bias;
+        p.col_bias = epi->col_bias;
+        p.act = epi->activation;
+    }
 
     if (no_product) {
         s = check_device();
@@ -511,6 +522,18 @@ fg_status fg_sgemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
                    const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
                    float* C, int64_t ldc, hipStream_t stream) {
     return fg_sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1);
+}
+
+fg_status fg_sgemm_fused(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                         float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                         float beta, float* C, int64_t ldc, const fg_epilogue* epilogue,
+                         hipStream_t stream, int32_t config_id) {
+    clear_error();
+    if (epilogue && (epilogue->activation < FG_ACT_NONE || epilogue->activation > FG_ACT_SILU))
+        return fail(FG_ERR_INVALID_ARG, 14, "activation %d is not an fg_activation",
+                    epilogue->activation);
+    return run_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                    config_id, 1, nullptr, 0, epilogue, 16);
 }
 
 double fg_probe_mfma_flops(int32_t workgroups, int32_t iterations) {

@@ -72,6 +72,45 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
+// Fused-epilogue activation in binary32. relu keeps NaN (x < 0 is false for
+// it); gelu is the erf form x * Phi(x); silu is x * sigma(x), which tends to
+// -0 for very negative x (exp overflows to inf).
+__device__ __forceinline__ float activate(float x, int act) {
+    if (act == ACT_RELU) return x < 0.f ? 0.f : x;
+    if (act == ACT_GELU) return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+    if (act == ACT_SILU) return x / (1.f + expf(-x));
+    return x;
+}
+
+// Scale factor alpha * r_i * c_j of element (i, j) under FLAG_EPI.
+__device__ __forceinline__ float epi_scale(const GemmParams& p, int64_t i, int64_t j) {
+    float s = p.alpha;
+    if (p.row_scale) s *= p.row_scale[i];
+    if (p.col_scale) s *= p.col_scale[j];
+    return s;
+}
+
+// act(o + u_i + w_j) of element (i, j) under FLAG_EPI.
+__device__ __forceinline__ float epi_finish(const GemmParams& p, float o, int64_t i, int64_t j) {
+    if (p.row_bias) o += p.row_bias[i];
+    if (p.col_bias) o += p.col_bias[j];
+    return activate(o, p.act);
+}
+
+// C element (i, j) from its plain product sum `acc` and its old value (read
+// only when beta != 0), with or without the fused epilogue.
+__device__ __forceinline__ float epilogue_value(const GemmParams& p, float acc, float cin,
+                                                bool beta0, int64_t i, int64_t j) {
+    if (p.flags & FLAG_EPI) {
+        float o = epi_scale(p, i, j) * acc;
+        if (!beta0) o += p.beta * cin;
+        return epi_finish(p, o, i, j);
+    }
+    float o = p.alpha * acc;
+    if (!beta0) o += p.beta * cin;
+    return o;
+}
+
 // Workgroup id -> (tile_m, tile_n).
 //
 // 1. XCD remap: consecutive workgroup ids are handed to the 8 XCDs in turn,

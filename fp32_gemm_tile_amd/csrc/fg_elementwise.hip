@@ -1,9 +1,11 @@
 // The two memory-bound kernels around the GEMM proper:
 //   * scale: C = beta * C (C = 0 without reading C when beta == 0), the
-//     whole result when K == 0 or alpha == 0;
+//     whole result when K == 0 or alpha == 0 (with the fused epilogue:
+//     C = act(beta * C + u_i + w_j));
 //   * split-K reduction: C = alpha * (W_0 + W_1 + ... + W_{S-1}) + beta * C,
 //     summing the per-split partial products in ascending split order, so
-//     the result does not depend on scheduling.
+//     the result does not depend on scheduling; the fused epilogue, when
+//     asked for, is applied to that sum.
 // Both walk the M x N window with a grid-stride loop; every index is inside
 // the caller's buffers by construction, so plain global accesses are used.
 #include "fg_device.h"
@@ -18,7 +20,9 @@ __global__ void __launch_bounds__(256) scale_kernel(GemmParams p) {
          t += (int64_t)gridDim.x * blockDim.x) {
         const int64_t i = t / p.N, j = t - i * p.N;
         float* c = p.C + i * p.ldc + j;
-        *c = beta0 ? 0.f : p.beta * *c;
+        float o = beta0 ? 0.f : p.beta * *c;
+        if (p.flags & FLAG_EPI) o = epi_finish(p, o, i, j);
+        *c = o;
     }
 }
 
@@ -39,15 +43,15 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
         if constexpr (VEC) {
             f4 acc = *reinterpret_cast<const f4*>(W + e);
             for (int s = 1; s < splits; ++s) acc = acc + *reinterpret_cast<const f4*>(W + s * mn + e);
-            f4 out = p.alpha * acc;
-            if (!beta0) out = out + p.beta * *reinterpret_cast<const f4*>(c);
+            const f4 cin = beta0 ? f4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f4*>(c);
+            f4 out;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) out[q] = epilogue_value(p, acc[q], cin[q], beta0, i, j + q);
             *reinterpret_cast<f4*>(c) = out;
         } else {
             float acc = W[e];
             for (int s = 1; s < splits; ++s) acc += W[s * mn + e];
-            float out = p.alpha * acc;
-            if (!beta0) out += p.beta * *c;
-            *c = out;
+            *c = epilogue_value(p, acc, beta0 ? 0.f : *c, beta0, i, j);
         }
     }
 }

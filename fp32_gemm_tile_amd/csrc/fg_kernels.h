@@ -28,7 +28,16 @@ struct GemmParams {
     // c_split_stride is 0.
     int32_t kt_per_split;
     int64_t c_split_stride;
+    // Fused epilogue (FLAG_EPI): C = act(alpha * r_i * c_j * acc + beta * C
+    // + u_i + w_j). A null vector means ones (scales) or zeros (biases).
+    const float* row_scale;  // r, M floats
+    const float* col_scale;  // c, N floats
+    const float* row_bias;   // u, M floats
+    const float* col_bias;   // w, N floats
+    int32_t act;             // ACT_* below
 };
+
+enum : int32_t { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_SILU = 3 };
 
 enum : int32_t {
     FLAG_VEC_A = 1,    // A rows start 16-byte aligned: 128-bit loads allowed
@@ -37,6 +46,7 @@ enum : int32_t {
     FLAG_BETA0 = 8,    // beta == 0: C is written, never read
     FLAG_XCD_REMAP = 16,  // remap workgroup ids so each XCD gets a contiguous tile range
     FLAG_VEC2_C = 32,  // C rows start 8-byte aligned: 64-bit loads/stores
+    FLAG_EPI = 64,     // apply the fused epilogue (scales, biases, activation)
 };
 
 // Launchers: enqueue one kernel on `stream`; return the HIP launch status.
@@ -50,9 +60,11 @@ hipError_t launch_valu(int variant, int trans_a, int trans_b, const GemmParams& 
 // once per block.
 hipError_t launch_skinny(int trans_a, int trans_b, const GemmParams& p, hipStream_t stream);
 // C = beta * C (beta == 0: C = 0 without reading it); for K == 0 or alpha == 0.
+// With FLAG_EPI: C = act(beta * C + u_i + w_j).
 hipError_t launch_scale(const GemmParams& p, hipStream_t stream);
 // Split-K reduction: C = alpha * sum_{s < splits} W_s + beta * C, where W_s is
-// the dense M x N slice W + s * M * N; the sum runs in ascending s.
+// the dense M x N slice W + s * M * N; the sum runs in ascending s. With
+// FLAG_EPI the fused epilogue is applied to that sum.
 hipError_t launch_splitk_reduce(const float* W, int32_t splits, const GemmParams& p,
                                 hipStream_t stream);
 // Machine probes (fg_probe.hip): an MFMA-only loop and a streaming read.

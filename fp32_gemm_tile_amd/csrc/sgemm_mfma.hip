@@ -465,7 +465,8 @@ sgemm_mfma_kernel(GemmParams p) {
         }
     }
 
-    // Epilogue: C = alpha * acc + beta * C, 128-bit where possible.
+    // Epilogue: C = alpha * acc + beta * C, 128-bit where possible, or with
+    // FLAG_EPI C = act(alpha * r_i * c_j * acc + beta * C + u_i + w_j).
     // Accumulator register r of a 32x32 block, lane (i = lane%32, h = lane/32),
     // holds block row 8*(r/4) + 4*h + r%4 and block column i.
     const int64_t c_org = (int64_t)m0 * p.ldc + n0;
@@ -480,38 +481,71 @@ sgemm_mfma_kernel(GemmParams p) {
     const int col0 = wave_n * WN + NB * li;  // first of this lane's NB columns
     const int cols_left = p.N - n0 - col0;
     const bool full_vec = vec_c && cols_left >= NB;
+    // Two copies of the store loop, chosen by a uniform branch: the plain
+    // one, and the fused epilogue, which reads r_i, c_j, u_i, w_j per element
+    // (cached loads) and stores with 32-bit accesses. One loop holding both
+    // grew past what the compiler fully unrolls, and the accumulators then
+    // went to scratch memory for the whole kernel.
+    const bool epi = p.flags & FLAG_EPI;
+    if (!epi) {
 #pragma unroll
-    for (int a = 0; a < MB; ++a) {
+        for (int a = 0; a < MB; ++a) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int brow = 8 * (r / 4) + 4 * lh + (r % 4);
-            const int row = wave_m * WM + MB * brow + a;
-            if (m0 + row >= p.M) continue;
-            const uint32_t off = (uint32_t)(row * p.ldc + col0) * 4u;
-            float v[NB];
+            for (int r = 0; r < 16; ++r) {
+                const int brow = 8 * (r / 4) + 4 * lh + (r % 4);
+                const int row = wave_m * WM + MB * brow + a;
+                if (m0 + row >= p.M) continue;
+                const uint32_t off = (uint32_t)(row * p.ldc + col0) * 4u;
+                float v[NB];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) v[b] = alpha * acc[a][b][r];
-            if constexpr (NB == 4) {
-                if (full_vec) {
-                    f4 o = {v[0], v[1], v[2], v[3]};
-                    if (!beta0) o = o + beta * ld4(rc, off);
-                    st4(rc, off, o);
-                    continue;
+                for (int b = 0; b < NB; ++b) v[b] = alpha * acc[a][b][r];
+                if constexpr (NB == 4) {
+                    if (full_vec) {
+                        f4 o = {v[0], v[1], v[2], v[3]};
+                        if (!beta0) o = o + beta * ld4(rc, off);
+                        st4(rc, off, o);
+                        continue;
+                    }
+                } else if constexpr (NB == 2) {
+                    if (full_vec) {
+                        f2 o = {v[0], v[1]};
+                        if (!beta0) o = o + beta * ld2(rc, off);
+                        st2(rc, off, o);
+                        continue;
+                    }
                 }
-            } else if constexpr (NB == 2) {
-                if (full_vec) {
-                    f2 o = {v[0], v[1]};
-                    if (!beta0) o = o + beta * ld2(rc, off);
-                    st2(rc, off, o);
-                    continue;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (b < cols_left) {
+                        float o = v[b];
+                        if (!beta0) o += beta * ld1(rc, off + 4 * b);
+                        st1(rc, off + 4 * b, o);
+                    }
                 }
             }
+        }
+    } else {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                if (b < cols_left) {
-                    float o = v[b];
-                    if (!beta0) o += beta * ld1(rc, off + 4 * b);
-                    st1(rc, off + 4 * b, o);
+        for (int a = 0; a < MB; ++a) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int brow = 8 * (r / 4) + 4 * lh + (r % 4);
+                const int row = wave_m * WM + MB * brow + a;
+                if (m0 + row >= p.M) continue;
+                const uint32_t off = (uint32_t)(row * p.ldc + col0) * 4u;
+                const int64_t i = (int64_t)m0 + row;
+                const float sr = p.row_scale ? alpha * p.row_scale[i] : alpha;
+                const float rbi = p.row_bias ? p.row_bias[i] : 0.f;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (b < cols_left) {
+                        const int64_t j = (int64_t)n0 + col0 + b;
+                        const float cs = p.col_scale ? p.col_scale[j] : 1.f;
+                        const float cb = p.col_bias ? p.col_bias[j] : 0.f;
+                        float o = (sr * cs) * acc[a][b][r];
+                        if (!beta0) o += beta * ld1(rc, off + 4 * b);
+                        st1(rc, off + 4 * b, activate((o + rbi) + cb, p.act));
+                    }
                 }
             }
         }

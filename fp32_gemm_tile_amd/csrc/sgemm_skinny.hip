@@ -162,9 +162,8 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
 #pragma unroll
                 for (int w = 1; w < NW; ++w) s += red[w][m][4 * g + j];
                 const uint32_t off = (uint32_t)(m * p.ldc + 4 * g + j) * 4u;
-                float o = p.alpha * s;
-                if (!beta0) o += p.beta * ld1(rc, off);
-                st1(rc, off, o);
+                const float cin = beta0 ? 0.f : ld1(rc, off);
+                st1(rc, off, epilogue_value(p, s, cin, beta0, (int64_t)m0 + m, (int64_t)n0 + 4 * g + j));
             }
         }
     }
@@ -250,9 +249,8 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_k_kernel(GemmParams p) 
             const float s = group_sum<0x3F>(acc[m][c]);
             if (lane == 0 && m < rows_left && c < cols_left) {
                 const uint32_t off = (uint32_t)(m * p.ldc + c) * 4u;
-                float o = p.alpha * s;
-                if (!beta0) o += p.beta * ld1(rc, off);
-                st1(rc, off, o);
+                const float cin = beta0 ? 0.f : ld1(rc, off);
+                st1(rc, off, epilogue_value(p, s, cin, beta0, (int64_t)m0 + m, (int64_t)n0 + c));
             }
         }
 }

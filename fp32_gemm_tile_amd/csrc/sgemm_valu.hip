@@ -177,17 +177,21 @@ sgemm_valu_kernel(GemmParams p) {
             const int col = g * SN + 4 * tx;
             const uint32_t off = (uint32_t)(row * p.ldc + col) * 4u;
             if (vec_c) {
-                f4 o = {p.alpha * acc[i][4 * g], p.alpha * acc[i][4 * g + 1],
-                        p.alpha * acc[i][4 * g + 2], p.alpha * acc[i][4 * g + 3]};
-                if (!beta0) o = o + p.beta * ld4(rc, off);
+                const f4 cin = beta0 ? f4{0.f, 0.f, 0.f, 0.f} : ld4(rc, off);
+                f4 o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[j] = epilogue_value(p, acc[i][4 * g + j], cin[j], beta0, (int64_t)m0 + row,
+                                          (int64_t)n0 + col + j);
                 st4(rc, off, o);
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if (n0 + col + j < p.N) {
-                        float o = p.alpha * acc[i][4 * g + j];
-                        if (!beta0) o += p.beta * ld1(rc, off + 4 * j);
-                        st1(rc, off + 4 * j, o);
+                        const float cin = beta0 ? 0.f : ld1(rc, off + 4 * j);
+                        st1(rc, off + 4 * j,
+                            epilogue_value(p, acc[i][4 * g + j], cin, beta0, (int64_t)m0 + row,
+                                           (int64_t)n0 + col + j));
                     }
                 }
             }

@@ -155,6 +155,50 @@ fg_status fg_sgemm_splitk(fg_op transA, fg_op transB, int64_t M, int64_t N, int6
                           float* C, int64_t ldc, int32_t splits,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Activations of the fused epilogue (binary32). */
+typedef enum fg_activation {
+    FG_ACT_NONE = 0,
+    FG_ACT_RELU = 1, /* max(x, 0); NaN stays NaN */
+    FG_ACT_GELU = 2, /* x * Phi(x) = x * (1 + erf(x / sqrt(2))) / 2 (erf form) */
+    FG_ACT_SILU = 3  /* x * sigma(x) = x / (1 + exp(-x)) */
+} fg_activation;
+
+/* Operations fused after the product; every vector is device memory owned by
+ * the caller (any 4-byte alignment), or NULL for the neutral value. */
+typedef struct fg_epilogue {
+    const float* row_scale; /* r, M floats (NULL: ones) */
+    const float* col_scale; /* c, N floats (NULL: ones) */
+    const float* row_bias;  /* u, M floats (NULL: zeros) */
+    const float* col_bias;  /* w, N floats (NULL: zeros) */
+    int32_t activation;     /* fg_activation */
+} fg_epilogue;
+
+/*
+ * fg_sgemm_fused: the GEMM with an epilogue fused into its store, as in the
+ * closing remarks of "Optimising fp32 GEMM on A100", section "Performance
+ * comparison" (operations after a GEMM are fused into it as an epilogue):
+ *
+ *     C(i,j) = act( alpha * r_i * c_j * (op(A) op(B))(i,j) + beta * C(i,j) + u_i + w_j )
+ *
+ * evaluated in binary32 in that order. Per-row / per-column scales, biases
+ * and the activation set are this library's choice of epilogue (the page
+ * names none).
+ *
+ * Arguments 1-13 as for fg_sgemm, then:
+ *   14 epilogue  : NULL (plain GEMM) or a description as above; an activation
+ *                  outside fg_activation is rejected
+ *   15 stream
+ *   16 config_id : -1 = automatic, else a table index (as fg_sgemm_ex)
+ * Quick returns as for fg_sgemm, except that with any epilogue operation
+ * (K == 0 or alpha == 0) and beta == 1 still runs: C = act(C + u_i + w_j).
+ * With beta == 0, C is not read. No split-K here.
+ */
+fg_status fg_sgemm_fused(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                         float alpha, const float* A, int64_t lda,
+                         const float* B, int64_t ldb, float beta,
+                         float* C, int64_t ldc, const fg_epilogue* epilogue,
+                         hipStream_t stream, int32_t config_id);
+
 /* Bytes of workspace fg_sgemm_splitk needs for `splits` slices of an M x N
  * result (0 when splits <= 1 or the result is empty). Host only. */
 size_t fg_sgemm_splitk_workspace_size(int64_t M, int64_t N, int32_t splits);

@@ -70,7 +70,7 @@ def check(c_gpu, c_ref, sabs, K, alpha=1.0, beta=0.0, cin=None, frob=True):
 
 
 def epilogue_tol(K, alpha, beta, sabs, cin, v_ref, row_scale=None, col_scale=None,
-                 row_bias=None, col_bias=None, act="none"):
+                 row_bias=None, col_bias=None, act="none", per_element=False):
     """Per-element bound for the fused epilogue
     D = act(alpha * r_i * c_j * s_ij + beta * C_ij + u_i + w_j).
 
@@ -84,19 +84,26 @@ def epilogue_tol(K, alpha, beta, sabs, cin, v_ref, row_scale=None, col_scale=Non
     The activation stretches that by at most its largest slope (1 for relu,
     1.129 for gelu, 1.1 for silu) and its own binary32 evaluation adds at most
     2^-20 * |v| (a few units in the last place of erf / exp and the products
-    around them)."""
+    around them). per_element: the four vectors are given already gathered
+    at the checked elements (arrays of the shape of sabs) instead of as
+    length-M / length-N vectors."""
     from .epilogue import LIPSCHITZ
     sabs = np.asarray(sabs, dtype=np.float64)
-    M, N = sabs.shape
-    r = np.ones(M) if row_scale is None else np.asarray(row_scale, np.float64).ravel()
-    c = np.ones(N) if col_scale is None else np.asarray(col_scale, np.float64).ravel()
-    t = np.abs(float(alpha) * r[:, None] * c[None, :]) * sabs
+    if per_element:
+        # vectors already gathered at the checked elements (shape of sabs)
+        def row(v, fill):
+            return fill if v is None else np.asarray(v, np.float64)
+        col = row
+    else:
+        def row(v, fill):
+            return fill if v is None else np.asarray(v, np.float64).ravel()[:, None]
+
+        def col(v, fill):
+            return fill if v is None else np.asarray(v, np.float64).ravel()[None, :]
+    t = np.abs(float(alpha) * row(row_scale, 1.0) * col(col_scale, 1.0)) * sabs
     if beta != 0 and cin is not None:
         t = t + abs(float(beta)) * np.abs(np.asarray(cin, dtype=np.float64))
-    if row_bias is not None:
-        t = t + np.abs(np.asarray(row_bias, np.float64).ravel())[:, None]
-    if col_bias is not None:
-        t = t + np.abs(np.asarray(col_bias, np.float64).ravel())[None, :]
+    t = t + np.abs(row(row_bias, 0.0)) + np.abs(col(col_bias, 0.0))
     tol_v = 8.0 * max(int(K), 1) * U32 * t + ABS_FLOOR
     if act == "none":
         return tol_v
@@ -104,7 +111,8 @@ def epilogue_tol(K, alpha, beta, sabs, cin, v_ref, row_scale=None, col_scale=Non
 
 
 def check_epilogue(d_gpu, d_ref, v_ref, sabs, K, alpha, beta, cin=None, row_scale=None,
-                   col_scale=None, row_bias=None, col_bias=None, act="none", frob=True):
+                   col_scale=None, row_bias=None, col_bias=None, act="none", frob=True,
+                   per_element=False):
     """(ok, info) for a fused-epilogue result, as check() for the plain GEMM:
     every element within epilogue_tol and the relative Frobenius error of the
     whole result at most 1e-5."""
@@ -116,7 +124,7 @@ def check_epilogue(d_gpu, d_ref, v_ref, sabs, K, alpha, beta, cin=None, row_scal
     if d_ref.size == 0:
         return True, info
     tol = epilogue_tol(K, alpha, beta, sabs, cin, v_ref, row_scale, col_scale, row_bias,
-                       col_bias, act)
+                       col_bias, act, per_element)
     err = np.abs(d_gpu - d_ref)
     finite = np.isfinite(d_gpu)
     ratio = np.where(finite, err / tol, np.inf)

@@ -90,3 +90,22 @@ def epilogue(s, alpha, beta, cin, row_scale=None, col_scale=None, row_bias=None,
     """D = act(pre_activation(...)) in binary64; returns (D, v)."""
     v = pre_activation(s, alpha, beta, cin, row_scale, col_scale, row_bias, col_bias)
     return activation(v, act), v
+
+
+def epilogue_elems(s, alpha, beta, cin, ii, jj, row_scale=None, col_scale=None,
+                   row_bias=None, col_bias=None, act="none"):
+    """The same definition at a list of elements (ii[t], jj[t]): s and cin
+    hold the plain product and the old C at those elements. Returns (D, v)
+    of shape (len(ii),)."""
+    s = np.asarray(s, dtype=np.float64)
+    ii = np.asarray(ii)
+    jj = np.asarray(jj)
+    r = np.ones(s.shape) if row_scale is None else np.asarray(row_scale, np.float64)[ii]
+    c = np.ones(s.shape) if col_scale is None else np.asarray(col_scale, np.float64)[jj]
+    u = np.zeros(s.shape) if row_bias is None else np.asarray(row_bias, np.float64)[ii]
+    w = np.zeros(s.shape) if col_bias is None else np.asarray(col_bias, np.float64)[jj]
+    v = float(alpha) * r * c * s
+    if beta != 0:
+        v = v + float(beta) * np.asarray(cin, dtype=np.float64)
+    v = v + u + w
+    return activation(v, act), v

@@ -252,3 +252,24 @@ def test_probe_validation_and_flop_count():
     assert fg.fg_probe_read(4100, 8, 4, 4096) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 1
     assert fg.fg_probe_read(4096, 8, 0, 4096) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 3
     assert fg.fg_probe_read(4096, 8, 4, 0) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 4
+
+
+def test_fused_validation_and_quick_returns():
+    ep = fg.make_epilogue(activation="relu")
+    call = lambda **kw: fg.fg_sgemm_fused(kw.get("ta", 0), 0, kw.get("M", 4), 4, kw.get("K", 4),
+                                          kw.get("alpha", 1.0), 16, 4, 16, 4, kw.get("beta", 0.0),
+                                          16, 4, kw.get("ep", ep), 0, kw.get("cfg", -1))
+    bad = fg.make_epilogue(activation=7)
+    assert call(ep=bad) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 14
+    bad.activation = -1
+    assert call(ep=bad) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 14
+    assert call(cfg=fg.fg_num_configs()) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 16
+    assert call(ta=5) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 1
+    # nothing to do without a GPU: empty result
+    assert call(M=0) == fg.FG_OK
+    # K == 0 with beta == 1 is a no-op for the plain call, but not with an
+    # activation: it must reach the device check (no GPU here)
+    assert fg.fg_sgemm_fused(0, 0, 4, 4, 0, 1.0, 0, 1, 0, 4, 1.0, 16, 4, None, 0, -1) == fg.FG_OK
+    assert call(K=0, beta=1.0) != fg.FG_OK and fg.fg_last_bad_arg() == 0
+    # an epilogue with nothing in it behaves as the plain call
+    assert call(K=0, beta=1.0, ep=fg.make_epilogue()) == fg.FG_OK

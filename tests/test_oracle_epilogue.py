@@ -144,11 +144,15 @@ MUTANTS = [
     ("row_bias_as_column", "return v + u[:, None] + w[None, :]",
      "return v + u[:M, None] * 0 + u.sum() + w[None, :]"),
     ("col_bias_dropped", "return v + u[:, None] + w[None, :]", "return v + u[:, None]"),
-    ("scale_on_beta_term_too", "v = v + float(beta) * np.asarray(cin, dtype=np.float64)",
-     "v = v + float(beta) * r[:, None] * np.asarray(cin, dtype=np.float64)"),
+    ("scale_on_beta_term_too",
+     "v = v + float(beta) * np.asarray(cin, dtype=np.float64)\n    return v + u[:, None]",
+     "v = v + float(beta) * r[:, None] * np.asarray(cin, dtype=np.float64)\n"
+     "    return v + u[:, None]"),
     ("col_scale_ignored", "v = float(alpha) * r[:, None] * c[None, :] * s",
      "v = float(alpha) * r[:, None] * s"),
-    ("beta_dropped", "v = v + float(beta) * np.asarray(cin, dtype=np.float64)", "v = v"),
+    ("beta_dropped",
+     "v = v + float(beta) * np.asarray(cin, dtype=np.float64)\n    return v + u[:, None]",
+     "v = v\n    return v + u[:, None]"),
 ]
 
 
@@ -173,3 +177,25 @@ def test_epilogue_mutant_fails_a_pin(tmp_path, name, old, new):
         except (AssertionError, ValueError, IndexError):
             failed.append(pin.__name__)
     assert failed, f"mutant {name} passed every pin"
+
+
+def test_epilogue_elems_equals_full():
+    rng = np.random.default_rng(21)
+    M, N = 7, 11
+    s = rng.standard_normal((M, N))
+    cin = rng.standard_normal((M, N))
+    vecs = [rng.standard_normal(M), rng.standard_normal(N), rng.standard_normal(M),
+            rng.standard_normal(N)]
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    for act in real_ep.ACTIVATIONS:
+        d, v = real_ep.epilogue(s, 1.3, 0.4, cin, *vecs, act=act)
+        de, ve = real_ep.epilogue_elems(s[ii, jj].ravel(), 1.3, 0.4, cin[ii, jj].ravel(),
+                                        ii.ravel(), jj.ravel(), *vecs, act=act)
+        assert np.array_equal(de, d.ravel()) and np.array_equal(ve, v.ravel()), act
+        from oracle import compare
+        t_full = compare.epilogue_tol(5, 1.3, 0.4, np.abs(s), cin, v, *vecs, act)
+        t_el = compare.epilogue_tol(5, 1.3, 0.4, np.abs(s).ravel(), cin.ravel(), ve,
+                                    vecs[0][ii.ravel()], vecs[1][jj.ravel()],
+                                    vecs[2][ii.ravel()], vecs[3][jj.ravel()], act,
+                                    per_element=True)
+        assert np.allclose(t_full.ravel(), t_el, rtol=1e-15, atol=0), act
