@@ -68,7 +68,8 @@ def load_traffic(workload, kernel_config):
     return t.get("bytes_per_launch")
 
 
-def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock=False):
+def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock=False,
+             epilogue=None):
     """Time `steps` calls on the current stream with a HIP event pair around
     each call. Warm (default): the calls run back to back and the mean is the
     whole range over `steps`. Cold: a 512 MiB device write runs before each
@@ -89,12 +90,23 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock
     ws = torch.empty(64 << 20, dtype=torch.float32, device="cuda") if splitk else None
     nsplit = int(splitk) if splitk and not isinstance(splitk, bool) else 0
     flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda") if cold else None
+    epi = None
+    if epilogue is not None:
+        # every vector present: the most work the fused epilogue can do
+        g = torch.Generator().manual_seed(w.seed)
+        vecs = [torch.rand(n, generator=g).cuda() + 0.5 for n in (w.M, w.N)] + \
+               [torch.randn(n, generator=g).cuda() for n in (w.M, w.N)]
+        epi = fg.make_epilogue(*[v.data_ptr() for v in vecs], epilogue)
 
     def step():
         if splitk:
             st = fg.fg_sgemm_splitk(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
                                     w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
                                     nsplit, ws.data_ptr(), ws.numel() * 4, sp)
+        elif epi is not None:
+            st = fg.fg_sgemm_fused(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
+                                   w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
+                                   epi, sp, config)
         else:
             st = fg.fg_sgemm_ex(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
                                 w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
@@ -297,10 +309,10 @@ def copy_probe(nbytes=1 << 30, reps=3):
 
 
 def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False, cold=False,
-            sample_clock=False):
+            sample_clock=False, epilogue=None):
     from fp32_gemm_tile_amd import workloads as wl
     w = wl.WORKLOADS[name]
-    g = time_gpu(w, steps, warmup, config, splitk, cold, sample_clock)
+    g = time_gpu(w, steps, warmup, config, splitk, cold, sample_clock, epilogue)
     tflops = w.flops / (g["ms_per_launch"] * 1e-3) / 1e12
     gbs = w.compulsory_bytes / (g["ms_per_launch"] * 1e-3) / 1e9
     traffic = load_traffic(name, g["config"])
@@ -335,6 +347,7 @@ def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False, cold=False,
         "ms_min": round(g["ms_min"], 4),
         "tflops_at_median": round(w.flops / (g["ms_median"] * 1e-3) / 1e12, 3),
         "caches": "cold (512 MiB written before each call)" if cold else "warm",
+        "epilogue": epilogue or "alpha/beta only",
         "gpu_clock_mhz_under_load": g["clock_mhz"],
         "hbm_gbs_compulsory": round(gbs, 1),
         "roofline": roof,
@@ -365,6 +378,9 @@ def main():
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured MFMA-peak and HBM-read probes and the "
                          "clock sampling under load")
+    ap.add_argument("--epilogue", choices=("none", "relu", "gelu", "silu"), default=None,
+                    help="time fg_sgemm_fused with row/column scales and biases and this "
+                         "activation")
     ap.add_argument("--cold", action="store_true",
                     help="write 512 MiB before every timed call (operands out of cache)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -400,22 +416,25 @@ def main():
                 if cid >= 0 and fg.fg_get_config(cid)["kind"] == fg.FG_KIND_SKINNY \
                         and wl.WORKLOADS[name].M > 2048:
                     continue
-                r = run_one(name, args.steps, args.warmup, False, cid, _splitk_arg(args))
+                r = run_one(name, args.steps, args.warmup, False, cid, _splitk_arg(args),
+                            epilogue=args.epilogue)
                 print(json.dumps({"workload": name, "config": r["config"]["kernel_config"],
-                                  "forced": cid, "splitk": _splitk_arg(args), "tflops": r["value"],
+                                  "forced": cid, "splitk": _splitk_arg(args),
+                                  "epilogue": args.epilogue, "tflops": r["value"],
                                   "ms": r["ms_per_step"], "pct": r["pct_of_fp32_peak"],
                                   "roofline": r["roofline"]}),
                       flush=True)
         return
 
     r = run_one(args.workload, args.steps, args.warmup, False, args.config, _splitk_arg(args),
-                args.cold, sample_clock=not args.no_probes)
+                args.cold, sample_clock=not args.no_probes, epilogue=args.epilogue)
     # The 4096^3 shape of the metric, and one GPU's row block of 8192^3 split
     # over eight GPUs, timed in the same run.
     if args.workload == "C5a":
         r["also"] = {}
         for extra in ("C6", "S8"):
-            r2 = run_one(extra, args.steps, args.warmup, False, args.config, cold=args.cold)
+            r2 = run_one(extra, args.steps, args.warmup, False, args.config, cold=args.cold,
+                         epilogue=args.epilogue)
             r["also"][r2["config"]["workload"]] = {
                 k: r2[k] for k in ("value", "unit", "ms_per_step", "ms_median", "ms_min",
                                    "pct_of_fp32_peak")}

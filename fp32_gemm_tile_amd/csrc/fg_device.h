@@ -72,15 +72,54 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
+// erf(x) for binary32, branch free: formula 7.1.26 of Abramowitz and Stegun,
+// "Handbook of Mathematical Functions" (after Hastings),
+//     erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+//     t = 1 / (1 + p z),  z >= 0,
+// whose absolute error is at most 1.5e-7, applied to |x| with the sign put
+// back (erf is odd). With the binary32 rounding of these few operations the
+// result stays within about 4e-7 of erf(x). The library erff branches on the
+// size of |x|, which diverges across a wavefront in an epilogue.
+__device__ __forceinline__ float erf_as7126(float x) {
+    const float z = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.f));
+    float poly = fmaf(t, 1.061405429f, -1.453152027f);
+    poly = fmaf(t, poly, 1.421413741f);
+    poly = fmaf(t, poly, -0.284496736f);
+    poly = fmaf(t, poly, 0.254829592f);
+    poly *= t;
+    const float e = 1.f - poly * __expf(-z * z);
+    return copysignf(e, x);
+}
+
 // Fused-epilogue activation in binary32. relu keeps NaN (x < 0 is false for
-// it); gelu is the erf form x * Phi(x); silu is x * sigma(x), which tends to
-// -0 for very negative x (exp overflows to inf).
+// it); gelu is the erf form x * Phi(x) = x (1 + erf(x / sqrt 2)) / 2; silu is
+// x * sigma(x) = x / (1 + exp(-x)), which tends to -0 for very negative x (exp
+// overflows to inf and its reciprocal is 0). Hardware reciprocal and exp2
+// (about 1 ulp each) keep both short and branch free.
+template <int ACT>
+__device__ __forceinline__ float activate_t(float x) {
+    if constexpr (ACT == ACT_RELU) return x < 0.f ? 0.f : x;
+    else if constexpr (ACT == ACT_GELU)
+        return 0.5f * x * (1.f + erf_as7126(x * 0.70710678118654752f));
+    else if constexpr (ACT == ACT_SILU) return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
+    else return x;
+}
+
+// The same with the activation chosen at run time (per element).
 __device__ __forceinline__ float activate(float x, int act) {
-    if (act == ACT_RELU) return x < 0.f ? 0.f : x;
-    if (act == ACT_GELU) return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
-    if (act == ACT_SILU) return x / (1.f + expf(-x));
+    if (act == ACT_RELU) return activate_t<ACT_RELU>(x);
+    if (act == ACT_GELU) return activate_t<ACT_GELU>(x);
+    if (act == ACT_SILU) return activate_t<ACT_SILU>(x);
     return x;
 }
+
+// Compile-time activation tag, for code that picks the activation once and
+// runs a loop specialised for it.
+template <int A>
+struct ActTag {
+    static constexpr int value = A;
+};
 
 // Scale factor alpha * r_i * c_j of element (i, j) under FLAG_EPI.
 __device__ __forceinline__ float epi_scale(const GemmParams& p, int64_t i, int64_t j) {

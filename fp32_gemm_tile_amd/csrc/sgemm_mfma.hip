@@ -469,6 +469,10 @@ sgemm_mfma_kernel(GemmParams p) {
     // FLAG_EPI C = act(alpha * r_i * c_j * acc + beta * C + u_i + w_j).
     // Accumulator register r of a 32x32 block, lane (i = lane%32, h = lane/32),
     // holds block row 8*(r/4) + 4*h + r%4 and block column i.
+    // Lane position again from the hardware lane id (v_mbcnt): keeping the
+    // earlier values live across the main loop cost a register spill.
+    const int elane = (int)__lane_id();
+    const int eli = elane & 31, elh = elane >> 5;
     const int64_t c_org = (int64_t)m0 * p.ldc + n0;
     float* const Cs = p.C + (int64_t)blockIdx.y * p.c_split_stride;  // this split's C
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cs + c_org, p.c_extent - c_org);
@@ -478,21 +482,20 @@ sgemm_mfma_kernel(GemmParams p) {
     const bool vec_c = NB == 4 ? (p.flags & FLAG_VEC_C) != 0
                                : (NB == 2 ? (p.flags & FLAG_VEC2_C) != 0 : false);
     const float alpha = p.alpha, beta = p.beta;
-    const int col0 = wave_n * WN + NB * li;  // first of this lane's NB columns
+    const int col0 = wave_n * WN + NB * eli;  // first of this lane's NB columns
     const int cols_left = p.N - n0 - col0;
     const bool full_vec = vec_c && cols_left >= NB;
     // Two copies of the store loop, chosen by a uniform branch: the plain
-    // one, and the fused epilogue, which reads r_i, c_j, u_i, w_j per element
-    // (cached loads) and stores with 32-bit accesses. One loop holding both
-    // grew past what the compiler fully unrolls, and the accumulators then
-    // went to scratch memory for the whole kernel.
+    // one and the fused epilogue. One loop holding both grew past what the
+    // compiler fully unrolls, and the accumulators then went to scratch
+    // memory for the whole kernel.
     const bool epi = p.flags & FLAG_EPI;
     if (!epi) {
 #pragma unroll
         for (int a = 0; a < MB; ++a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int brow = 8 * (r / 4) + 4 * lh + (r % 4);
+                const int brow = 8 * (r / 4) + 4 * elh + (r % 4);
                 const int row = wave_m * WM + MB * brow + a;
                 if (m0 + row >= p.M) continue;
                 const uint32_t off = (uint32_t)(row * p.ldc + col0) * 4u;
@@ -525,29 +528,90 @@ sgemm_mfma_kernel(GemmParams p) {
             }
         }
     } else {
+        // The tile's slices of r, u (BM each) and c, w (BN each) are staged in
+        // the now idle operand ring, so that the per-row values come from LDS:
+        // global loads would share the vector-memory counter with the stores
+        // and every row would wait for the previous row's stores. Each
+        // element gets one inlined activation; the old C is read (and the
+        // result stored) as one vector when the lane's columns allow, else
+        // element by element.
+        static_assert(2 * (BM + BN) <= NS * (OpA::kStage + OpB::kStage), "vectors fit in LDS");
+        float* const vr = sA;           // r: BM, then u: BM, then c: BN, then w: BN
+        __syncthreads();                // every wave is done with the operand ring
+        const int etid = wave * 64 + elane;
+        for (int t = etid; t < BM; t += NT) {
+            const int64_t i = (int64_t)m0 + t;
+            const bool in = i < p.M;
+            vr[t] = (p.row_scale && in) ? p.row_scale[i] : 1.f;
+            vr[BM + t] = (p.row_bias && in) ? p.row_bias[i] : 0.f;
+        }
+        for (int t = etid; t < BN; t += NT) {
+            const int64_t j = (int64_t)n0 + t;
+            const bool in = j < p.N;
+            vr[2 * BM + t] = (p.col_scale && in) ? p.col_scale[j] : 1.f;
+            vr[2 * BM + BN + t] = (p.col_bias && in) ? p.col_bias[j] : 0.f;
+        }
+        __syncthreads();
+        float csc[NB], cbi[NB];
 #pragma unroll
-        for (int a = 0; a < MB; ++a) {
+        for (int b = 0; b < NB; ++b) {
+            csc[b] = vr[2 * BM + col0 + b];
+            cbi[b] = vr[2 * BM + BN + col0 + b];
+        }
+        // One copy of the store loop per activation, picked once (a per-element
+        // choice cost a chain of branches around every element).
+        auto store_tile = [&](auto tag) {
+            constexpr int ACT = decltype(tag)::value;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int brow = 8 * (r / 4) + 4 * lh + (r % 4);
-                const int row = wave_m * WM + MB * brow + a;
-                if (m0 + row >= p.M) continue;
-                const uint32_t off = (uint32_t)(row * p.ldc + col0) * 4u;
-                const int64_t i = (int64_t)m0 + row;
-                const float sr = p.row_scale ? alpha * p.row_scale[i] : alpha;
-                const float rbi = p.row_bias ? p.row_bias[i] : 0.f;
+            for (int a = 0; a < MB; ++a) {
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (b < cols_left) {
-                        const int64_t j = (int64_t)n0 + col0 + b;
-                        const float cs = p.col_scale ? p.col_scale[j] : 1.f;
-                        const float cb = p.col_bias ? p.col_bias[j] : 0.f;
-                        float o = (sr * cs) * acc[a][b][r];
-                        if (!beta0) o += beta * ld1(rc, off + 4 * b);
-                        st1(rc, off + 4 * b, activate((o + rbi) + cb, p.act));
+                for (int r = 0; r < 16; ++r) {
+                    const int brow = 8 * (r / 4) + 4 * elh + (r % 4);
+                    const int row = wave_m * WM + MB * brow + a;
+                    if (m0 + row >= p.M) continue;
+                    const uint32_t off = (uint32_t)(row * p.ldc + col0) * 4u;
+                    const float sr = alpha * vr[row];
+                    const float rbi = vr[BM + row];
+                    float v[NB];
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) v[b] = (sr * csc[b]) * acc[a][b][r];
+                    if (!beta0) {
+                        float cin[NB];
+                        if constexpr (NB == 4) {
+                            if (full_vec) {
+                                const f4 c4 = ld4(rc, off);
+#pragma unroll
+                                for (int b = 0; b < 4; ++b) cin[b] = c4[b];
+                            } else {
+#pragma unroll
+                                for (int b = 0; b < 4; ++b) cin[b] = b < cols_left ? ld1(rc, off + 4 * b) : 0.f;
+                            }
+                        } else {
+#pragma unroll
+                            for (int b = 0; b < NB; ++b) cin[b] = b < cols_left ? ld1(rc, off + 4 * b) : 0.f;
+                        }
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) v[b] += beta * cin[b];
                     }
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) v[b] = activate_t<ACT>((v[b] + rbi) + cbi[b]);
+                    if constexpr (NB == 4) {
+                        if (full_vec) {
+                            st4(rc, off, f4{v[0], v[1], v[2], v[3]});
+                            continue;
+                        }
+                    }
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        if (b < cols_left) st1(rc, off + 4 * b, v[b]);
                 }
             }
+        };
+        switch (p.act) {
+            case ACT_RELU: store_tile(ActTag<ACT_RELU>{}); break;
+            case ACT_GELU: store_tile(ActTag<ACT_GELU>{}); break;
+            case ACT_SILU: store_tile(ActTag<ACT_SILU>{}); break;
+            default: store_tile(ActTag<ACT_NONE>{}); break;
         }
     }
     (void)mn_interior;

@@ -58,7 +58,7 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
     const int g = lane & 7;                 // column group: 4 columns
     const int rcls = (lane >> 3) + 8 * wave;  // k class 0..31
     const int n0 = blockIdx.x * 32, m0 = blockIdx.y * MR;
-    const int rows_left = p.M - m0, cols_left = p.N - n0 - 4 * g;
+    const int rows_left = p.M - m0;
 
     float acc[MR][4];
 #pragma unroll
@@ -148,23 +148,21 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
             if (lane < 8) red[wave][m][4 * g + j] = s;
         }
     __syncthreads();
-    if (wave == 0 && lane < 8) {
-        const int64_t c_org = (int64_t)m0 * p.ldc + n0;
-        const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c_org, p.c_extent - c_org);
-        const bool beta0 = p.flags & FLAG_BETA0;
+    // One element of the MR x 32 block per thread (row t / 32, column t % 32):
+    // the wave sums in fixed order, then the epilogue and a coalesced store.
+    static_assert(MR * 32 <= kSkinnyThreads, "one thread per element");
+    {
+        const int m = threadIdx.x >> 5, col = threadIdx.x & 31;
+        if (m < MR && m < rows_left && col < p.N - n0) {
+            float s = red[0][m][col];
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            if (m >= rows_left) break;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (j >= cols_left) break;
-                float s = red[0][m][4 * g + j];
-#pragma unroll
-                for (int w = 1; w < NW; ++w) s += red[w][m][4 * g + j];
-                const uint32_t off = (uint32_t)(m * p.ldc + 4 * g + j) * 4u;
-                const float cin = beta0 ? 0.f : ld1(rc, off);
-                st1(rc, off, epilogue_value(p, s, cin, beta0, (int64_t)m0 + m, (int64_t)n0 + 4 * g + j));
-            }
+            for (int w = 1; w < NW; ++w) s += red[w][m][col];
+            const int64_t c_org = (int64_t)m0 * p.ldc + n0;
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c_org, p.c_extent - c_org);
+            const bool beta0 = p.flags & FLAG_BETA0;
+            const uint32_t off = (uint32_t)(m * p.ldc + col) * 4u;
+            const float cin = beta0 ? 0.f : ld1(rc, off);
+            st1(rc, off, epilogue_value(p, s, cin, beta0, (int64_t)m0 + m, (int64_t)n0 + col));
         }
     }
 }
@@ -239,20 +237,25 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_k_kernel(GemmParams p) 
         }
     }
 
-    const int64_t c_org = (int64_t)m0 * p.ldc + n0;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c_org, p.c_extent - c_org);
-    const bool beta0 = p.flags & FLAG_BETA0;
+    // Every lane ends up with every sum; lane 4m + c keeps element (m, c) and
+    // the MR x 4 elements go through the epilogue side by side.
+    float mine = 0.f;
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const float s = group_sum<0x3F>(acc[m][c]);
-            if (lane == 0 && m < rows_left && c < cols_left) {
-                const uint32_t off = (uint32_t)(m * p.ldc + c) * 4u;
-                const float cin = beta0 ? 0.f : ld1(rc, off);
-                st1(rc, off, epilogue_value(p, s, cin, beta0, (int64_t)m0 + m, (int64_t)n0 + c));
-            }
+            if (lane == 4 * m + c) mine = s;
         }
+    const int m = lane >> 2, c = lane & 3;
+    if (m < MR && m < rows_left && c < cols_left) {
+        const int64_t c_org = (int64_t)m0 * p.ldc + n0;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c_org, p.c_extent - c_org);
+        const bool beta0 = p.flags & FLAG_BETA0;
+        const uint32_t off = (uint32_t)(m * p.ldc + c) * 4u;
+        const float cin = beta0 ? 0.f : ld1(rc, off);
+        st1(rc, off, epilogue_value(p, mine, cin, beta0, (int64_t)m0 + m, (int64_t)n0 + c));
+    }
 }
 
 template <int MR>

@@ -109,6 +109,31 @@ def test_epilogue_oracle_pin(pin):
     pin(real_ep)
 
 
+def _gelu_as7126_f32(x):
+    """gelu with erf from formula 7.1.26 of Abramowitz and Stegun, every
+    operation rounded to binary32 (a stand-in for an approximate device
+    evaluation)."""
+    f = np.float32
+    x = np.asarray(x, dtype=np.float32)
+    z = np.abs(x * f(0.70710678118654752))
+    t = (f(1) / (f(1) + f(0.3275911) * z)).astype(np.float32)
+    poly = t * (f(0.254829592) + t * (f(-0.284496736) + t * (f(1.421413741) + t * (
+        f(-1.453152027) + t * f(1.061405429)))))
+    e = np.copysign(f(1) - poly.astype(np.float32) * np.exp(-z * z).astype(np.float32), x)
+    return (f(0.5) * x * (f(1) + e.astype(np.float32))).astype(np.float32)
+
+
+def test_epilogue_tolerance_covers_approximate_gelu():
+    """Formula 7.1.26 in binary32 stays inside the gelu part of the bound on
+    a dense sweep of inputs (tol_v set to 0 here: only the activation's own
+    error is being checked)."""
+    x = np.concatenate([np.linspace(-12, 12, 200001), np.geomspace(1e-30, 1e3, 20001)])
+    x = np.concatenate([x, -x]).astype(np.float32)
+    got = _gelu_as7126_f32(x).astype(np.float64)
+    want = real_ep.activation(x.astype(np.float64), "gelu")
+    assert np.all(np.abs(got - want) <= 2.0 ** -20 * np.abs(x.astype(np.float64)) + 1e-37)
+
+
 def test_epilogue_tolerance_covers_binary32_evaluation():
     """The bound of oracle.compare.epilogue_tol holds for the same epilogue
     evaluated step by step in binary32 (numpy float32, erf from binary64
