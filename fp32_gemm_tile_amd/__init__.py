@@ -123,6 +123,13 @@ def load_library(path: str = LIB_PATH):
     lib.fg_abi_version.restype = i32
     lib.fg_sgemm_fused.argtypes = gemm_args[:13] + [ctypes.POINTER(fg_epilogue), vp, i32]
     lib.fg_sgemm_fused.restype = i32
+    lib.fg_estimate_seconds.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.fg_estimate_seconds.restype = ctypes.c_double
+    lib.fg_get_efficiency.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_double)]
+    lib.fg_get_efficiency.restype = i32
+    lib.fg_set_efficiency.argtypes = [i32, ctypes.c_double, ctypes.c_double]
+    lib.fg_set_efficiency.restype = i32
     lib.fg_probe_mfma.argtypes = [i32, i32, vp, vp]
     lib.fg_probe_mfma.restype = i32
     lib.fg_probe_mfma_flops.argtypes = [i32, i32]
@@ -221,6 +228,22 @@ def fg_sgemm_fused(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
     ep = ctypes.byref(epilogue) if epilogue is not None else None
     return load_library().fg_sgemm_fused(_op(transA), _op(transB), M, N, K, alpha, A, lda,
                                          B, ldb, beta, C, ldc, ep, stream or None, config)
+
+
+def fg_estimate_seconds(M, N, K, config_id, splits=1, beta_zero=True) -> float:
+    """Cost-model estimate of one call with a given entry (fp32gemm_tune.h)."""
+    return load_library().fg_estimate_seconds(M, N, K, config_id, splits, int(bool(beta_zero)))
+
+
+def fg_get_efficiency(config_id):
+    """(eff, eff1) of a matrix-core entry."""
+    e, e1 = ctypes.c_double(), ctypes.c_double()
+    _raise_if(load_library().fg_get_efficiency(config_id, ctypes.byref(e), ctypes.byref(e1)))
+    return e.value, e1.value
+
+
+def fg_set_efficiency(config_id, eff, eff1) -> int:
+    return load_library().fg_set_efficiency(config_id, eff, eff1)
 
 
 def fg_probe_mfma(workgroups, iterations, out, stream=0) -> int:

@@ -23,6 +23,7 @@
 
 #include "../../include/fp32gemm.h"
 #include "../../include/fp32gemm_probe.h"
+#include "../../include/fp32gemm_tune.h"
 #include "fg_kernels.h"
 
 namespace {
@@ -57,8 +58,9 @@ struct Entry {
     fg_config cfg;
     int variant;   // index inside the kernel family's launcher
     int wps;       // resident waves per SIMD
-    double eff;    // relative efficiency for the cost model, SIMD full
-    double eff1;   // the same with one wave per SIMD (small grids)
+    double eff;    // default efficiency for the cost model, SIMD full
+    double eff1;   // the same with one wave per SIMD (small grids); both are
+                   // replaced by the generated table fg_tuned.inc
     int fallback;  // entry used instead when A or B rows are not 16-byte
                    // aligned (entries with 16-byte direct-to-LDS loads only;
                    // -1 = any alignment is fine)
@@ -93,8 +95,8 @@ Entry make_entry(int id, fg_kind kind, int variant, int bm, int bn, int bk, int 
 
 const Entry* table() {
     static const Entry t[] = {
-        // eff: fraction of the fp32 matrix peak measured at 8192^3 NN with
-        // the SIMDs full (bench.py --calibrate, profiles/calibration_*.md).
+        // eff / eff1 here are defaults (first calibration at 8192^3 NN); the
+        // values in use come from the generated table fg_tuned.inc.
         make_entry(0, FG_KIND_MFMA, 0, 256, 256, 16, 128, 128, 256, 2, 1, 0.857, "mfma_256x256x16_w2x2"),
         make_entry(1, FG_KIND_MFMA, 1, 256, 128, 16, 128, 128, 128, 2, 1, 0.866, "mfma_256x128x16_w2x1"),
         make_entry(2, FG_KIND_MFMA, 2, 128, 128, 16, 128, 128, 64, 2, 1, 0.850, "mfma_128x128x16_w1x1"),
@@ -114,7 +116,7 @@ const Entry* table() {
         make_entry(12, FG_KIND_MFMA, 10, 256, 128, 16, 128, 64, 256, 3, 2, 0.90, "mfma_256x128x16_w2x2_s3", 1, 0.86),
         // Few-row kernel: bm = rows per block (up to 8), bn = columns per
         // workgroup for B stored K x N; memory-bound, costed separately.
-        make_entry(13, FG_KIND_SKINNY, 0, 8, 32, 0, 8, 4, 256, 0, 2, 1.0, "valu_skinny_m8"),
+        make_entry(13, FG_KIND_SKINNY, 0, 8, 32, 0, 8, 4, 256, 0, 2, 0.7, "valu_skinny_m8"),
         // Small tiles for grids the entries above leave under-filled; several
         // workgroups share a CU.
         // eff1: measured with one workgroup per CU (M <= 256, N = K = 4096).
@@ -125,6 +127,38 @@ const Entry* table() {
     return t;
 }
 constexpr int kNumEntries = 17;
+
+// Cost-model efficiencies, one pair per entry: from the generated table
+// (fg_tuned.inc) over the defaults above, and replaceable at run time by a
+// tuner (fg_set_efficiency). Atomics: a tuner may set them while other
+// threads plan calls.
+struct Efficiency {
+    std::atomic<double> eff, eff1;
+};
+
+Efficiency* efficiencies() {
+    static Efficiency e[kNumEntries];
+    static std::once_flag once;
+    std::call_once(once, [] {
+        struct Tuned {
+            int id;
+            double eff, eff1;
+        };
+        static const Tuned tuned[] = {
+#include "fg_tuned.inc"
+        };
+        for (int i = 0; i < kNumEntries; ++i) {
+            e[i].eff.store(table()[i].eff);
+            e[i].eff1.store(table()[i].eff1);
+        }
+        for (const Tuned& t : tuned) {
+            if (t.id < 0 || t.id >= kNumEntries) continue;
+            e[t.id].eff.store(t.eff);
+            e[t.id].eff1.store(t.eff1);
+        }
+    });
+    return e;
+}
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -160,8 +194,9 @@ double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, boo
     for (int64_t left = tiles * s; left > 0;) {
         const int64_t per_cu = std::min<int64_t>(cdiv(left, kNumCUs), slots);
         const int64_t share = std::max<int64_t>(1, cdiv(per_cu * w, kSimdsPerCU));
-        const double eff =
-            e.wps > 1 ? e.eff1 + (e.eff - e.eff1) * (double)(share - 1) / (e.wps - 1) : e.eff;
+        const double full = efficiencies()[e.cfg.id].eff.load(std::memory_order_relaxed);
+        const double one = efficiencies()[e.cfg.id].eff1.load(std::memory_order_relaxed);
+        const double eff = e.wps > 1 ? one + (full - one) * (double)(share - 1) / (e.wps - 1) : full;
         t += wave_flops * (double)share / (eff * kSimdFlops);
         left -= per_cu * kNumCUs;
     }
@@ -170,24 +205,25 @@ double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, boo
     return t;
 }
 
-// Few-row kernel, fitted to measurements on one MI355X: a workgroup owns 32
-// columns of C for one block of up to 8 rows and walks K in steps of 32 rows
-// of op(B). One workgroup per CU is latency-bound (a step takes 0.17 us with
-// one row, 0.27 us with eight); with several per CU the CU's throughput
-// (0.1 us per workgroup-step) takes over. op(B) crosses HBM at least once.
-// The fixed cost covers the launch and the final cross-wave reduction.
-constexpr double kSkinnyFixed = 7e-6;
+// Few-row kernel, modelled from measurements on one MI355X: a workgroup owns
+// 32 columns of C for one block of up to 8 rows and walks K in steps of 32
+// rows of op(B). One workgroup per CU is latency-bound (a step costs about
+// 0.12 + 0.01 * (rows - 1) us at efficiency 1); with several per CU the CU's
+// throughput (0.07 us per workgroup-step) takes over. The entry's efficiency
+// (0.7 by default, fitted by the tuner) divides both. op(B) crosses HBM at
+// least once. The fixed cost covers the launch and the final reduction.
+constexpr double kSkinnyFixed = 5e-6;
 constexpr double kHbmPeakish = 6.3e12;  // best streaming rate measured (GEMV)
-double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0) {
+double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0, double eff) {
     const int64_t rows = M < 8 ? M : 8;
     const double blocks = (double)cdiv(M, 8);
     const double wgs = blocks * (double)cdiv(N, 32);
     const double steps = (double)cdiv(K, 32);
     const double per_cu = std::ceil(wgs / kNumCUs);
-    const double t_lat = steps * (0.17e-6 + (double)(rows - 1) * 0.0143e-6);
-    const double t_thr = per_cu * steps * 0.1e-6;
+    const double t_lat = steps * (0.12e-6 + (double)(rows - 1) * 0.01e-6);
+    const double t_thr = per_cu * steps * 0.07e-6;
     const double bytes = 4.0 * ((double)K * N + (double)M * K + (double)M * N * (beta0 ? 1 : 2));
-    return kSkinnyFixed + std::max(std::max(t_lat, t_thr), bytes / kHbmPeakish);
+    return kSkinnyFixed + std::max(std::max(t_lat, t_thr) / eff, bytes / kHbmPeakish);
 }
 
 // Best MFMA or few-row entry (and split count, at most max_splits). With
@@ -202,7 +238,7 @@ int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_s
         const Entry& e = table()[i];
         if (e.cfg.kind == FG_KIND_SKINNY) {
             if (mfma_only) continue;
-            const double c = skinny_cost(M, N, K, beta0);
+            const double c = skinny_cost(M, N, K, beta0, efficiencies()[i].eff.load());
             if (best < 0 || c < best_cost) {
                 best = i;
                 best_cost = c;
@@ -534,6 +570,38 @@ fg_status fg_sgemm_fused(fg_op transA, fg_op transB, int64_t M, int64_t N, int64
                     epilogue->activation);
     return run_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
                     config_id, 1, nullptr, 0, epilogue, 16);
+}
+
+double fg_estimate_seconds(int64_t M, int64_t N, int64_t K, int32_t config_id, int32_t splits,
+                           int32_t beta_zero) {
+    if (M < 0 || N < 0 || K < 0 || config_id < 0 || config_id >= kNumEntries) return -1.0;
+    const Entry& e = table()[config_id];
+    if (e.cfg.kind == FG_KIND_SKINNY)
+        return skinny_cost(M, N, K, beta_zero != 0, efficiencies()[config_id].eff.load());
+    if (e.cfg.kind != FG_KIND_MFMA) return -1.0;
+    return cost(e, M, N, K, splits < 1 ? 1 : splits, beta_zero != 0);
+}
+
+fg_status fg_get_efficiency(int32_t config_id, double* eff, double* eff1) {
+    clear_error();
+    if (config_id < 0 || config_id >= kNumEntries || table()[config_id].cfg.kind == FG_KIND_VALU)
+        return fail(FG_ERR_INVALID_ARG, 1, "config %d has no modelled efficiency", config_id);
+    if (!eff) return fail(FG_ERR_INVALID_ARG, 2, "eff is NULL");
+    if (!eff1) return fail(FG_ERR_INVALID_ARG, 3, "eff1 is NULL");
+    *eff = efficiencies()[config_id].eff.load();
+    *eff1 = efficiencies()[config_id].eff1.load();
+    return FG_OK;
+}
+
+fg_status fg_set_efficiency(int32_t config_id, double eff, double eff1) {
+    clear_error();
+    if (config_id < 0 || config_id >= kNumEntries || table()[config_id].cfg.kind == FG_KIND_VALU)
+        return fail(FG_ERR_INVALID_ARG, 1, "config %d has no modelled efficiency", config_id);
+    if (!(eff > 0.0 && eff <= 1.0)) return fail(FG_ERR_INVALID_ARG, 2, "eff outside (0, 1]");
+    if (!(eff1 > 0.0 && eff1 <= 1.0)) return fail(FG_ERR_INVALID_ARG, 3, "eff1 outside (0, 1]");
+    efficiencies()[config_id].eff.store(eff);
+    efficiencies()[config_id].eff1.store(eff1);
+    return FG_OK;
 }
 
 double fg_probe_mfma_flops(int32_t workgroups, int32_t iterations) {

@@ -1,0 +1,55 @@
+/*
+ * fp32gemm_tune -- hooks for tuning the tile-configuration table offline.
+ * Host only; no GPU is needed for any of these.
+ *
+ * fg_sgemm picks a table entry with a cost model (see fg_select_config). For
+ * every matrix-core entry the model holds two efficiencies: `eff`, the
+ * fraction of the fp32 matrix peak one wave reaches with its SIMD full, and
+ * `eff1`, the same with one wave per SIMD; the few-row entry has one (`eff`
+ * divides its modelled time per step of K, `eff1` is ignored there). The
+ * library starts from a
+ * generated table of them (fg_tuned.inc, written by the package's autotune
+ * module from timings of every entry on a grid of shapes), following the
+ * empirical configuration search of "How to get a matmul kernel into the
+ * top percentile (worklog)", section "Extra" (retune per GPU) and "Matmul
+ * II: register blocking, warp tiling, tensor cores", section 8 (many
+ * variants and a heuristic that picks one per call).
+ *
+ * Errors as in fp32gemm.h: fg_last_bad_arg() / fg_last_error().
+ */
+#ifndef FP32GEMM_TUNE_H
+#define FP32GEMM_TUNE_H
+
+#include "fp32gemm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * The model's estimate, in seconds, of one call of M x N x K with table
+ * entry config_id and `splits` split-K slices (values below 1 mean 1);
+ * beta_zero != 0 when beta == 0. Matrix-core and few-row entries only;
+ * returns -1 for a vector-ALU entry, an id out of range or a negative size.
+ * The layout flags do not enter the present model.
+ */
+double fg_estimate_seconds(int64_t M, int64_t N, int64_t K, int32_t config_id, int32_t splits,
+                           int32_t beta_zero);
+
+/* The efficiencies of entry config_id (arguments 2, 3: outputs, non-NULL).
+ * FG_ERR_INVALID_ARG (bad argument 1) for a vector-ALU entry (not modelled)
+ * or an id out of range. */
+fg_status fg_get_efficiency(int32_t config_id, double* eff, double* eff1);
+
+/*
+ * Replace the efficiencies of entry config_id (matrix-core or few-row) for
+ * this process (both in (0, 1]). Every later selection, on every thread, uses them. For
+ * tuners: a production build takes its values from fg_tuned.inc.
+ */
+fg_status fg_set_efficiency(int32_t config_id, double eff, double eff1);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP32GEMM_TUNE_H */

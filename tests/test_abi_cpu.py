@@ -273,3 +273,69 @@ def test_fused_validation_and_quick_returns():
     assert call(K=0, beta=1.0) != fg.FG_OK and fg.fg_last_bad_arg() == 0
     # an epilogue with nothing in it behaves as the plain call
     assert call(K=0, beta=1.0, ep=fg.make_epilogue()) == fg.FG_OK
+
+
+def test_tuning_hooks():
+    """The generated efficiency table is what the library uses, the model's
+    estimate reacts to a changed efficiency, and the hooks validate."""
+    import re
+    inc = open(os.path.join(ROOT, "fp32_gemm_tile_amd", "csrc", "fg_tuned.inc")).read()
+    rows = re.findall(r"\{(\d+), ([\d.]+), ([\d.]+)\}", inc)
+    assert rows
+    for i, e, e1 in rows:
+        got = fg.fg_get_efficiency(int(i))
+        assert abs(got[0] - float(e)) < 1e-12 and abs(got[1] - float(e1)) < 1e-12
+    t0 = fg.fg_estimate_seconds(8192, 8192, 8192, 7)
+    # 2*8192^3 FLOP at the tuned efficiency, plus one launch
+    eff = fg.fg_get_efficiency(7)[0]
+    assert abs(t0 - (2 * 8192 ** 3 / (eff * 157.3e12) + 3e-6)) < 1e-6 * t0 + 1e-7
+    old = fg.fg_get_efficiency(7)
+    try:
+        assert fg.fg_set_efficiency(7, old[0] / 2, old[1]) == fg.FG_OK
+        assert abs(fg.fg_estimate_seconds(8192, 8192, 8192, 7) / t0 - 2) < 0.01
+    finally:
+        assert fg.fg_set_efficiency(7, *old) == fg.FG_OK
+    assert fg.fg_estimate_seconds(8192, 8192, 8192, 5) == -1.0   # vector-ALU entry
+    assert fg.fg_estimate_seconds(1, 8192, 8192, 13) > 0          # few-row entry
+    assert fg.fg_set_efficiency(5, 0.5, 0.5) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 1
+    assert fg.fg_set_efficiency(7, 0.0, 0.5) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 2
+    assert fg.fg_set_efficiency(7, 0.5, 1.5) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 3
+    with pytest.raises(fg.FgError):
+        fg.fg_get_efficiency(5)
+    # the few-row entry has one efficiency dividing its modelled step time
+    old13 = fg.fg_get_efficiency(13)
+    t13 = fg.fg_estimate_seconds(64, 4096, 4096, 13)
+    try:
+        fg.fg_set_efficiency(13, old13[0] / 2, old13[1])
+        assert fg.fg_estimate_seconds(64, 4096, 4096, 13) > 1.5 * t13 - 5e-6
+    finally:
+        fg.fg_set_efficiency(13, *old13)
+
+
+def test_autotune_fit_recovers_known_efficiencies():
+    """The tuner's fit, given times that the model itself produces for known
+    efficiencies, finds those efficiencies again (host only)."""
+    from fp32_gemm_tile_amd import autotune
+    entry = 14  # 64 x 64 tiles: several waves per SIMD, both figures matter
+    old = fg.fg_get_efficiency(entry)
+    shapes = [(256, 256, 256), (1024, 1024, 1024), (2048, 2048, 2048), (128, 4096, 4096),
+              (4096, 4096, 4096)]
+    try:
+        fg.fg_set_efficiency(entry, 0.81, 0.47)
+        samples = [(M, N, K, fg.fg_estimate_seconds(M, N, K, entry)) for M, N, K in shapes]
+        eff, eff1, rms = autotune.fit_entry(entry, samples, True)
+        assert (eff, eff1) == (0.81, 0.47) and rms < 1e-6
+        assert fg.fg_get_efficiency(entry) == (0.81, 0.47)
+    finally:
+        fg.fg_set_efficiency(entry, *old)
+
+
+def test_autotune_candidates():
+    from fp32_gemm_tile_amd import autotune
+    names = lambda sh: {fg.fg_get_config(i)["name"] for i in autotune.candidates(sh)}
+    aligned = names((4096, 4096, 4096, "N", "N", None, None, None))
+    ragged = names((3001, 2047, 1025, "T", "N", 3001, 2047, 2047))
+    assert "mfma_256x256x16_w2x2_s4" in aligned and "valu_skinny_m8" not in aligned
+    assert "mfma_256x256x16_w2x2_s4" not in ragged and "mfma_64x64x16_w2x2_s4_dw" in ragged
+    assert "valu_skinny_m8" in names((64, 4096, 4096, "N", "N", None, None, None))
+    assert not any(n.startswith("valu_") and "skinny" not in n for n in aligned | ragged)
