@@ -50,7 +50,10 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-template <int MR, int TA, bool VEC>
+// PIPE: software-pipelined k loop (two blocks of op(B) in flight per wave,
+// more registers); for grids of at most a few workgroups per CU, where the
+// loads' latency is not hidden by other workgroups.
+template <int MR, int TA, bool VEC, bool PIPE>
 __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p) {
     // B stored K x N. Workgroup: columns [n0, n0 + 32), rows [m0, m0 + MR).
     constexpr int NW = kSkinnyThreads / 64;
@@ -75,16 +78,16 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
     constexpr bool STAGE_A = MR > 1;
     __shared__ __attribute__((aligned(16))) float sa[STAGE_A ? 2 : 1][KB][MR];
 
-    int it = 0;
-    for (int kb = 0; kb < p.K; kb += KB, ++it) {
+    // Loads of k block kb: this thread's op(A) values for the LDS stage (issued
+    // first, so that waiting for them leaves the B loads in flight) and its
+    // kUnrollMN 128-bit pieces of op(B). Past K both read as 0.
+    auto load_block = [&](int kb, float (&astage)[MR], f4 (&b)[kUnrollMN]) {
         // Buffer resources based at this k block keep the 32-bit offsets small.
         const int64_t a_org = TA ? (int64_t)kb * p.lda + m0 : (int64_t)m0 * p.lda + kb;
         const int64_t b_org = (int64_t)kb * p.ldb + n0;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_org, p.b_extent - b_org);
-        float astage[MR];
         if constexpr (STAGE_A) {
-            // Issued before the B loads so waiting for them leaves B in flight.
             const int kk = threadIdx.x;
             if (kb + kk < p.K) {
                 load_a<MR, TA>(ra, p.lda, rows_left, kk, astage);
@@ -93,7 +96,6 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
                 for (int m = 0; m < MR; ++m) astage[m] = 0.f;
             }
         }
-        f4 b[kUnrollMN];
 #pragma unroll
         for (int u = 0; u < kUnrollMN; ++u) {
             const int kk = rcls + 32 * u;  // k - kb
@@ -101,12 +103,18 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
             const f4 z = {0.f, 0.f, 0.f, 0.f};
             b[u] = kb + kk < p.K ? ld4_guard(rb, off, 4 * g, p.N - n0, VEC) : z;
         }
+    };
+    // The FMAs of k block kb (op(A) from LDS buffer `it & 1`, or from memory
+    // for one row).
+    auto compute_block = [&](int kb, int it, const float (&astage)[MR], const f4 (&b)[kUnrollMN]) {
         if constexpr (STAGE_A) {
             float* dst = &sa[it & 1][threadIdx.x][0];
 #pragma unroll
             for (int m = 0; m < MR; ++m) dst[m] = astage[m];
             lds_barrier();
         }
+        const int64_t a_org = TA ? (int64_t)kb * p.lda + m0 : (int64_t)m0 * p.lda + kb;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
 #pragma unroll
         for (int u = 0; u < kUnrollMN; ++u) {
             const int kk = rcls + 32 * u;
@@ -133,6 +141,32 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
             for (int m = 0; m < MR; ++m)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[m][j] = __builtin_fmaf(a[m], b[u][j], acc[m][j]);
+        }
+    };
+
+    // Software pipeline over k blocks: the loads of block i + 1 are issued
+    // before the FMAs of block i, so that each wave keeps two blocks of
+    // op(B) in flight (two register sets, used alternately).
+    // Without PIPE, one block at a time.
+    if constexpr (PIPE) {
+        float as0[MR], as1[MR];
+        f4 b0[kUnrollMN], b1[kUnrollMN];
+        if (p.K > 0) load_block(0, as0, b0);
+        int it = 0;
+        for (int kb = 0; kb < p.K; kb += 2 * KB, it += 2) {
+            if (kb + KB < p.K) load_block(kb + KB, as1, b1);
+            compute_block(kb, it, as0, b0);
+            if (kb + KB >= p.K) break;
+            if (kb + 2 * KB < p.K) load_block(kb + 2 * KB, as0, b0);
+            compute_block(kb + KB, it + 1, as1, b1);
+        }
+    } else {
+        int it = 0;
+        for (int kb = 0; kb < p.K; kb += KB, ++it) {
+            float as[MR];
+            f4 b[kUnrollMN];
+            load_block(kb, as, b);
+            compute_block(kb, it, as, b);
         }
     }
 
@@ -265,12 +299,30 @@ hipError_t launch_mr(int ta, int tb, const GemmParams& p, hipStream_t s) {
     const dim3 block(kSkinnyThreads);
     if (tb == 0) {  // B stored K x N
         const dim3 grid((p.N + 31) / 32, rblocks);
+        // Pipelined while the whole grid is resident at once (up to 3
+        // workgroups per CU, the pipelined kernel's occupancy; measured:
+        // 8 x 4096 x 4096 36.5 -> 32.8 us, 8 x 8192 x 8192 67.6 -> 62.6 us);
+        // beyond that the extra registers cost a round of workgroups
+        // (64 x 4096 x 4096, 1024 workgroups: 49 us plain, 69 pipelined).
+        // With one row the loop is light enough that the plain one streams
+        // as fast (1 x 8192 x 8192: 44.1 us plain, 45.8 pipelined).
+        const bool pipe = MR > 1 && (int64_t)grid.x * grid.y <= 3 * 256;
         if (ta == 0) {
-            if (vec_b) hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, true>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, false>), grid, block, 0, s, p);
+            if (vec_b) {
+                if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, true, true>), grid, block, 0, s, p);
+                else hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, true, false>), grid, block, 0, s, p);
+            } else {
+                if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, false, true>), grid, block, 0, s, p);
+                else hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, false, false>), grid, block, 0, s, p);
+            }
         } else {
-            if (vec_b) hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, true>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, false>), grid, block, 0, s, p);
+            if (vec_b) {
+                if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, true, true>), grid, block, 0, s, p);
+                else hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, true, false>), grid, block, 0, s, p);
+            } else {
+                if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, false, true>), grid, block, 0, s, p);
+                else hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, false, false>), grid, block, 0, s, p);
+            }
         }
     } else {  // B stored N x K
         const int cols_per_wg = 4 * (kSkinnyThreads / 64);

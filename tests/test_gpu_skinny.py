@@ -6,7 +6,7 @@ import fp32_gemm_tile_amd as fg
 from fp32_gemm_tile_amd import workloads as wl
 import oracle
 
-from gpu_util import check_full, check_sampled, run_fg
+from gpu_util import check_full, check_sampled, log, run_fg
 
 pytestmark = pytest.mark.gpu
 
@@ -72,3 +72,20 @@ def test_skinny_repeatable():
     o1, _ = run_fg(w, A, B, config=skinny_id())
     o2, _ = run_fg(w, A, B, config=skinny_id())
     assert np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("ta", ["N", "T"])
+def test_skinny_both_k_loops(ta):
+    """B stored K x N takes the software-pipelined k loop on grids of at most
+    768 workgroups with more than one row per block, and the plain one
+    otherwise: both, with a ragged last k block
+    and K shorter than one block, against the oracle."""
+    cid = skinny_id()
+    for i, (M, N, K) in enumerate([(8, 1000, 777), (200, 8192, 300), (130, 2047, 100),
+                                   (1, 9000, 2000), (3, 4000, 1500)]):
+        wgs = -(-N // 32) * -(-M // 8)
+        log(f"  grid {wgs} workgroups ({'pipelined' if wgs <= 768 and M > 1 else 'plain'} loop)")
+        w = wl.custom(M, N, K, ta, "N", alpha=1.5, beta=0.5, dist="normal", seed=120 + i)
+        A, B, C = wl.make_inputs(w)
+        out, _ = run_fg(w, A, B, C, config=cid)
+        check_full(w, A, B, C, out)
