@@ -8,12 +8,14 @@ Flags:
     must not form v_pk_* fp32 instructions on its own).
 Environment:
   FG_SAVE_TEMPS=1    keep the device assembly (.s) under _build/ for reading
-  FG_RESOURCE_USAGE=1  print per-kernel register/LDS/occupancy remarks
+  FG_RESOURCE_USAGE=1  print the per-kernel register/LDS/occupancy remarks (always
+                       written to _build/<source>.resources.txt)
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -39,8 +41,10 @@ def _compile(src: str, verbose: bool) -> str:
         cmd[1:1] = ["-x", "hip"]
         if os.environ.get("FG_SAVE_TEMPS"):
             cmd += ["-save-temps=obj"]
-        if os.environ.get("FG_RESOURCE_USAGE"):
-            cmd += ["-Rpass-analysis=kernel-resource-usage"]
+        # Per-kernel register / LDS / scratch report of the device pass, kept
+        # in _build/<source>.resources.txt (a test checks that no kernel
+        # spills to scratch memory).
+        cmd += ["-Rpass-analysis=kernel-resource-usage"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,8 +53,18 @@ def _compile(src: str, verbose: bool) -> str:
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{msgs}")
-    if msgs.strip() and (verbose or os.environ.get("FG_RESOURCE_USAGE")):
-        print(msgs, flush=True)
+    remarks = [l for l in msgs.splitlines() if "kernel-resource-usage" in l]
+    if src.endswith(".hip"):
+        with open(os.path.join(BUILD, os.path.splitext(src)[0] + ".resources.txt"), "w") as f:
+            f.write("\n".join(remarks) + "\n")
+    # (the remarks come with source excerpts: "  16 | code" and "  | ^")
+    others = "\n".join(l for l in msgs.splitlines()
+                       if "kernel-resource-usage" not in l and not re.match(r"^\s*\d*\s*\|", l))
+    if verbose or os.environ.get("FG_RESOURCE_USAGE"):
+        if msgs.strip():
+            print(msgs, flush=True)
+    elif others.strip():
+        print(others, flush=True)
     return obj
 
 

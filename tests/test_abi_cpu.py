@@ -339,3 +339,19 @@ def test_autotune_candidates():
     assert "mfma_256x256x16_w2x2_s4" not in ragged and "mfma_64x64x16_w2x2_s4_dw" in ragged
     assert "valu_skinny_m8" in names((64, 4096, 4096, "N", "N", None, None, None))
     assert not any(n.startswith("valu_") and "skinny" not in n for n in aligned | ragged)
+
+
+def test_no_kernel_uses_scratch_memory():
+    """Every kernel of the last build keeps its values in registers and LDS:
+    the compiler's resource report (written by the build next to the
+    objects) shows ScratchSize 0 for all of them. A spill of the
+    accumulators once cost the matrix-core kernel its speed."""
+    import re
+    reports = glob.glob(os.path.join(ROOT, "_build", "*.resources.txt"))
+    if not reports:
+        pytest.skip("no build report (build with fp32_gemm_tile_amd/build.py)")
+    sizes = []
+    for path in reports:
+        sizes += [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", open(path).read())]
+    assert len(sizes) >= 100, len(sizes)
+    assert max(sizes) == 0
