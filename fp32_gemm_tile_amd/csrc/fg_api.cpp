@@ -167,6 +167,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // split-K, the partial slices written, read back and reduced at HBM speed.
 constexpr double kSimdFlops = 157.3e12 / (kNumCUs * kSimdsPerCU);  // fp32 MFMA per SIMD
 constexpr double kHbmBytes = 5.0e12;                              // sustained, not peak
+constexpr double kHbmStream = 6.3e12;                             // best streaming rate measured
 constexpr double kLaunch = 3e-6;                                  // one more kernel
 
 int64_t effective_splits(int64_t K, int64_t bk, int64_t splits, int64_t* kt_per_split) {
@@ -200,6 +201,11 @@ double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, boo
         t += wave_flops * (double)share / (eff * kSimdFlops);
         left -= per_cu * kNumCUs;
     }
+    // Every operand byte crosses HBM at least once (what bounds few-row
+    // shapes whatever the tile).
+    const double compulsory =
+        4.0 * ((double)M * K + (double)K * N + (double)M * N * (beta0 ? 1 : 2));
+    t = std::max(t, kLaunch + compulsory / kHbmStream);
     if (s > 1)
         t += ((double)(2 * s + (beta0 ? 1 : 2)) * M * N * 4.0) / kHbmBytes + kLaunch;
     return t;
@@ -213,7 +219,6 @@ double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, boo
 // (0.7 by default, fitted by the tuner) divides both. op(B) crosses HBM at
 // least once. The fixed cost covers the launch and the final reduction.
 constexpr double kSkinnyFixed = 5e-6;
-constexpr double kHbmPeakish = 6.3e12;  // best streaming rate measured (GEMV)
 double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0, double eff) {
     const int64_t rows = M < 8 ? M : 8;
     const double blocks = (double)cdiv(M, 8);
@@ -223,7 +228,7 @@ double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0, double eff) {
     const double t_lat = steps * (0.12e-6 + (double)(rows - 1) * 0.01e-6);
     const double t_thr = per_cu * steps * 0.07e-6;
     const double bytes = 4.0 * ((double)K * N + (double)M * K + (double)M * N * (beta0 ? 1 : 2));
-    return kSkinnyFixed + std::max(std::max(t_lat, t_thr) / eff, bytes / kHbmPeakish);
+    return kSkinnyFixed + std::max(std::max(t_lat, t_thr) / eff, bytes / kHbmStream);
 }
 
 // Best MFMA or few-row entry (and split count, at most max_splits). With

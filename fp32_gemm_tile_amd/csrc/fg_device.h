@@ -39,11 +39,19 @@ __device__ __forceinline__ float ld1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off
 __device__ __forceinline__ void st4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 0);
 }
+// 128-bit store with the non-temporal cache hint (nt): results of a GEMM are
+// written once and not read again by the kernel.
+__device__ __forceinline__ void st4_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 2);
+}
 __device__ __forceinline__ void st1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
 }
 __device__ __forceinline__ f2 ld2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void st2_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 2);
 }
 __device__ __forceinline__ void st2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f2 v) {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 0);
