@@ -15,7 +15,7 @@ row block one of eight GPUs would own, and measures the device's attainable
 MFMA and HBM-read rates with the library's probe kernels.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C5a]
-                       [--suite] [--calibrate] [--splitk [S]] [--cold]
+                       [--suite] [--calibrate] [--splitk [S]] [--streamk] [--cold]
                        [--no-cpu] [--no-probes] [--copy-probe]
 """
 from __future__ import annotations
@@ -69,7 +69,7 @@ def load_traffic(workload, kernel_config):
 
 
 def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock=False,
-             epilogue=None):
+             epilogue=None, streamk=False):
     """Time `steps` calls on the current stream with a HIP event pair around
     each call. Warm (default): the calls run back to back and the mean is the
     whole range over `steps`. Cold: a 512 MiB device write runs before each
@@ -90,6 +90,11 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock
     ws = torch.empty(64 << 20, dtype=torch.float32, device="cuda") if splitk else None
     nsplit = int(splitk) if splitk and not isinstance(splitk, bool) else 0
     flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda") if cold else None
+    sk_ws, sk_bytes = None, 0
+    if streamk:
+        sk_bytes = fg.fg_sgemm_streamk_workspace_size(w.transA, w.transB, w.M, w.N, w.K,
+                                                      dA.data_ptr(), w.LDA, dB.data_ptr(), w.LDB)
+        sk_ws = torch.empty(max(sk_bytes, 16) // 4, dtype=torch.float32, device="cuda")
     epi = None
     if epilogue is not None:
         # every vector present: the most work the fused epilogue can do
@@ -103,6 +108,10 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock
             st = fg.fg_sgemm_splitk(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
                                     w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
                                     nsplit, ws.data_ptr(), ws.numel() * 4, sp)
+        elif streamk:
+            st = fg.fg_sgemm_streamk(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
+                                     w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
+                                     sk_ws.data_ptr(), sk_bytes, sp)
         elif epi is not None:
             st = fg.fg_sgemm_fused(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
                                    w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
@@ -309,10 +318,10 @@ def copy_probe(nbytes=1 << 30, reps=3):
 
 
 def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False, cold=False,
-            sample_clock=False, epilogue=None):
+            sample_clock=False, epilogue=None, streamk=False):
     from fp32_gemm_tile_amd import workloads as wl
-    w = wl.WORKLOADS[name]
-    g = time_gpu(w, steps, warmup, config, splitk, cold, sample_clock, epilogue)
+    w = wl.WORKLOADS[name] if isinstance(name, str) else name
+    g = time_gpu(w, steps, warmup, config, splitk, cold, sample_clock, epilogue, streamk)
     tflops = w.flops / (g["ms_per_launch"] * 1e-3) / 1e12
     gbs = w.compulsory_bytes / (g["ms_per_launch"] * 1e-3) / 1e9
     traffic = load_traffic(name, g["config"])
@@ -381,6 +390,9 @@ def main():
     ap.add_argument("--epilogue", choices=("none", "relu", "gelu", "silu"), default=None,
                     help="time fg_sgemm_fused with row/column scales and biases and this "
                          "activation")
+    ap.add_argument("--streamk", action="store_true",
+                    help="time fg_sgemm_streamk (split tail round; workspace as the library "
+                         "asks)")
     ap.add_argument("--cold", action="store_true",
                     help="write 512 MiB before every timed call (operands out of cache)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -417,17 +429,19 @@ def main():
                         and wl.WORKLOADS[name].M > 2048:
                     continue
                 r = run_one(name, args.steps, args.warmup, False, cid, _splitk_arg(args),
-                            epilogue=args.epilogue)
+                            epilogue=args.epilogue, streamk=args.streamk)
                 print(json.dumps({"workload": name, "config": r["config"]["kernel_config"],
                                   "forced": cid, "splitk": _splitk_arg(args),
-                                  "epilogue": args.epilogue, "tflops": r["value"],
+                                  "epilogue": args.epilogue, "streamk": args.streamk,
+                                  "tflops": r["value"],
                                   "ms": r["ms_per_step"], "pct": r["pct_of_fp32_peak"],
                                   "roofline": r["roofline"]}),
                       flush=True)
         return
 
     r = run_one(args.workload, args.steps, args.warmup, False, args.config, _splitk_arg(args),
-                args.cold, sample_clock=not args.no_probes, epilogue=args.epilogue)
+                args.cold, sample_clock=not args.no_probes, epilogue=args.epilogue,
+                streamk=args.streamk)
     # The 4096^3 shape of the metric, and one GPU's row block of 8192^3 split
     # over eight GPUs, timed in the same run.
     if args.workload == "C5a":

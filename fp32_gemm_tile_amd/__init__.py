@@ -121,6 +121,10 @@ def load_library(path: str = LIB_PATH):
     lib.fg_status_string.restype = ctypes.c_char_p
     lib.fg_abi_version.argtypes = []
     lib.fg_abi_version.restype = i32
+    lib.fg_sgemm_streamk.argtypes = gemm_args[:13] + [vp, ctypes.c_size_t, vp]
+    lib.fg_sgemm_streamk.restype = i32
+    lib.fg_sgemm_streamk_workspace_size.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64]
+    lib.fg_sgemm_streamk_workspace_size.restype = ctypes.c_size_t
     lib.fg_sgemm_fused.argtypes = gemm_args[:13] + [ctypes.POINTER(fg_epilogue), vp, i32]
     lib.fg_sgemm_fused.restype = i32
     lib.fg_estimate_seconds.argtypes = [i64, i64, i64, i32, i32, i32]
@@ -130,6 +134,8 @@ def load_library(path: str = LIB_PATH):
     lib.fg_get_efficiency.restype = i32
     lib.fg_set_efficiency.argtypes = [i32, ctypes.c_double, ctypes.c_double]
     lib.fg_set_efficiency.restype = i32
+    lib.fg_set_streamk_policy.argtypes = [i32]
+    lib.fg_set_streamk_policy.restype = i32
     lib.fg_probe_mfma.argtypes = [i32, i32, vp, vp]
     lib.fg_probe_mfma.restype = i32
     lib.fg_probe_mfma_flops.argtypes = [i32, i32]
@@ -222,6 +228,23 @@ def fg_abi_version() -> int:
     return load_library().fg_abi_version()
 
 
+def fg_sgemm_streamk(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                     workspace, workspace_bytes, stream=0):
+    """Raw call with the stream-K tail (device addresses as ints)."""
+    return load_library().fg_sgemm_streamk(_op(transA), _op(transB), M, N, K, alpha, A, lda,
+                                           B, ldb, beta, C, ldc, workspace or None,
+                                           workspace_bytes, stream or None)
+
+
+def fg_sgemm_streamk_workspace_size(transA, transB, M, N, K, A=0, lda=None, B=0,
+                                    ldb=None) -> int:
+    ta, tb = _op(transA), _op(transB)
+    lda = lda if lda is not None else max(1, M if ta else K)
+    ldb = ldb if ldb is not None else max(1, K if tb else N)
+    return load_library().fg_sgemm_streamk_workspace_size(ta, tb, M, N, K, A or None, lda,
+                                                          B or None, ldb)
+
+
 def fg_sgemm_fused(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                    epilogue=None, stream=0, config=-1):
     """Raw call with a fused epilogue (an fg_epilogue, or None for none)."""
@@ -244,6 +267,11 @@ def fg_get_efficiency(config_id):
 
 def fg_set_efficiency(config_id, eff, eff1) -> int:
     return load_library().fg_set_efficiency(config_id, eff, eff1)
+
+
+def fg_set_streamk_policy(policy) -> int:
+    """0: split the stream-K tail when the model expects a gain; 1: always."""
+    return load_library().fg_set_streamk_policy(policy)
 
 
 def fg_probe_mfma(workgroups, iterations, out, stream=0) -> int:

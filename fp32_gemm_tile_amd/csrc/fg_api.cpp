@@ -179,28 +179,34 @@ int64_t effective_splits(int64_t K, int64_t bk, int64_t splits, int64_t* kt_per_
     return cdiv(kt_total, kps);
 }
 
-double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, bool beta0) {
-    int64_t kps = 0;
-    const int64_t s = effective_splits(K, e.cfg.bk, splits, &kps);
-    const int64_t tiles = cdiv(M, e.cfg.bm) * cdiv(N, e.cfg.bn);
+// Time of `workgroups` workgroups of entry e, each summing kps k-tiles, placed
+// in rounds of resident workgroups: a workgroup's waves share one CU, and a
+// CU holds up to `slots` workgroups (wps waves per SIMD); the last round may
+// leave CUs idle. A SIMD shared by `share` waves finishes them after
+// share * wave_flops at an efficiency that grows from eff1 (one wave: little
+// latency hiding) to eff (wps waves).
+double rounds_time(const Entry& e, int64_t workgroups, int64_t kps) {
     const double wave_flops = 2.0 * e.cfg.wm * e.cfg.wn * (double)kps * e.cfg.bk;
-    // Rounds of resident workgroups: a workgroup's waves share one CU, and a
-    // CU holds up to `slots` workgroups (wps waves per SIMD); the last round
-    // may leave CUs idle. A SIMD shared by `share` waves finishes them after
-    // share * wave_flops at an efficiency that grows from eff1 (one wave:
-    // little latency hiding) to eff (wps waves).
     const int64_t w = e.cfg.threads / 64;
     const int64_t slots = std::max<int64_t>(1, (int64_t)e.wps * kSimdsPerCU / w);
-    double t = kLaunch;
-    for (int64_t left = tiles * s; left > 0;) {
+    const double full = efficiencies()[e.cfg.id].eff.load(std::memory_order_relaxed);
+    const double one = efficiencies()[e.cfg.id].eff1.load(std::memory_order_relaxed);
+    double t = 0.0;
+    for (int64_t left = workgroups; left > 0;) {
         const int64_t per_cu = std::min<int64_t>(cdiv(left, kNumCUs), slots);
         const int64_t share = std::max<int64_t>(1, cdiv(per_cu * w, kSimdsPerCU));
-        const double full = efficiencies()[e.cfg.id].eff.load(std::memory_order_relaxed);
-        const double one = efficiencies()[e.cfg.id].eff1.load(std::memory_order_relaxed);
         const double eff = e.wps > 1 ? one + (full - one) * (double)(share - 1) / (e.wps - 1) : full;
         t += wave_flops * (double)share / (eff * kSimdFlops);
         left -= per_cu * kNumCUs;
     }
+    return t;
+}
+
+double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, bool beta0) {
+    int64_t kps = 0;
+    const int64_t s = effective_splits(K, e.cfg.bk, splits, &kps);
+    const int64_t tiles = cdiv(M, e.cfg.bm) * cdiv(N, e.cfg.bn);
+    double t = kLaunch + rounds_time(e, tiles * s, kps);
     // Every operand byte crosses HBM at least once (what bounds few-row
     // shapes whatever the tile).
     const double compulsory =
@@ -345,6 +351,61 @@ fg_status validate(fg_op ta, fg_op tb, int64_t M, int64_t N, int64_t K, float al
     return FG_OK;
 }
 
+// Stream-K plan for a call: the table entry fg_sgemm would run, its tiles in
+// full rounds of resident workgroups (data-parallel), and the tiles of the
+// last, partial round (the tail), each split along K into `splits` slices so
+// that the tail's tiles x splits workgroups fill one round. Worth it only when
+// the tail round is at most three quarters full; otherwise (and whenever the
+// workspace holds fewer than two slices per tail tile) the plain call runs.
+struct StreamPlan {
+    int idx = -1;           // table entry (after the alignment fallback)
+    int64_t tiles = 0, full = 0, tail = 0, splits = 1, kps = 0;
+    size_t ws_bytes = 0;    // workspace the tail needs
+};
+
+// fg_set_streamk_policy: 0 = split the tail when the model expects a gain,
+// 1 = whenever the tail round is at most three quarters full.
+std::atomic<int> g_streamk_policy{0};
+
+bool plan_streamk(int64_t M, int64_t N, int64_t K, bool ab_aligned, bool beta0, size_t ws_avail,
+                  StreamPlan* out) {
+    int64_t sp = 1;
+    int idx = select_entry(M, N, K, ab_aligned, 1, beta0, &sp);
+    if (idx < 0) return false;
+    if (table()[idx].fallback >= 0 && !ab_aligned) idx = table()[idx].fallback;
+    const Entry& e = table()[idx];
+    out->idx = idx;
+    if (e.cfg.kind != FG_KIND_MFMA || K <= 0) return false;
+    const int64_t waves = e.cfg.threads / 64;
+    const int64_t slots = std::max<int64_t>(1, (int64_t)e.wps * kSimdsPerCU / waves);
+    const int64_t round = (int64_t)kNumCUs * slots;
+    const int64_t tiles = cdiv(M, e.cfg.bm) * cdiv(N, e.cfg.bn);
+    const int64_t full = tiles / round * round, tail = tiles - full;
+    if (tail == 0 || 4 * tail > 3 * round) return false;
+    const int64_t slot_bytes = (int64_t)e.cfg.bm * e.cfg.bn * 4;
+    int64_t want = round / tail;
+    const int64_t fit = (int64_t)std::min<size_t>(ws_avail / (size_t)(tail * slot_bytes),
+                                                  (size_t)1 << 30);
+    if (want > fit) want = fit;
+    int64_t kps = 0;
+    const int64_t splits = effective_splits(K, e.cfg.bk, want, &kps);
+    if (splits < 2) return false;
+    // Only when the model expects a gain: full rounds + the split tail + the
+    // slot traffic of the reduction against the plain call.
+    const int64_t kt_total = cdiv(K, e.cfg.bk);
+    const double t_split = 3 * kLaunch + rounds_time(e, full, kt_total) +
+                           rounds_time(e, tail * splits, kps) +
+                           (double)tail * (splits + (beta0 ? 1 : 2)) * slot_bytes / kHbmBytes;
+    if (g_streamk_policy.load() == 0 && t_split > 0.97 * cost(e, M, N, K, 1, beta0)) return false;
+    out->tiles = tiles;
+    out->full = full;
+    out->tail = tail;
+    out->splits = splits;
+    out->kps = kps;
+    out->ws_bytes = (size_t)(tail * splits * slot_bytes);
+    return true;
+}
+
 int32_t build_flags(const float* A, int64_t lda, const float* B, int64_t ldb, const float* C,
                     int64_t ldc, float beta) {
     int32_t f = fg::FLAG_XCD_REMAP;
@@ -410,7 +471,7 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
                    const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
                    float* C, int64_t ldc, hipStream_t stream, int32_t config_id,
                    int64_t splits, float* ws, size_t ws_bytes,
-                   const fg_epilogue* epi = nullptr, int config_arg = 15) {
+                   const fg_epilogue* epi = nullptr, int config_arg = 15, bool streamk = false) {
     clear_error();
     fg_status s = validate(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
     if (s != FG_OK) return s;
@@ -462,6 +523,47 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
     }
 
     const bool ab_aligned = (p.flags & fg::FLAG_VEC_A) && (p.flags & fg::FLAG_VEC_B);
+
+    StreamPlan plan;
+    if (streamk && plan_streamk(M, N, K, ab_aligned, beta == 0.0f, ws ? ws_bytes : 0, &plan)) {
+        // Full rounds data-parallel into C, the tail's (tile, split) partials
+        // into their workspace slots, then the fixed-order tail reduction.
+        const Entry& en = table()[plan.idx];
+        s = check_device();
+        if (s != FG_OK) return s;
+        p.tiles_m = (int32_t)cdiv(M, en.cfg.bm);
+        p.tiles_n = (int32_t)cdiv(N, en.cfg.bn);
+        p.group_m = group_m_override() > 0 ? group_m_override() : 4;
+        if (p.group_m > p.tiles_m) p.group_m = p.tiles_m;
+        hipError_t e = hipSuccess;
+        if (plan.full > 0) {
+            fg::GemmParams d = p;
+            d.kt_per_split = (int32_t)cdiv(K, en.cfg.bk);  // tile ids [0, full), all of K
+            e = fg::launch_mfma_tiles(en.variant, transA, transB, d, (int32_t)plan.full, 1,
+                                      stream);
+        }
+        if (e == hipSuccess) {
+            fg::GemmParams q = p;
+            q.C = ws;
+            q.ldc = en.cfg.bn;
+            q.c_extent = (int64_t)(plan.ws_bytes / sizeof(float));
+            q.alpha = 1.0f;
+            q.beta = 0.0f;
+            q.flags = build_flags(A, lda, B, ldb, ws, en.cfg.bn, 0.0f) | fg::FLAG_TILE_WS;
+            q.tile_base = (int32_t)plan.full;
+            q.kt_per_split = (int32_t)plan.kps;
+            e = fg::launch_mfma_tiles(en.variant, transA, transB, q, (int32_t)plan.tail,
+                                      (int32_t)plan.splits, stream);
+        }
+        if (e == hipSuccess) {
+            fg::GemmParams r = p;
+            r.tile_base = (int32_t)plan.full;
+            e = fg::launch_tile_reduce(ws, (int32_t)plan.splits, (int32_t)plan.tail, en.cfg.bm,
+                                       en.cfg.bn, r, stream);
+        }
+        if (e != hipSuccess) return fail(FG_ERR_HIP, 0, "kernel launch: %s", hipGetErrorString(e));
+        return FG_OK;
+    }
     const int64_t slice = M * N;  // floats per split-K partial
     // One slice needs no workspace, so at least one is always possible.
     int64_t max_splits = ws ? (int64_t)(ws_bytes / (sizeof(float) * (size_t)slice)) : 1;
@@ -559,6 +661,32 @@ fg_status fg_sgemm_splitk(fg_op transA, fg_op transB, int64_t M, int64_t N, int6
                     splits, (float*)workspace, workspace ? workspace_bytes : 0);
 }
 
+size_t fg_sgemm_streamk_workspace_size(fg_op transA, fg_op transB, int64_t M, int64_t N,
+                                       int64_t K, const float* A, int64_t lda, const float* B,
+                                       int64_t ldb) {
+    if (validate(transA, transB, M, N, K, 1.0f, A, lda, B, ldb, nullptr, std::max<int64_t>(1, N),
+                 false) != FG_OK)
+        return 0;
+    if (M == 0 || N == 0 || K == 0) return 0;
+    const int32_t f = build_flags(A, lda, B, ldb, nullptr, N, 0.0f);
+    const bool ab_aligned = (f & fg::FLAG_VEC_A) && (f & fg::FLAG_VEC_B);
+    StreamPlan plan;
+    // beta does not change the plan (only the cost of the plain choice)
+    if (!plan_streamk(M, N, K, ab_aligned, true, (size_t)-1, &plan)) return 0;
+    return plan.ws_bytes;
+}
+
+fg_status fg_sgemm_streamk(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                           float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                           float beta, float* C, int64_t ldc, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    clear_error();
+    if (workspace && ((uintptr_t)workspace & 15u))
+        return fail(FG_ERR_INVALID_ARG, 14, "workspace is not 16-byte aligned");
+    return run_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1, 1,
+                    (float*)workspace, workspace ? workspace_bytes : 0, nullptr, 15, true);
+}
+
 fg_status fg_sgemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, float alpha,
                    const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
                    float* C, int64_t ldc, hipStream_t stream) {
@@ -606,6 +734,13 @@ fg_status fg_set_efficiency(int32_t config_id, double eff, double eff1) {
     if (!(eff1 > 0.0 && eff1 <= 1.0)) return fail(FG_ERR_INVALID_ARG, 3, "eff1 outside (0, 1]");
     efficiencies()[config_id].eff.store(eff);
     efficiencies()[config_id].eff1.store(eff1);
+    return FG_OK;
+}
+
+fg_status fg_set_streamk_policy(int32_t policy) {
+    clear_error();
+    if (policy != 0 && policy != 1) return fail(FG_ERR_INVALID_ARG, 1, "policy must be 0 or 1");
+    g_streamk_policy.store(policy);
     return FG_OK;
 }
 

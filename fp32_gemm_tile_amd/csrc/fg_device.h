@@ -158,21 +158,11 @@ __device__ __forceinline__ float epilogue_value(const GemmParams& p, float acc, 
     return o;
 }
 
-// Workgroup id -> (tile_m, tile_n).
-//
-// 1. XCD remap: consecutive workgroup ids are handed to the 8 XCDs in turn,
-//    and each XCD has its own L2. Renumbering so that XCD x receives the
-//    contiguous range [x*G/8, (x+1)*G/8) makes the tiles that run together on
-//    one XCD neighbours in the order below, so they share operand panels in
-//    that XCD's L2.
-// 2. Grouped raster order: tiles are visited in bands of `group_m` tile rows,
-//    column by column inside a band, so that a run of consecutive ids covers
-//    a compact block of C (few distinct A row-panels and B column-panels).
-__device__ __forceinline__ void map_tile(int bid, int nblocks, const GemmParams& p,
-                                         int& tm, int& tn) {
-    int L = bid;
-    if ((p.flags & FLAG_XCD_REMAP) && (nblocks % 8) == 0)
-        L = (bid % 8) * (nblocks / 8) + bid / 8;
+// Tile id -> (tile_m, tile_n) in grouped raster order: tiles are visited in
+// bands of `group_m` tile rows, column by column inside a band, so that a run
+// of consecutive ids covers a compact block of C (few distinct A row-panels
+// and B column-panels).
+__device__ __forceinline__ void tile_coords(int L, const GemmParams& p, int& tm, int& tn) {
     const int per_group = p.group_m * p.tiles_n;
     const int g = L / per_group;
     const int first_m = g * p.group_m;
@@ -181,6 +171,23 @@ __device__ __forceinline__ void map_tile(int bid, int nblocks, const GemmParams&
     const int r = L - g * per_group;
     tm = first_m + r % gm;
     tn = r / gm;
+}
+
+// Workgroup id -> tile id (returned) and (tile_m, tile_n).
+//
+// XCD remap: consecutive workgroup ids are handed to the 8 XCDs in turn, and
+// each XCD has its own L2. Renumbering so that XCD x receives the contiguous
+// range [x*G/8, (x+1)*G/8) makes the tiles that run together on one XCD
+// neighbours in the raster order, so they share operand panels in that XCD's
+// L2. A launch covers tile ids [p.tile_base, p.tile_base + nblocks).
+__device__ __forceinline__ int map_tile(int bid, int nblocks, const GemmParams& p, int& tm,
+                                        int& tn) {
+    int L = bid;
+    if ((p.flags & FLAG_XCD_REMAP) && (nblocks % 8) == 0)
+        L = (bid % 8) * (nblocks / 8) + bid / 8;
+    L += p.tile_base;
+    tile_coords(L, p, tm, tn);
+    return L;
 }
 
 }  // namespace fg

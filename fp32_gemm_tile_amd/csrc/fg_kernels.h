@@ -28,6 +28,8 @@ struct GemmParams {
     // c_split_stride is 0.
     int32_t kt_per_split;
     int64_t c_split_stride;
+    // First tile id of the launch (grouped raster order); 0 for a whole GEMM.
+    int32_t tile_base;
     // Fused epilogue (FLAG_EPI): C = act(alpha * r_i * c_j * acc + beta * C
     // + u_i + w_j). A null vector means ones (scales) or zeros (biases).
     const float* row_scale;  // r, M floats
@@ -47,6 +49,9 @@ enum : int32_t {
     FLAG_XCD_REMAP = 16,  // remap workgroup ids so each XCD gets a contiguous tile range
     FLAG_VEC2_C = 32,  // C rows start 8-byte aligned: 64-bit loads/stores
     FLAG_EPI = 64,     // apply the fused epilogue (scales, biases, activation)
+    FLAG_TILE_WS = 128,  // write each (tile, split) partial to its own dense
+                         // BM x BN slot of C (ldc = BN): slot
+                         // (tile id - tile_base) * splits + split
 };
 
 // Launchers: enqueue one kernel on `stream`; return the HIP launch status.
@@ -54,6 +59,10 @@ enum : int32_t {
 // fg_api.cpp); trans_a / trans_b select the operand layouts.
 hipError_t launch_mfma(int variant, int trans_a, int trans_b, const GemmParams& p,
                        hipStream_t stream);
+// The same on an explicit grid: `tiles` workgroups along x (tile ids
+// p.tile_base ..), `splits` along y (k ranges of p.kt_per_split k-tiles).
+hipError_t launch_mfma_tiles(int variant, int trans_a, int trans_b, const GemmParams& p,
+                             int32_t tiles, int32_t splits, hipStream_t stream);
 hipError_t launch_valu(int variant, int trans_a, int trans_b, const GemmParams& p,
                        hipStream_t stream);
 // Few-row GEMM (memory-bound): blocks of up to 8 rows of C, op(B) streamed
@@ -67,6 +76,11 @@ hipError_t launch_scale(const GemmParams& p, hipStream_t stream);
 // FLAG_EPI the fused epilogue is applied to that sum.
 hipError_t launch_splitk_reduce(const float* W, int32_t splits, const GemmParams& p,
                                 hipStream_t stream);
+// Stream-K tail reduction: for tiles [p.tile_base, p.tile_base + count) of a
+// bm x bn tiling, C = epilogue(sum_{s < splits} slot(tile, s)) with the slots
+// written by an FLAG_TILE_WS launch (summed in ascending s).
+hipError_t launch_tile_reduce(const float* W, int32_t splits, int32_t count, int32_t bm,
+                              int32_t bn, const GemmParams& p, hipStream_t stream);
 // Machine probes (fg_probe.hip): an MFMA-only loop and a streaming read.
 hipError_t launch_probe_mfma(int workgroups, int iters, float* out, hipStream_t stream);
 hipError_t launch_probe_read(const float* x, int64_t n4, int workgroups, float* out,

@@ -287,7 +287,7 @@ sgemm_mfma_kernel(GemmParams p) {
     float* sB = sA + NS * OpA::kStage;
 
     int tm, tn;
-    map_tile(blockIdx.x, gridDim.x, p, tm, tn);
+    const int tile_id = map_tile(blockIdx.x, gridDim.x, p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep in SGPRs
@@ -475,9 +475,15 @@ sgemm_mfma_kernel(GemmParams p) {
     // earlier values live across the main loop cost a register spill.
     const int elane = (int)__lane_id();
     const int eli = elane & 31, elh = elane >> 5;
-    const int64_t c_org = (int64_t)m0 * p.ldc + n0;
-    float* const Cs = p.C + (int64_t)blockIdx.y * p.c_split_stride;  // this split's C
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cs + c_org, p.c_extent - c_org);
+    // C, this split's slice of C, or (FLAG_TILE_WS) this tile's and split's
+    // own BM x BN slot, addressed tile-locally with ldc = BN.
+    const bool tile_ws = p.flags & FLAG_TILE_WS;
+    const int64_t c_org = tile_ws ? 0 : (int64_t)m0 * p.ldc + n0;
+    float* const Cs =
+        tile_ws ? p.C + ((int64_t)(tile_id - p.tile_base) * gridDim.y + blockIdx.y) * (BM * BN)
+                : p.C + (int64_t)blockIdx.y * p.c_split_stride;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(Cs + c_org, tile_ws ? (int64_t)BM * BN : p.c_extent - c_org);
     const bool beta0 = p.flags & FLAG_BETA0;
     // A lane's NB columns are one 128-bit (NB = 4) or 64-bit (NB = 2) access
     // when C's rows are aligned for it and all NB columns are inside N.
@@ -619,9 +625,13 @@ sgemm_mfma_kernel(GemmParams p) {
     (void)mn_interior;
 }
 
+// Grid: x = tiles (all of them unless given), y = split-K slices.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int DMAB = 16, int OCC = 1>
-hipError_t launch_shape(int ta, int tb, const GemmParams& p, hipStream_t s) {
-    const dim3 grid(p.tiles_m * p.tiles_n, (p.K + kBK * p.kt_per_split - 1) / (kBK * p.kt_per_split)),
+hipError_t launch_shape(int ta, int tb, const GemmParams& p, hipStream_t s, int32_t tiles = -1,
+                        int32_t splits = -1) {
+    const dim3 grid(tiles >= 0 ? tiles : p.tiles_m * p.tiles_n,
+                    splits >= 0 ? splits
+                                : (p.K + kBK * p.kt_per_split - 1) / (kBK * p.kt_per_split)),
         block(64 * WAVES_M * WAVES_N);
     if (ta == 0 && tb == 0)
         hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 0, STAGES, DMAB, OCC>), grid, block, 0, s, p);
@@ -655,21 +665,26 @@ hipError_t launch_shape(int ta, int tb, const GemmParams& p, hipStream_t s) {
 //  12: as 11 with 4-byte direct-to-LDS loads
 //  13: 128 x  64, 2 x 2 waves of  64 x  32, 4-stage direct-to-LDS ring
 hipError_t launch_mfma(int variant, int ta, int tb, const GemmParams& p, hipStream_t s) {
+    return launch_mfma_tiles(variant, ta, tb, p, -1, -1, s);
+}
+
+hipError_t launch_mfma_tiles(int variant, int ta, int tb, const GemmParams& p, int32_t tiles,
+                             int32_t splits, hipStream_t s) {
     switch (variant) {
-        case 0: return launch_shape<256, 256, 2, 2, 2>(ta, tb, p, s);
-        case 1: return launch_shape<256, 128, 2, 1, 2>(ta, tb, p, s);
-        case 2: return launch_shape<128, 128, 1, 1, 2>(ta, tb, p, s);
-        case 3: return launch_shape<64, 128, 1, 1, 2>(ta, tb, p, s);
-        case 4: return launch_shape<32, 128, 1, 1, 2>(ta, tb, p, s);
-        case 5: return launch_shape<256, 256, 2, 2, 4>(ta, tb, p, s);
-        case 6: return launch_shape<256, 128, 2, 1, 3>(ta, tb, p, s);
-        case 7: return launch_shape<128, 128, 2, 2, 4>(ta, tb, p, s);
-        case 8: return launch_shape<128, 128, 2, 2, 4, 4>(ta, tb, p, s);
-        case 9: return launch_shape<256, 256, 4, 2, 4>(ta, tb, p, s);
-        case 10: return launch_shape<256, 128, 2, 2, 3, 16, 2>(ta, tb, p, s);
-        case 11: return launch_shape<64, 64, 2, 2, 4, 16, 2>(ta, tb, p, s);
-        case 12: return launch_shape<64, 64, 2, 2, 4, 4, 2>(ta, tb, p, s);
-        case 13: return launch_shape<128, 64, 2, 2, 4, 16, 2>(ta, tb, p, s);
+        case 0: return launch_shape<256, 256, 2, 2, 2>(ta, tb, p, s, tiles, splits);
+        case 1: return launch_shape<256, 128, 2, 1, 2>(ta, tb, p, s, tiles, splits);
+        case 2: return launch_shape<128, 128, 1, 1, 2>(ta, tb, p, s, tiles, splits);
+        case 3: return launch_shape<64, 128, 1, 1, 2>(ta, tb, p, s, tiles, splits);
+        case 4: return launch_shape<32, 128, 1, 1, 2>(ta, tb, p, s, tiles, splits);
+        case 5: return launch_shape<256, 256, 2, 2, 4>(ta, tb, p, s, tiles, splits);
+        case 6: return launch_shape<256, 128, 2, 1, 3>(ta, tb, p, s, tiles, splits);
+        case 7: return launch_shape<128, 128, 2, 2, 4>(ta, tb, p, s, tiles, splits);
+        case 8: return launch_shape<128, 128, 2, 2, 4, 4>(ta, tb, p, s, tiles, splits);
+        case 9: return launch_shape<256, 256, 4, 2, 4>(ta, tb, p, s, tiles, splits);
+        case 10: return launch_shape<256, 128, 2, 2, 3, 16, 2>(ta, tb, p, s, tiles, splits);
+        case 11: return launch_shape<64, 64, 2, 2, 4, 16, 2>(ta, tb, p, s, tiles, splits);
+        case 12: return launch_shape<64, 64, 2, 2, 4, 4, 2>(ta, tb, p, s, tiles, splits);
+        case 13: return launch_shape<128, 64, 2, 2, 4, 16, 2>(ta, tb, p, s, tiles, splits);
         default: return hipErrorInvalidValue;
     }
 }

@@ -199,6 +199,46 @@ fg_status fg_sgemm_fused(fg_op transA, fg_op transB, int64_t M, int64_t N, int64
                          float* C, int64_t ldc, const fg_epilogue* epilogue,
                          hipStream_t stream, int32_t config_id);
 
+/*
+ * fg_sgemm_streamk: fg_sgemm with stream-K style scheduling of the last,
+ * partial round of output tiles ("Matmul II: register blocking, warp tiling,
+ * tensor cores", section 8: split-K when the tiles cannot fill the machine,
+ * here only for the tiles that would otherwise run in a round of their own).
+ *
+ * The table entry is the one fg_sgemm would use. Its tiles that fill whole
+ * rounds of resident workgroups run as usual; the remaining tiles (when they
+ * would fill at most three quarters of a round, and the cost model expects
+ * the split to gain at least 3%; see fg_set_streamk_policy in
+ * fp32gemm_tune.h) are each split along K into
+ * S slices, S chosen so that tiles x S fill one round, the partial sums go to
+ * per-(tile, slice) slots of `workspace`, and a last kernel adds each tile's
+ * slices in ascending order (repeated calls give identical bits) and applies
+ * alpha and beta. Otherwise, or when the workspace holds fewer than two
+ * slices per tail tile, it runs exactly as fg_sgemm.
+ *
+ * Arguments 1-13 as for fg_sgemm, then:
+ *   14 workspace       : device memory owned by the caller, 16-byte aligned,
+ *                        or NULL (then no split); must not overlap A, B or C
+ *                        or be used by a call that may run at the same time
+ *   15 workspace_bytes : its size; fg_sgemm_streamk_workspace_size gives what
+ *                        the full plan needs (less is never an error: fewer
+ *                        slices, or none)
+ *   16 stream
+ */
+fg_status fg_sgemm_streamk(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                           float alpha, const float* A, int64_t lda,
+                           const float* B, int64_t ldb, float beta,
+                           float* C, int64_t ldc, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Workspace bytes fg_sgemm_streamk would use for this call (the plan
+ * depends on the shape and on the 16-byte alignment of A, B, lda and ldb;
+ * pointers are inspected, never dereferenced). 0 when no tail is split or
+ * the arguments are invalid. Host only. */
+size_t fg_sgemm_streamk_workspace_size(fg_op transA, fg_op transB, int64_t M, int64_t N,
+                                       int64_t K, const float* A, int64_t lda,
+                                       const float* B, int64_t ldb);
+
 /* Bytes of workspace fg_sgemm_splitk needs for `splits` slices of an M x N
  * result (0 when splits <= 1 or the result is empty). Host only. */
 size_t fg_sgemm_splitk_workspace_size(int64_t M, int64_t N, int32_t splits);

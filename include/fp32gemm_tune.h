@@ -48,6 +48,15 @@ fg_status fg_get_efficiency(int32_t config_id, double* eff, double* eff1);
  */
 fg_status fg_set_efficiency(int32_t config_id, double eff, double eff1);
 
+/*
+ * When fg_sgemm_streamk splits the last, partial round of tiles: policy 0
+ * (the default) only when the cost model expects it to beat the plain call
+ * by at least 3%; policy 1 whenever that round is at most three quarters
+ * full (for tests and measurements). Process-wide. FG_ERR_INVALID_ARG for
+ * any other value.
+ */
+fg_status fg_set_streamk_policy(int32_t policy);
+
 #ifdef __cplusplus
 }
 #endif

@@ -355,3 +355,25 @@ def test_no_kernel_uses_scratch_memory():
         sizes += [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", open(path).read())]
     assert len(sizes) >= 100, len(sizes)
     assert max(sizes) == 0
+
+
+def test_streamk_plan_and_validation():
+    """Host side of fg_sgemm_streamk: the plan's workspace, the policy switch,
+    argument checks (no GPU needed)."""
+    try:
+        assert fg.fg_set_streamk_policy(1) == fg.FG_OK
+        need = fg.fg_sgemm_streamk_workspace_size("N", "N", 1000, 1000, 500)
+        assert need > 0 and need % (64 * 64 * 4) == 0
+        assert fg.fg_sgemm_streamk_workspace_size("N", "N", 8192, 8192, 8192) == 0  # no tail
+        assert fg.fg_sgemm_streamk_workspace_size("N", "N", 4, 4, 0) == 0
+        assert fg.fg_sgemm_streamk_workspace_size("N", "N", 4, 4, 4, lda=1) == 0    # invalid
+        assert fg.fg_set_streamk_policy(0) == fg.FG_OK
+        assert fg.fg_sgemm_streamk_workspace_size("N", "N", 1000, 1000, 500) <= need
+        assert fg.fg_set_streamk_policy(2) == fg.FG_ERR_INVALID_ARG
+    finally:
+        fg.fg_set_streamk_policy(0)
+    st = fg.fg_sgemm_streamk(0, 0, 64, 64, 64, 1.0, 16, 64, 16, 64, 0.0, 16, 64, 4100, 1 << 20, 0)
+    assert st == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 14
+    st = fg.fg_sgemm_streamk(0, 0, 64, 64, 64, 1.0, 16, 63, 16, 64, 0.0, 16, 64, 0, 0, 0)
+    assert st == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 8
+    assert fg.fg_sgemm_streamk(0, 0, 0, 64, 64, 1.0, 16, 64, 16, 64, 0.0, 16, 64, 0, 0, 0) == 0
