@@ -123,10 +123,13 @@ const Entry* table() {
         make_entry(14, FG_KIND_MFMA, 11, 64, 64, 16, 32, 32, 256, 4, 5, 0.75, "mfma_64x64x16_w2x2_s4", 15, 0.57),
         make_entry(15, FG_KIND_MFMA, 12, 64, 64, 16, 32, 32, 256, 4, 5, 0.72, "mfma_64x64x16_w2x2_s4_dw", -1, 0.55),
         make_entry(16, FG_KIND_MFMA, 13, 128, 64, 16, 64, 32, 256, 4, 3, 0.80, "mfma_128x64x16_w2x2_s4", 15, 0.74),
+        // Eight waves per workgroup: two per SIMD even when the grid has only
+        // one workgroup per CU.
+        make_entry(17, FG_KIND_MFMA, 14, 128, 128, 16, 32, 64, 512, 4, 4, 0.85, "mfma_128x128x16_w4x2_s4", 10, 0.80),
     };
     return t;
 }
-constexpr int kNumEntries = 17;
+constexpr int kNumEntries = 18;
 
 // Cost-model efficiencies, one pair per entry: from the generated table
 // (fg_tuned.inc) over the defaults above, and replaceable at run time by a

@@ -664,6 +664,8 @@ hipError_t launch_shape(int ta, int tb, const GemmParams& p, hipStream_t s, int3
 //      (several workgroups per CU: grids too small for the large tiles)
 //  12: as 11 with 4-byte direct-to-LDS loads
 //  13: 128 x  64, 2 x 2 waves of  64 x  32, 4-stage direct-to-LDS ring
+//  14: 128 x 128, 4 x 2 waves of  32 x  64, 4-stage direct-to-LDS ring
+//      (two waves per SIMD from one workgroup per CU)
 hipError_t launch_mfma(int variant, int ta, int tb, const GemmParams& p, hipStream_t s) {
     return launch_mfma_tiles(variant, ta, tb, p, -1, -1, s);
 }
@@ -685,6 +687,7 @@ hipError_t launch_mfma_tiles(int variant, int ta, int tb, const GemmParams& p, i
         case 11: return launch_shape<64, 64, 2, 2, 4, 16, 2>(ta, tb, p, s, tiles, splits);
         case 12: return launch_shape<64, 64, 2, 2, 4, 4, 2>(ta, tb, p, s, tiles, splits);
         case 13: return launch_shape<128, 64, 2, 2, 4, 16, 2>(ta, tb, p, s, tiles, splits);
+        case 14: return launch_shape<128, 128, 4, 2, 4, 16, 2>(ta, tb, p, s, tiles, splits);
         default: return hipErrorInvalidValue;
     }
 }

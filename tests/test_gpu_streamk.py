@@ -106,8 +106,14 @@ def test_streamk_no_tail_is_plain():
 
 
 def test_streamk_large_sampled():
-    """6144^3 (the 128 x 128 entry leaves half a round: its tail is split)."""
-    w = wl.custom(6144, 6144, 6144, seed=79)
+    """A large shape whose plan has a split tail (the first of a few
+    candidates that has one with the current table), checked on a sample."""
+    cands = [(4096, 5120, 4096), (4352, 4608, 4096), (4096, 6144, 4096), (4608, 4608, 4096),
+             (5120, 5120, 4096), (6144, 6144, 6144)]
+    shape = next((c for c in cands if fg.fg_sgemm_streamk_workspace_size("N", "N", *c) > 0), None)
+    assert shape is not None, "no candidate has a split tail"
+    log(f"  large stream-K shape {shape}")
+    w = wl.custom(*shape, seed=79)
     A, B, _ = wl.make_inputs(w)
     out, need = run_streamk(w, A, B)
     assert need > 0
