@@ -69,7 +69,7 @@ def load_traffic(workload, kernel_config):
 
 
 def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock=False,
-             epilogue=None, streamk=False):
+             epilogue=None, streamk=False, min_warm_s=0.0):
     """Time `steps` calls on the current stream with a HIP event pair around
     each call. Warm (default): the calls run back to back and the mean is the
     whole range over `steps`. Cold: a 512 MiB device write runs before each
@@ -126,6 +126,14 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # Tables of many short runs (--suite, --calibrate) keep calling until
+    # min_warm_s has passed: after the host-side set-up between runs the GPU
+    # idles, and a few short calls do not bring its clock back up.
+    t_warm = time.perf_counter()
+    while min_warm_s > 0 and time.perf_counter() - t_warm < min_warm_s:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
     # Per-call event pairs (for the median and the minimum). Their records sit
     # between the calls, so the warm mean comes from a second pass with one
     # event pair around all `steps` calls.
@@ -318,10 +326,11 @@ def copy_probe(nbytes=1 << 30, reps=3):
 
 
 def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False, cold=False,
-            sample_clock=False, epilogue=None, streamk=False):
+            sample_clock=False, epilogue=None, streamk=False, min_warm_s=0.0):
     from fp32_gemm_tile_amd import workloads as wl
     w = wl.WORKLOADS[name] if isinstance(name, str) else name
-    g = time_gpu(w, steps, warmup, config, splitk, cold, sample_clock, epilogue, streamk)
+    g = time_gpu(w, steps, warmup, config, splitk, cold, sample_clock, epilogue, streamk,
+                 min_warm_s)
     tflops = w.flops / (g["ms_per_launch"] * 1e-3) / 1e12
     gbs = w.compulsory_bytes / (g["ms_per_launch"] * 1e-3) / 1e9
     traffic = load_traffic(name, g["config"])
@@ -429,7 +438,7 @@ def main():
                         and wl.WORKLOADS[name].M > 2048:
                     continue
                 r = run_one(name, args.steps, args.warmup, False, cid, _splitk_arg(args),
-                            epilogue=args.epilogue, streamk=args.streamk)
+                            epilogue=args.epilogue, streamk=args.streamk, min_warm_s=0.2)
                 print(json.dumps({"workload": name, "config": r["config"]["kernel_config"],
                                   "forced": cid, "splitk": _splitk_arg(args),
                                   "epilogue": args.epilogue, "streamk": args.streamk,

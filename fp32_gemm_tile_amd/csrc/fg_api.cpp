@@ -205,11 +205,30 @@ double rounds_time(const Entry& e, int64_t workgroups, int64_t kps) {
     return t;
 }
 
+// Time the workgroups' C tiles take to leave the CUs: every round ends with
+// each CU writing its tiles (BM x BN floats each). Unless several workgroups
+// share each SIMD, the SIMDs of a storing workgroup idle meanwhile; when they
+// do, one workgroup's stores overlap another's main loop (counted at a
+// quarter).
+constexpr double kHbmWrite = 6.4e12;  // C stores with the non-temporal hint
+double store_time(const Entry& e, int64_t workgroups) {
+    const int64_t w = e.cfg.threads / 64;
+    const int64_t slots = std::max<int64_t>(1, (int64_t)e.wps * kSimdsPerCU / w);
+    const double tile_bytes = 4.0 * e.cfg.bm * e.cfg.bn;
+    const int64_t per_simd = slots * std::min<int64_t>(w, kSimdsPerCU) / kSimdsPerCU;
+    const double exposed = per_simd > 1 ? 0.25 : 1.0;
+    double t = 0.0;
+    for (int64_t left = workgroups; left > 0; left -= (int64_t)kNumCUs * slots)
+        t += exposed * (double)std::min<int64_t>(left, (int64_t)kNumCUs * slots) * tile_bytes /
+             kHbmWrite;
+    return t;
+}
+
 double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, bool beta0) {
     int64_t kps = 0;
     const int64_t s = effective_splits(K, e.cfg.bk, splits, &kps);
     const int64_t tiles = cdiv(M, e.cfg.bm) * cdiv(N, e.cfg.bn);
-    double t = kLaunch + rounds_time(e, tiles * s, kps);
+    double t = kLaunch + rounds_time(e, tiles * s, kps) + store_time(e, tiles * s);
     // Every operand byte crosses HBM at least once (what bounds few-row
     // shapes whatever the tile).
     const double compulsory =
@@ -242,6 +261,11 @@ double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0, double eff) {
 
 // Best MFMA or few-row entry (and split count, at most max_splits). With
 // mfma_only (the caller asked for a split), only the MFMA kernels compete.
+// A later candidate must beat the best so far by 2%: estimates that close
+// are within the model's error (the tuner fits efficiencies in steps of
+// 0.01, about 1%), and the earlier table entry stays the pick, so refitted
+// efficiencies do not flip the choice between equivalent kernels.
+constexpr double kPickMargin = 0.98;
 int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_splits,
                  bool beta0, int64_t* best_splits, bool mfma_only = false) {
     static const int64_t kSplits[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
@@ -253,7 +277,7 @@ int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_s
         if (e.cfg.kind == FG_KIND_SKINNY) {
             if (mfma_only) continue;
             const double c = skinny_cost(M, N, K, beta0, efficiencies()[i].eff.load());
-            if (best < 0 || c < best_cost) {
+            if (best < 0 || c < kPickMargin * best_cost) {
                 best = i;
                 best_cost = c;
                 *best_splits = 1;
@@ -265,7 +289,7 @@ int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_s
         for (int64_t sp : kSplits) {
             if (sp > max_splits) break;
             const double c = cost(e, M, N, K, sp, beta0);
-            if (best < 0 || c < best_cost) {
+            if (best < 0 || c < kPickMargin * best_cost) {
                 best = i;
                 best_cost = c;
                 *best_splits = sp;
@@ -396,8 +420,8 @@ bool plan_streamk(int64_t M, int64_t N, int64_t K, bool ab_aligned, bool beta0, 
     // Only when the model expects a gain: full rounds + the split tail + the
     // slot traffic of the reduction against the plain call.
     const int64_t kt_total = cdiv(K, e.cfg.bk);
-    const double t_split = 3 * kLaunch + rounds_time(e, full, kt_total) +
-                           rounds_time(e, tail * splits, kps) +
+    const double t_split = 3 * kLaunch + rounds_time(e, full, kt_total) + store_time(e, full) +
+                           rounds_time(e, tail * splits, kps) + store_time(e, tail * splits) +
                            (double)tail * (splits + (beta0 ? 1 : 2)) * slot_bytes / kHbmBytes;
     if (g_streamk_policy.load() == 0 && t_split > 0.97 * cost(e, M, N, K, 1, beta0)) return false;
     out->tiles = tiles;

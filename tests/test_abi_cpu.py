@@ -286,13 +286,14 @@ def test_tuning_hooks():
         got = fg.fg_get_efficiency(int(i))
         assert abs(got[0] - float(e)) < 1e-12 and abs(got[1] - float(e1)) < 1e-12
     t0 = fg.fg_estimate_seconds(8192, 8192, 8192, 7)
-    # 2*8192^3 FLOP at the tuned efficiency, plus one launch
+    # 2*8192^3 FLOP at the tuned efficiency, plus one launch and the tile
+    # stores of four rounds (under 1% here)
     eff = fg.fg_get_efficiency(7)[0]
-    assert abs(t0 - (2 * 8192 ** 3 / (eff * 157.3e12) + 3e-6)) < 1e-6 * t0 + 1e-7
+    assert abs(t0 / (2 * 8192 ** 3 / (eff * 157.3e12) + 3e-6) - 1) < 0.01
     old = fg.fg_get_efficiency(7)
     try:
         assert fg.fg_set_efficiency(7, old[0] / 2, old[1]) == fg.FG_OK
-        assert abs(fg.fg_estimate_seconds(8192, 8192, 8192, 7) / t0 - 2) < 0.01
+        assert abs(fg.fg_estimate_seconds(8192, 8192, 8192, 7) / t0 - 2) < 0.02
     finally:
         assert fg.fg_set_efficiency(7, *old) == fg.FG_OK
     assert fg.fg_estimate_seconds(8192, 8192, 8192, 5) == -1.0   # vector-ALU entry
