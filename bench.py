@@ -415,7 +415,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only (--gpus 1); "
+        print("bench.py: runs on one GPU only (--gpus 1); "
               "multi-GPU sharding is not implemented", file=sys.stderr)
         sys.exit(2)
 

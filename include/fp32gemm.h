@@ -55,7 +55,7 @@ typedef enum fg_status {
     FG_OK = 0,
     FG_ERR_INVALID_ARG = 1, /* an argument is out of its domain; nothing enqueued */
     FG_ERR_HIP = 2,         /* the HIP runtime reported an error (launch, device query) */
-    FG_ERR_UNSUPPORTED = 3  /* valid BLAS arguments this build cannot run, e.g. a
+    FG_ERR_UNSUPPORTED = 3  /* valid BLAS arguments this library cannot run, e.g. a
                                device that is not gfx950 or a leading dimension
                                above FG_MAX_LD */
 } fg_status;
