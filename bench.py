@@ -43,7 +43,7 @@ def kernel_source_sha(kernel_config="mfma_"):
     elif kernel_config.startswith("valu_"):
         family = "sgemm_valu.hip"
     else:
-        family = "sgemm_mfma.hip"
+        family = "sgemm_mfma.h"
     h = hashlib.sha256()
     for f in (family, "fg_device.h", "fg_kernels.h"):
         with open(os.path.join(ROOT, "fp32_gemm_tile_amd", "csrc", f), "rb") as fh:

@@ -42,7 +42,8 @@ class fg_config(ctypes.Structure):
                 ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
                 ("wm", ctypes.c_int32), ("wn", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("stages", ctypes.c_int32),
-                ("lds_bytes", ctypes.c_int32), ("name", ctypes.c_char * 40)]
+                ("lds_bytes", ctypes.c_int32), ("mr", ctypes.c_int32),
+                ("name", ctypes.c_char * 40)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_}
@@ -134,6 +135,10 @@ def load_library(path: str = LIB_PATH):
     lib.fg_get_efficiency.restype = i32
     lib.fg_set_efficiency.argtypes = [i32, ctypes.c_double, ctypes.c_double]
     lib.fg_set_efficiency.restype = i32
+    lib.fg_set_raster.argtypes = [i32, i32]
+    lib.fg_set_raster.restype = i32
+    lib.fg_get_raster.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.fg_get_raster.restype = i32
     lib.fg_set_streamk_policy.argtypes = [i32]
     lib.fg_set_streamk_policy.restype = i32
     lib.fg_probe_mfma.argtypes = [i32, i32, vp, vp]
@@ -272,6 +277,19 @@ def fg_set_efficiency(config_id, eff, eff1) -> int:
 def fg_set_streamk_policy(policy) -> int:
     """0: split the stream-K tail when the model expects a gain; 1: always."""
     return load_library().fg_set_streamk_policy(policy)
+
+
+def fg_set_raster(group_m, xcd_remap) -> int:
+    """Raster order of the matrix-core kernels (fp32gemm_tune.h): band height
+    in tile rows (0 = default) and the XCD renumbering (1 on, 0 off)."""
+    return load_library().fg_set_raster(group_m, xcd_remap)
+
+
+def fg_get_raster():
+    """(group_m, xcd_remap) in use."""
+    g, x = ctypes.c_int32(), ctypes.c_int32()
+    _raise_if(load_library().fg_get_raster(ctypes.byref(g), ctypes.byref(x)))
+    return g.value, x.value
 
 
 def fg_probe_mfma(workgroups, iterations, out, stream=0) -> int:

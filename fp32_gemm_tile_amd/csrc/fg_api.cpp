@@ -5,8 +5,8 @@
 // The argument list and its meaning follow the BLAS-style routine of
 // "CuTe-ly writing an SM86 SGEMM", section "host-side setup" (row-major
 // here, with transpose flags); the per-shape choice of tile follows "Matmul
-// II: register blocking, warp tiling, tensor cores", section 8 (many kernel
-// variants and a heuristic that picks one per call).
+// II: register blocking, warp tiling, tensor cores", section 8 (a library
+// ships a family of tile variants and chooses among them for each shape).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -25,6 +25,15 @@
 #include "../../include/fp32gemm_probe.h"
 #include "../../include/fp32gemm_tune.h"
 #include "fg_kernels.h"
+
+// The instance list and the fitted efficiencies; a tuner builds a search
+// library from other lists by defining these.
+#ifndef FG_INSTANCES_INC
+#define FG_INSTANCES_INC "fg_mfma_instances.inc"
+#endif
+#ifndef FG_TUNED_INC
+#define FG_TUNED_INC "fg_tuned.inc"
+#endif
 
 namespace {
 
@@ -48,19 +57,17 @@ void clear_error() {
 // ---------------------------------------------------------------------------
 // Tile-configuration table.
 //
-// MFMA rows: workgroup tile bm x bn, k-tile 16, wave tile wm x wn built from
-// 32x32 accumulator blocks. `wps` is how many waves of that kernel one SIMD
-// holds at once (a 128 x 128 wave tile keeps 256 accumulators plus its
-// operands, which fills the 512 registers a SIMD lane has, so one). `eff` is
-// the fraction of a SIMD's matrix-core peak one wave reaches when it has the
-// SIMD to itself; it only ranks the candidates.
+// Matrix-core rows come from the instance list (fg_mfma_instances.inc, one
+// compiled kernel instance per row): workgroup tile bm x bn, k-tile bk, wave
+// tile wm x wn built from mr x mr accumulator blocks. `wps` is how many waves
+// of that kernel one SIMD holds at once (a 128 x 128 wave tile keeps 256
+// accumulators plus its operands, which fills the 512 registers a SIMD lane
+// has, so one). The vector-ALU and few-row rows are listed here.
 struct Entry {
     fg_config cfg;
-    int variant;   // index inside the kernel family's launcher
+    int variant;   // index inside the kernel family's launcher (the table id
+                   // for matrix-core entries)
     int wps;       // resident waves per SIMD
-    double eff;    // default efficiency for the cost model, SIMD full
-    double eff1;   // the same with one wave per SIMD (small grids); both are
-                   // replaced by the generated table fg_tuned.inc
     int fallback;  // entry used instead when A or B rows are not 16-byte
                    // aligned (entries with 16-byte direct-to-LDS loads only;
                    // -1 = any alignment is fine)
@@ -70,8 +77,8 @@ constexpr int kNumCUs = 256;
 constexpr int kSimdsPerCU = 4;
 
 Entry make_entry(int id, fg_kind kind, int variant, int bm, int bn, int bk, int wm, int wn,
-                 int threads, int stages, int wps, double eff, const char* name,
-                 int fallback = -1, double eff1 = 0) {
+                 int threads, int stages, int wps, const char* name, int fallback = -1,
+                 int mr = 0) {
     Entry e;
     memset(&e, 0, sizeof e);
     e.cfg.id = id;
@@ -83,64 +90,86 @@ Entry make_entry(int id, fg_kind kind, int variant, int bm, int bn, int bk, int 
     e.cfg.wn = wn;
     e.cfg.threads = threads;
     e.cfg.stages = stages;
+    e.cfg.mr = mr;
     e.cfg.lds_bytes = kind == FG_KIND_SKINNY ? 4 * bm * 32 * 4 : stages * (bm + bn) * bk * 4;
     snprintf(e.cfg.name, sizeof e.cfg.name, "%s", name);
     e.variant = variant;
     e.wps = wps;
-    e.eff = eff;
-    e.eff1 = eff1 > 0 ? eff1 : eff;
     e.fallback = fallback;
     return e;
 }
 
-const Entry* table() {
-    static const Entry t[] = {
-        // eff / eff1 here are defaults (first calibration at 8192^3 NN); the
-        // values in use come from the generated table fg_tuned.inc.
-        make_entry(0, FG_KIND_MFMA, 0, 256, 256, 16, 128, 128, 256, 2, 1, 0.857, "mfma_256x256x16_w2x2"),
-        make_entry(1, FG_KIND_MFMA, 1, 256, 128, 16, 128, 128, 128, 2, 1, 0.866, "mfma_256x128x16_w2x1"),
-        make_entry(2, FG_KIND_MFMA, 2, 128, 128, 16, 128, 128, 64, 2, 1, 0.850, "mfma_128x128x16_w1x1"),
-        make_entry(3, FG_KIND_MFMA, 3, 64, 128, 16, 64, 128, 64, 2, 1, 0.786, "mfma_64x128x16_w1x1"),
-        make_entry(4, FG_KIND_MFMA, 4, 32, 128, 16, 32, 128, 64, 2, 2, 0.737, "mfma_32x128x16_w1x1"),
-        // VALU rows: wm x wn is the per-thread tile; never auto-selected.
-        make_entry(5, FG_KIND_VALU, 0, 128, 128, 8, 8, 8, 256, 2, 2, 0.55, "valu_128x128x8_t8x8"),
-        make_entry(6, FG_KIND_VALU, 1, 64, 64, 8, 4, 4, 256, 2, 4, 0.44, "valu_64x64x8_t4x4"),
-        // MFMA rows fed by direct-to-LDS loads. The 16-byte form needs rows
-        // of A and B 16-byte aligned (otherwise the named entry runs); the
-        // 4-byte form (_dw) takes any rows.
-        make_entry(7, FG_KIND_MFMA, 5, 256, 256, 16, 128, 128, 256, 4, 1, 0.931, "mfma_256x256x16_w2x2_s4", 0),
-        make_entry(8, FG_KIND_MFMA, 6, 256, 128, 16, 128, 128, 128, 3, 1, 0.921, "mfma_256x128x16_w2x1_s3", 1),
-        make_entry(9, FG_KIND_MFMA, 7, 128, 128, 16, 64, 64, 256, 4, 2, 0.899, "mfma_128x128x16_w2x2_s4", 10),
-        make_entry(10, FG_KIND_MFMA, 8, 128, 128, 16, 64, 64, 256, 4, 2, 0.881, "mfma_128x128x16_w2x2_s4_dw"),
-        make_entry(11, FG_KIND_MFMA, 9, 256, 256, 16, 64, 128, 512, 4, 2, 0.90, "mfma_256x256x16_w4x2_s4", 0),
-        make_entry(12, FG_KIND_MFMA, 10, 256, 128, 16, 128, 64, 256, 3, 2, 0.90, "mfma_256x128x16_w2x2_s3", 1, 0.86),
-        // Few-row kernel: bm = rows per block (up to 8), bn = columns per
-        // workgroup for B stored K x N; memory-bound, costed separately.
-        make_entry(13, FG_KIND_SKINNY, 0, 8, 32, 0, 8, 4, 256, 0, 2, 0.7, "valu_skinny_m8"),
-        // Small tiles for grids the entries above leave under-filled; several
-        // workgroups share a CU.
-        // eff1: measured with one workgroup per CU (M <= 256, N = K = 4096).
-        make_entry(14, FG_KIND_MFMA, 11, 64, 64, 16, 32, 32, 256, 4, 5, 0.75, "mfma_64x64x16_w2x2_s4", 15, 0.57),
-        make_entry(15, FG_KIND_MFMA, 12, 64, 64, 16, 32, 32, 256, 4, 5, 0.72, "mfma_64x64x16_w2x2_s4_dw", -1, 0.55),
-        make_entry(16, FG_KIND_MFMA, 13, 128, 64, 16, 64, 32, 256, 4, 3, 0.80, "mfma_128x64x16_w2x2_s4", 15, 0.74),
-        // Eight waves per workgroup: two per SIMD even when the grid has only
-        // one workgroup per CU.
-        make_entry(17, FG_KIND_MFMA, 14, 128, 128, 16, 32, 64, 512, 4, 4, 0.85, "mfma_128x128x16_w4x2_s4", 10, 0.80),
-    };
-    return t;
+// Name of a matrix-core entry: tile, k-tile depth, wave grid, then the
+// ring depth (direct-to-LDS entries), "_dw" for 4-byte direct-to-LDS loads
+// and "_m16" for 16 x 16 blocks.
+Entry mfma_entry(int id, int bm, int bn, int waves_m, int waves_n, int bk, int mr, int stages,
+                 int dmab, int wps, int fallback) {
+    char name[40];
+    int n = snprintf(name, sizeof name, "mfma_%dx%dx%d_w%dx%d", bm, bn, bk, waves_m, waves_n);
+    if (stages > 2) n += snprintf(name + n, sizeof name - n, "_s%d", stages);
+    if (stages > 2 && dmab == 4) n += snprintf(name + n, sizeof name - n, "_dw");
+    if (mr == 16) snprintf(name + n, sizeof name - n, "_m16");
+    return make_entry(id, FG_KIND_MFMA, id, bm, bn, bk, bm / waves_m, bn / waves_n,
+                      64 * waves_m * waves_n, stages, wps, name, fallback, mr);
 }
-constexpr int kNumEntries = 18;
 
-// Cost-model efficiencies, one pair per entry: from the generated table
-// (fg_tuned.inc) over the defaults above, and replaceable at run time by a
-// tuner (fg_set_efficiency). Atomics: a tuner may set them while other
-// threads plan calls.
-struct Efficiency {
-    std::atomic<double> eff, eff1;
+struct Table {
+    Entry* rows = nullptr;
+    int n = 0;
 };
 
+const Table& table_rows() {
+    static const Table t = [] {
+        static Entry fixed[] = {
+            // VALU rows: wm x wn is the per-thread tile; never auto-selected.
+            make_entry(5, FG_KIND_VALU, 0, 128, 128, 8, 8, 8, 256, 2, 2, "valu_128x128x8_t8x8"),
+            make_entry(6, FG_KIND_VALU, 1, 64, 64, 8, 4, 4, 256, 2, 4, "valu_64x64x8_t4x4"),
+            // Few-row kernel: bm = rows per block (up to 8), bn = columns per
+            // workgroup for B stored K x N; memory-bound, costed separately.
+            make_entry(13, FG_KIND_SKINNY, 0, 8, 32, 0, 8, 4, 256, 0, 2, "valu_skinny_m8"),
+        };
+        static Entry mfma[] = {
+#define FG_MFMA_ENTRY(id, bm, bn, wm, wn, bk, mr, st, dmab, occ, wps, fb) \
+    mfma_entry(id, bm, bn, wm, wn, bk, mr, st, dmab, wps, fb),
+#include FG_INSTANCES_INC
+#undef FG_MFMA_ENTRY
+        };
+        const int nf = sizeof fixed / sizeof fixed[0], nm = sizeof mfma / sizeof mfma[0];
+        static Entry all[sizeof fixed / sizeof fixed[0] + sizeof mfma / sizeof mfma[0]];
+        Table t;
+        t.rows = all;
+        t.n = nf + nm;
+        // Place every row at its id; the ids must be exactly 0 .. n-1.
+        bool seen[sizeof all / sizeof all[0]] = {};
+        auto place = [&](const Entry& e) {
+            if (e.cfg.id < 0 || e.cfg.id >= t.n || seen[e.cfg.id]) {
+                fprintf(stderr, "fp32gemm: table id %d duplicated or out of range\n", e.cfg.id);
+                abort();
+            }
+            seen[e.cfg.id] = true;
+            all[e.cfg.id] = e;
+        };
+        for (int i = 0; i < nf; ++i) place(fixed[i]);
+        for (int i = 0; i < nm; ++i) place(mfma[i]);
+        return t;
+    }();
+    return t;
+}
+
+const Entry* table() { return table_rows().rows; }
+int num_entries() { return table_rows().n; }
+
+// Cost-model efficiencies, one pair per entry: from the generated table
+// (fg_tuned.inc) where it has the entry, else a neutral default, and
+// replaceable at run time by a tuner (fg_set_efficiency). Atomics: a tuner
+// may set them while other threads plan calls.
+struct Efficiency {
+    std::atomic<double> eff{0.8}, eff1{0.8};
+};
+constexpr int kMaxEntries = 256;
+
 Efficiency* efficiencies() {
-    static Efficiency e[kNumEntries];
+    static Efficiency e[kMaxEntries];
     static std::once_flag once;
     std::call_once(once, [] {
         struct Tuned {
@@ -148,14 +177,10 @@ Efficiency* efficiencies() {
             double eff, eff1;
         };
         static const Tuned tuned[] = {
-#include "fg_tuned.inc"
+#include FG_TUNED_INC
         };
-        for (int i = 0; i < kNumEntries; ++i) {
-            e[i].eff.store(table()[i].eff);
-            e[i].eff1.store(table()[i].eff1);
-        }
         for (const Tuned& t : tuned) {
-            if (t.id < 0 || t.id >= kNumEntries) continue;
+            if (t.id < 0 || t.id >= num_entries()) continue;
             e[t.id].eff.store(t.eff);
             e[t.id].eff1.store(t.eff1);
         }
@@ -272,7 +297,7 @@ int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_s
     int best = -1;
     double best_cost = 0;
     *best_splits = 1;
-    for (int i = 0; i < kNumEntries; ++i) {
+    for (int i = 0; i < num_entries(); ++i) {
         const Entry& e = table()[i];
         if (e.cfg.kind == FG_KIND_SKINNY) {
             if (mfma_only) continue;
@@ -299,24 +324,12 @@ int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_s
     return best;
 }
 
-// Tuning overrides (environment, read once): FG_FORCE_CONFIG=<id> forces a
-// table entry in calls that do not name one; FG_GROUP_M=<n> sets the raster
-// band height. For measurements only.
-int force_config_override() {
-    static int v = [] {
-        const char* s = getenv("FG_FORCE_CONFIG");
-        return s ? atoi(s) : -1;
-    }();
-    return v;
-}
-
-int group_m_override() {
-    static int v = [] {
-        const char* s = getenv("FG_GROUP_M");
-        return s ? atoi(s) : 0;
-    }();
-    return v;
-}
+// Raster order of the matrix-core kernels (fg_set_raster in fp32gemm_tune.h;
+// for measurements): band height in tile rows, and whether workgroup ids are
+// renumbered so each XCD gets a contiguous run of tiles.
+constexpr int kDefaultGroupM = 4;
+std::atomic<int> g_group_m{kDefaultGroupM};
+std::atomic<int> g_xcd_remap{1};
 
 // ---------------------------------------------------------------------------
 // Device check: the kernels are built for gfx950 only.
@@ -435,7 +448,7 @@ bool plan_streamk(int64_t M, int64_t N, int64_t K, bool ab_aligned, bool beta0, 
 
 int32_t build_flags(const float* A, int64_t lda, const float* B, int64_t ldb, const float* C,
                     int64_t ldc, float beta) {
-    int32_t f = fg::FLAG_XCD_REMAP;
+    int32_t f = g_xcd_remap.load(std::memory_order_relaxed) ? fg::FLAG_XCD_REMAP : 0;
     if (aligned16(A) && lda % 4 == 0) f |= fg::FLAG_VEC_A;
     if (aligned16(B) && ldb % 4 == 0) f |= fg::FLAG_VEC_B;
     if (aligned16(C) && ldc % 4 == 0) f |= fg::FLAG_VEC_C;
@@ -448,7 +461,7 @@ int32_t build_flags(const float* A, int64_t lda, const float* B, int64_t ldb, co
 
 extern "C" {
 
-int32_t fg_abi_version(void) { return 1; }
+int32_t fg_abi_version(void) { return 2; }
 
 int32_t fg_last_bad_arg(void) { return t_bad_arg; }
 
@@ -464,11 +477,11 @@ const char* fg_status_string(fg_status s) {
     }
 }
 
-int32_t fg_num_configs(void) { return kNumEntries; }
+int32_t fg_num_configs(void) { return num_entries(); }
 
 fg_status fg_get_config(int32_t id, fg_config* out) {
     clear_error();
-    if (id < 0 || id >= kNumEntries) return fail(FG_ERR_INVALID_ARG, 1, "config id %d out of range", id);
+    if (id < 0 || id >= num_entries()) return fail(FG_ERR_INVALID_ARG, 1, "config id %d out of range", id);
     if (!out) return fail(FG_ERR_INVALID_ARG, 2, "out is NULL");
     *out = table()[id].cfg;
     return FG_OK;
@@ -502,7 +515,7 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
     clear_error();
     fg_status s = validate(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
     if (s != FG_OK) return s;
-    if (config_id < -1 || config_id >= kNumEntries)
+    if (config_id < -1 || config_id >= num_entries())
         return fail(FG_ERR_INVALID_ARG, config_arg, "config id %d out of range", config_id);
     const bool epi_on = epi && (epi->row_scale || epi->col_scale || epi->row_bias ||
                                 epi->col_bias || epi->activation != FG_ACT_NONE);
@@ -560,8 +573,7 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
         if (s != FG_OK) return s;
         p.tiles_m = (int32_t)cdiv(M, en.cfg.bm);
         p.tiles_n = (int32_t)cdiv(N, en.cfg.bn);
-        p.group_m = group_m_override() > 0 ? group_m_override() : 4;
-        if (p.group_m > p.tiles_m) p.group_m = p.tiles_m;
+        p.group_m = std::min(g_group_m.load(std::memory_order_relaxed), p.tiles_m);
         hipError_t e = hipSuccess;
         if (plan.full > 0) {
             fg::GemmParams d = p;
@@ -597,8 +609,6 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
     if (max_splits < 1) max_splits = 1;
     int64_t want = splits;
     int idx;
-    if (config_id < 0 && force_config_override() >= 0 && force_config_override() < kNumEntries)
-        config_id = force_config_override();
     if (config_id >= 0) {
         idx = config_id;
         if (want == 0) want = 1;
@@ -608,7 +618,7 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
                            &auto_splits, want > 1);
         if (want == 0) want = auto_splits;
     }
-    if (idx < 0 || idx >= kNumEntries)
+    if (idx < 0 || idx >= num_entries())
         return fail(FG_ERR_UNSUPPORTED, 0, "no table entry fits this call");
     if (table()[idx].fallback >= 0 && !ab_aligned) idx = table()[idx].fallback;
     const Entry& en = table()[idx];
@@ -629,8 +639,7 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
     p.tiles_n = (int32_t)cdiv(N, en.cfg.bn);
     const int64_t nblocks = (int64_t)p.tiles_m * p.tiles_n;
     if (nblocks > 0x7FFFFFFF) return fail(FG_ERR_UNSUPPORTED, 0, "too many tiles");
-    p.group_m = group_m_override() > 0 ? group_m_override() : 4;
-    if (p.group_m > p.tiles_m) p.group_m = p.tiles_m;
+    p.group_m = std::min(g_group_m.load(std::memory_order_relaxed), p.tiles_m);
     p.kt_per_split = (int32_t)kps;
     p.c_split_stride = 0;
 
@@ -734,7 +743,7 @@ fg_status fg_sgemm_fused(fg_op transA, fg_op transB, int64_t M, int64_t N, int64
 
 double fg_estimate_seconds(int64_t M, int64_t N, int64_t K, int32_t config_id, int32_t splits,
                            int32_t beta_zero) {
-    if (M < 0 || N < 0 || K < 0 || config_id < 0 || config_id >= kNumEntries) return -1.0;
+    if (M < 0 || N < 0 || K < 0 || config_id < 0 || config_id >= num_entries()) return -1.0;
     const Entry& e = table()[config_id];
     if (e.cfg.kind == FG_KIND_SKINNY)
         return skinny_cost(M, N, K, beta_zero != 0, efficiencies()[config_id].eff.load());
@@ -744,7 +753,7 @@ double fg_estimate_seconds(int64_t M, int64_t N, int64_t K, int32_t config_id, i
 
 fg_status fg_get_efficiency(int32_t config_id, double* eff, double* eff1) {
     clear_error();
-    if (config_id < 0 || config_id >= kNumEntries || table()[config_id].cfg.kind == FG_KIND_VALU)
+    if (config_id < 0 || config_id >= num_entries() || table()[config_id].cfg.kind == FG_KIND_VALU)
         return fail(FG_ERR_INVALID_ARG, 1, "config %d has no modelled efficiency", config_id);
     if (!eff) return fail(FG_ERR_INVALID_ARG, 2, "eff is NULL");
     if (!eff1) return fail(FG_ERR_INVALID_ARG, 3, "eff1 is NULL");
@@ -755,12 +764,32 @@ fg_status fg_get_efficiency(int32_t config_id, double* eff, double* eff1) {
 
 fg_status fg_set_efficiency(int32_t config_id, double eff, double eff1) {
     clear_error();
-    if (config_id < 0 || config_id >= kNumEntries || table()[config_id].cfg.kind == FG_KIND_VALU)
+    if (config_id < 0 || config_id >= num_entries() || table()[config_id].cfg.kind == FG_KIND_VALU)
         return fail(FG_ERR_INVALID_ARG, 1, "config %d has no modelled efficiency", config_id);
     if (!(eff > 0.0 && eff <= 1.0)) return fail(FG_ERR_INVALID_ARG, 2, "eff outside (0, 1]");
     if (!(eff1 > 0.0 && eff1 <= 1.0)) return fail(FG_ERR_INVALID_ARG, 3, "eff1 outside (0, 1]");
     efficiencies()[config_id].eff.store(eff);
     efficiencies()[config_id].eff1.store(eff1);
+    return FG_OK;
+}
+
+fg_status fg_set_raster(int32_t group_m, int32_t xcd_remap) {
+    clear_error();
+    if (group_m < 0 || group_m > 4096)
+        return fail(FG_ERR_INVALID_ARG, 1, "group_m %d outside 0..4096", group_m);
+    if (xcd_remap != 0 && xcd_remap != 1)
+        return fail(FG_ERR_INVALID_ARG, 2, "xcd_remap must be 0 or 1");
+    g_group_m.store(group_m == 0 ? kDefaultGroupM : group_m);
+    g_xcd_remap.store(xcd_remap);
+    return FG_OK;
+}
+
+fg_status fg_get_raster(int32_t* group_m, int32_t* xcd_remap) {
+    clear_error();
+    if (!group_m) return fail(FG_ERR_INVALID_ARG, 1, "group_m is NULL");
+    if (!xcd_remap) return fail(FG_ERR_INVALID_ARG, 2, "xcd_remap is NULL");
+    *group_m = g_group_m.load();
+    *xcd_remap = g_xcd_remap.load();
     return FG_OK;
 }
 

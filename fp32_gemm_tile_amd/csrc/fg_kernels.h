@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fp32gemm.h"
+
 namespace fg {
 
 // Everything a GEMM kernel needs, passed by value as the kernel argument.
@@ -55,13 +57,14 @@ enum : int32_t {
 };
 
 // Launchers: enqueue one kernel on `stream`; return the HIP launch status.
-// `variant` indexes the kernel's compile-time tile shape (see the table in
-// fg_api.cpp); trans_a / trans_b select the operand layouts.
-hipError_t launch_mfma(int variant, int trans_a, int trans_b, const GemmParams& p,
+// For the matrix-core kernels `id` is the table id of a line of the
+// instance list (fg_mfma_instances.inc); for the others `variant` indexes the
+// family's compile-time shapes. trans_a / trans_b select the operand layouts.
+hipError_t launch_mfma(int id, int trans_a, int trans_b, const GemmParams& p,
                        hipStream_t stream);
 // The same on an explicit grid: `tiles` workgroups along x (tile ids
 // p.tile_base ..), `splits` along y (k ranges of p.kt_per_split k-tiles).
-hipError_t launch_mfma_tiles(int variant, int trans_a, int trans_b, const GemmParams& p,
+hipError_t launch_mfma_tiles(int id, int trans_a, int trans_b, const GemmParams& p,
                              int32_t tiles, int32_t splits, hipStream_t stream);
 hipError_t launch_valu(int variant, int trans_a, int trans_b, const GemmParams& p,
                        hipStream_t stream);

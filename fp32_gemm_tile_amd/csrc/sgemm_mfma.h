@@ -1,25 +1,32 @@
-// True-fp32 SGEMM on the gfx950 matrix cores (v_mfma_f32_32x32x2_f32).
+// True-fp32 SGEMM on the gfx950 matrix cores: the kernel template behind
+// every matrix-core table entry. Each entry is one instance of it, compiled in
+// its own translation unit (sgemm_mfma_inst.hip) from the instance list
+// fg_mfma_instances.inc.
 //
 // Structure (the block-tile / warp-tile / thread-tile hierarchy of "Matmul
 // II: register blocking, warp tiling, tensor cores", sections 1, 5 and 7,
 // rebuilt for 64-wide wavefronts and the MFMA register layout):
 //
-//   workgroup tile BM x BN, k-tiles of BK = 16 staged in a 2-buffer LDS ring;
-//   wavefront tile WM x WN = (MB x 32) x (NB x 32), i.e. MB x NB accumulator
-//   blocks of 32 x 32, 16 fp32 registers per lane each;
-//   one v_mfma_f32_32x32x2_f32 per block and k-step of 2.
+//   workgroup tile BM x BN, k-tiles of BK (8, 16 or 32) staged in LDS;
+//   wavefront tile WM x WN = (MB x MR) x (NB x MR), i.e. MB x NB accumulator
+//   blocks of MR x MR;
+//   MR = 32: one v_mfma_f32_32x32x2_f32 per block and k-step (2 k values),
+//            16 fp32 accumulator registers per lane and block;
+//   MR = 16: one v_mfma_f32_16x16x4_f32 per block and k-step (4 k values),
+//            4 accumulator registers per lane and block.
 //
-// k mapping. One MFMA consumes two k values: lanes 0-31 supply k-index 0 and
-// lanes 32-63 k-index 1 (A: lane l holds A[l%32][l/32]; B: lane l holds
-// B[l/32][l%32]). Summation order is free, so inside a 16-deep k-tile the
-// instruction at k-step s (0..7) takes k = s for lanes 0-31 and k = 8 + s for
-// lanes 32-63. A lane then needs k = 8h .. 8h+7 of its row across the eight
-// k-steps: two 128-bit LDS reads when the tile is stored k-contiguous.
+// k mapping. One MFMA consumes KS = 64 / MR k values: lanes are KS groups of
+// MR (group h = lane / MR, position i = lane % MR), and group h supplies
+// k-index h (A: lane holds A[i][h]; B: lane holds B[h][i]). Summation order is
+// free, so inside a BK-deep k-tile the instruction at k-step s (of KPL =
+// BK / KS) takes k = h * KPL + s from group h. A lane then needs k = h * KPL
+// .. h * KPL + KPL - 1 of its row across the k-steps: KPL / 4 128-bit LDS
+// reads when the tile is stored k-contiguous.
 //
 // Interleaved blocks. Inside a wave tile, block b of the N direction holds
-// columns NB*j + b (j = lane % 32) instead of 32*b + j; likewise rows MB*i + a
-// for the M direction. A lane's operands for all NB blocks at one k are then
-// NB consecutive floats of an n-contiguous LDS row (one 128-bit read for
+// columns NB*i + b instead of MR*b + i; likewise rows MB*i + a for the M
+// direction. A lane's operands for all NB blocks at one k are then NB
+// consecutive floats of an n-contiguous LDS row (one 128-bit read for
 // NB = 4), and its results for those blocks are NB consecutive columns of C
 // (one 128-bit store), which is the wide-store epilogue of "CuTe-ly writing
 // an SM86 SGEMM", section "wide epilogue instructions", obtained here from
@@ -29,65 +36,97 @@
 //   * mn-contiguous in global memory (A^T stored K x M, or B stored K x N):
 //     LDS row = one k, BX floats; lanes read consecutive addresses.
 //   * k-contiguous (A stored M x K, or B^T stored N x K): LDS row = one m (or
-//     n), 16 floats. Rows are placed in "physical" order so that the 32 rows
-//     read by one instruction are consecutive, and the four 16-byte chunks of
-//     a row are XOR-swizzled with bits 2-3 of the physical row, so sixteen
-//     consecutive rows' chunk c land in sixteen distinct 16-byte bank groups
-//     (the XOR swizzle of "CuTe-ly writing an SM86 SGEMM", section "swizzles
-//     & shared memory", at 16-byte granularity).
+//     n), BK floats. Rows are placed in "physical" order so that the MR rows
+//     read by one instruction are consecutive, and the 16-byte chunks of a
+//     row are XOR-swizzled with the bits of the physical row above the rows
+//     that share one 256-byte window, so sixteen consecutive rows' chunk c
+//     land in sixteen distinct 16-byte slots (the XOR swizzle of "CuTe-ly
+//     writing an SM86 SGEMM", section "swizzles & shared memory", at 16-byte
+//     granularity).
 //
-// Pipeline (one barrier per k-tile): while the MFMAs of k-tile t run from LDS
-// buffer t%2, the registers already hold k-tile t+1 loaded from global
-// memory; they are written to buffer (t+1)%2 after the MFMAs are issued and
-// the loads for k-tile t+2 are started. Buffer (t+1)%2 was last read in
-// iteration t-1, which the barrier closing that iteration protects.
-//
-// Edges: interior tiles use unguarded 128-bit buffer loads; tiles that cross
-// M, N or K (and operands whose rows are not 16-byte aligned) use guarded
-// loads that read out-of-range elements as zero. Every global access goes
+// Loader and pipeline: see sgemm_mfma_kernel below. Every global access goes
 // through a buffer resource bounded by the matrix's extent, so no access can
 // leave the caller's allocation.
+#pragma once
+
 #include "fg_device.h"
 
 namespace fg {
-namespace {
+namespace mfma {
 
-constexpr int kBK = 16;
+// Accumulator block type and MFMA of one block shape.
+template <int MR>
+struct Mfma;
 
-// One operand's share of a k-tile and how this thread loads and reads it.
+template <>
+struct Mfma<32> {
+    using acc_t = f16v;
+    static constexpr int kRegs = 16;
+    __device__ static acc_t step(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    // Block row held by accumulator register r of lane group h (the
+    // instruction's output layout: rows 8 (r / 4) + 4 h + r % 4).
+    __device__ static int row(int r, int h) { return 8 * (r / 4) + 4 * h + (r % 4); }
+};
+
+template <>
+struct Mfma<16> {
+    using acc_t = f4;
+    static constexpr int kRegs = 4;
+    __device__ static acc_t step(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    // Output layout of the 16 x 16 instruction: rows 4 h + r.
+    __device__ static int row(int r, int h) { return 4 * h + r; }
+};
+
+// One operand's share of a k-tile and how this thread loads and reads it
+// through registers (2-stage entries, and the partial last k-tile of the
+// direct-to-LDS entries).
 //   BX: tile extent in M (for A) or N (for B); WX: wave extent; XB: blocks per
-//   wave; MN: operand is mn-contiguous in global memory; NT: threads.
-template <int BX, int WX, int XB, bool MN, int NT>
+//   wave; MN: operand is mn-contiguous in global memory; NT: threads; BK:
+//   k-tile depth; MR: block edge.
+template <int BX, int WX, int XB, bool MN, int NT, int BK, int MR>
 struct Operand {
-    static constexpr int kStage = BX * kBK;    // floats per LDS buffer
+    static constexpr int kStage = BX * BK;     // floats per LDS buffer
     static constexpr int kVecs = kStage / 4;   // 16-byte vectors per k-tile
-    static constexpr int kVPT = kVecs / NT;    // vectors per thread
-    static_assert(kVecs % NT == 0, "tile must split evenly over threads");
+    static constexpr int kVPT = (kVecs + NT - 1) / NT;  // vectors per thread
+    static constexpr bool kAll = kVecs % NT == 0;        // every thread, every slot
+    static constexpr int kKS = 64 / MR;        // k values per instruction
+    static constexpr int kKPL = BK / kKS;      // k values per lane per k-tile
+    static constexpr int kCH = BK / 4;         // 16-byte chunks per k-contiguous row
+    static_assert(BK == 8 || BK == 16 || BK == 32, "k-tile depth 8, 16 or 32");
+    static_assert(MR == 16 || MR == 32, "16 x 16 or 32 x 32 blocks");
+    static_assert(kKPL == 2 || kKPL % 4 == 0, "k values per lane");
     static_assert(XB == 1 || XB == 2 || XB == 4, "1, 2 or 4 blocks per wave");
-    static_assert(WX == 32 * XB, "wave extent is XB blocks of 32");
+    static_assert(WX == MR * XB, "wave extent is XB blocks of MR");
 
     uint32_t goff[kVPT];  // byte offset inside the k-tile (global)
     int lds[kVPT];        // float offset inside one LDS buffer
     int row[kVPT];        // k row (MN) or m/n row (k-contiguous) within the tile
     int col[kVPT];        // first element along the contiguous direction
+    bool act[kVPT];       // this slot exists (kVecs not a multiple of NT)
     f4 reg[kVPT];
 
     // Physical LDS row of logical tile row x (k-contiguous layout) and back.
     __device__ static int phys_to_logical(int pr) {
         const int w = pr / WX, within = pr % WX;
-        const int a = within / 32, i = within % 32;
+        const int a = within / MR, i = within % MR;
         return w * WX + i * XB + a;
     }
     // 16-byte chunk swizzle of a k-contiguous row: an ds_read_b128 is served
-    // 16 lanes (256 bytes) at a time, and 16 consecutive physical rows hold
-    // chunk c at 16 distinct 16-byte slots of a 256-byte window when the
-    // chunk index is XORed with bits 2-3 of the row.
-    __device__ static int swz(int pr) { return (pr >> 2) & 3; }
+    // 16 lanes (256 bytes) at a time, a 256-byte window holds 64 / BK rows,
+    // and sixteen consecutive physical rows hold chunk c at sixteen distinct
+    // 16-byte slots of a window when the chunk index is XORed with the row
+    // bits above that (bits 2-3 for BK = 16, 1-3 for 32, bit 3 for 8).
+    __device__ static int swz(int pr) { return ((pr * BK) >> 6) & (kCH - 1); }
 
     __device__ void init(int tid, int ld) {
 #pragma unroll
         for (int q = 0; q < kVPT; ++q) {
             const int v = tid + NT * q;
+            act[q] = kAll || v < kVecs;
             if constexpr (MN) {
                 const int r = v / (BX / 4), c = v % (BX / 4);
                 row[q] = r;
@@ -95,11 +134,11 @@ struct Operand {
                 lds[q] = r * BX + 4 * c;
                 goff[q] = (uint32_t)(r * ld + 4 * c) * 4u;
             } else {
-                const int pr = v / 4, c = v % 4;
+                const int pr = v / kCH, c = v % kCH;
                 const int x = phys_to_logical(pr);
                 row[q] = x;
                 col[q] = 4 * c;
-                lds[q] = pr * kBK + 4 * (c ^ swz(pr));
+                lds[q] = pr * BK + 4 * (c ^ swz(pr));
                 goff[q] = (uint32_t)(x * ld + 4 * c) * 4u;
             }
         }
@@ -111,29 +150,31 @@ struct Operand {
                          int len) {
         if (fast) {
 #pragma unroll
-            for (int q = 0; q < kVPT; ++q) reg[q] = ld4(r, goff[q]);
+            for (int q = 0; q < kVPT; ++q)
+                if (act[q]) reg[q] = ld4(r, goff[q]);
         } else {
 #pragma unroll
             for (int q = 0; q < kVPT; ++q) {
                 f4 z = {0.f, 0.f, 0.f, 0.f};
-                reg[q] = row[q] < rows_left ? ld4_guard(r, goff[q], col[q], len, vec) : z;
+                reg[q] = act[q] && row[q] < rows_left ? ld4_guard(r, goff[q], col[q], len, vec) : z;
             }
         }
     }
 
     __device__ void store_lds(float* buf) const {
 #pragma unroll
-        for (int q = 0; q < kVPT; ++q) *reinterpret_cast<f4*>(buf + lds[q]) = reg[q];
+        for (int q = 0; q < kVPT; ++q)
+            if (act[q]) *reinterpret_cast<f4*>(buf + lds[q]) = reg[q];
     }
 
-    // Operands of this lane for all 8 k-steps and XB blocks:
-    // frag[s][x] = op(X) at k = 8h + s, block x, lane position i.
+    // Operands of this lane for all KPL k-steps and XB blocks:
+    // frag[s][x] = op(X) at k = KPL h + s, block x, lane position i.
     __device__ static void read_frags(const float* buf, int wbase, int i, int h,
-                                      float (&frag)[kBK / 2][XB]) {
+                                      float (&frag)[kKPL][XB]) {
         if constexpr (MN) {
 #pragma unroll
-            for (int s = 0; s < kBK / 2; ++s) {
-                const float* p = buf + (8 * h + s) * BX + wbase + XB * i;
+            for (int s = 0; s < kKPL; ++s) {
+                const float* p = buf + (kKPL * h + s) * BX + wbase + XB * i;
                 if constexpr (XB == 4) {
                     f4 v = *reinterpret_cast<const f4*>(p);
                     frag[s][0] = v[0]; frag[s][1] = v[1]; frag[s][2] = v[2]; frag[s][3] = v[3];
@@ -147,18 +188,29 @@ struct Operand {
         } else {
 #pragma unroll
             for (int x = 0; x < XB; ++x) {
-                const int pr = wbase + 32 * x + i;
-                const float* rowp = buf + pr * kBK;
-                f4 lo = *reinterpret_cast<const f4*>(rowp + 4 * ((2 * h) ^ swz(pr)));
-                f4 hi = *reinterpret_cast<const f4*>(rowp + 4 * ((2 * h + 1) ^ swz(pr)));
+                const int pr = wbase + MR * x + i;
+                const float* rowp = buf + pr * BK;
+                if constexpr (kKPL >= 4) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    frag[s][x] = lo[s];
-                    frag[s + 4][x] = hi[s];
+                    for (int q = 0; q < kKPL / 4; ++q) {
+                        const int c = h * (kKPL / 4) + q;
+                        f4 v = *reinterpret_cast<const f4*>(rowp + 4 * (c ^ swz(pr)));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) frag[4 * q + e][x] = v[e];
+                    }
+                } else {
+                    // two k values: half of chunk h / 2
+                    const int c = h >> 1;
+                    f2 v = *reinterpret_cast<const f2*>(rowp + 4 * (c ^ swz(pr)) + 2 * (h & 1));
+                    frag[0][x] = v[0];
+                    frag[1][x] = v[1];
                 }
             }
         }
     }
+
+    // LDS read instructions read_frags() issues per k-tile.
+    static constexpr int kReads = MN ? kKPL : XB * (kKPL >= 4 ? kKPL / 4 : 1);
 };
 
 // One operand's k-tile filled by direct-to-LDS buffer loads. A
@@ -172,14 +224,14 @@ struct Operand {
 // global-to-shared copy of "Matmul II", section 7 (t3) and "CuTe-ly writing
 // an SM86 SGEMM", section "mainloop": the data bypasses registers and the
 // wave keeps issuing MFMAs.
-template <int BX, int WX, int XB, bool MN, int NW, int BYTES>
+template <int BX, int WX, int XB, bool MN, int NW, int BYTES, int BK, int MR>
 struct DmaOperand {
-    using Op = Operand<BX, WX, XB, MN, 64 * NW>;
+    using Op = Operand<BX, WX, XB, MN, 64 * NW, BK, MR>;
     static constexpr int kW = BYTES / 4;                    // floats per lane
     static constexpr int kInst = Op::kStage / (64 * kW);    // instructions per stage
     static constexpr int kPerWave = kInst / NW;
     static_assert(BYTES == 4 || BYTES == 16, "dword or dwordx4");
-    static_assert(kInst % NW == 0, "stage must split evenly over the waves");
+    static_assert(kInst % NW == 0 && kPerWave > 0, "stage must split evenly over the waves");
 
     uint32_t voff[kPerWave];
 
@@ -192,7 +244,7 @@ struct DmaOperand {
                 const int k = pos / BX, col = pos % BX;
                 voff[q] = (uint32_t)(k * ld + col) * 4u;
             } else {
-                const int pr = pos / kBK, slot = (pos % kBK) / 4, e = pos % 4;
+                const int pr = pos / BK, slot = (pos % BK) / 4, e = pos % 4;
                 const int c = slot ^ Op::swz(pr);
                 const int x = Op::phys_to_logical(pr);
                 voff[q] = (uint32_t)(x * ld + 4 * c + e) * 4u;
@@ -234,53 +286,57 @@ __device__ __forceinline__ void wait_vm_lds() {
 // the compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
-// LDS read instructions read_frags() issues for one operand per k-tile.
-template <int XB, bool MN>
-constexpr int read_count() {
-    return MN ? (kBK / 2) * (XB == 8 ? 2 : 1) : 2 * XB;
-}
-
-template <int MB, int NB>
-__device__ __forceinline__ void mfma_kstep(f16v (&acc)[MB][NB], const float (&fa)[kBK / 2][MB],
-                                           const float (&fb)[kBK / 2][NB], int s) {
+template <int MR, int MB, int NB, int KPL>
+__device__ __forceinline__ void mfma_kstep(typename Mfma<MR>::acc_t (&acc)[MB][NB],
+                                           const float (&fa)[KPL][MB],
+                                           const float (&fb)[KPL][NB], int s) {
 #pragma unroll
     for (int a = 0; a < MB; ++a)
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[s][a], fb[s][b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < NB; ++b) acc[a][b] = Mfma<MR>::step(fa[s][a], fb[s][b], acc[a][b]);
 }
 
-template <int MB, int NB>
-__device__ __forceinline__ void mfma_ktile(f16v (&acc)[MB][NB], const float (&fa)[kBK / 2][MB],
-                                           const float (&fb)[kBK / 2][NB]) {
+template <int MR, int MB, int NB, int KPL>
+__device__ __forceinline__ void mfma_ktile(typename Mfma<MR>::acc_t (&acc)[MB][NB],
+                                           const float (&fa)[KPL][MB],
+                                           const float (&fb)[KPL][NB]) {
 #pragma unroll
-    for (int s = 0; s < kBK / 2; ++s) mfma_kstep<MB, NB>(acc, fa, fb, s);
+    for (int s = 0; s < KPL; ++s) mfma_kstep<MR, MB, NB, KPL>(acc, fa, fb, s);
 }
 
-// STAGES == 2: register-staged loop (any alignment, any edges).
+// STAGES == 2: register-staged loop (any alignment, any edges): while the
+// MFMAs of k-tile t run from LDS buffer t%2, the registers already hold
+// k-tile t+1 loaded from global memory; they are written to buffer (t+1)%2
+// after the MFMAs are issued and the loads for k-tile t+2 are started.
+// Buffer (t+1)%2 was last read in iteration t-1, which the barrier closing
+// that iteration protects.
 // STAGES >= 3: direct-to-LDS loop over a STAGES-deep ring, with the next
 // k-tile's fragments read during the current k-tile's MFMAs. DMAB = 16 needs
 // the rows of A and B to start 16-byte aligned (the dispatcher checks);
-// DMAB = 4 takes any rows. Tiles that
-// cross M or N take the same loop: a row of op(A) past M (a column of op(B)
-// past N) only feeds elements of C that are never stored, and the bounded
-// buffer resources return 0 past the end of each matrix. A partial last
-// k-tile (K not a multiple of 16) must read as exact zeros past K, so it goes
-// through the guarded register path once after the loop.
+// DMAB = 4 takes any rows. Tiles that cross M or N take the same loop: a row
+// of op(A) past M (a column of op(B) past N) only feeds elements of C that
+// are never stored, and the bounded buffer resources return 0 past the end
+// of each matrix. A partial last k-tile (K not a multiple of BK) must read as
+// exact zeros past K, so it goes through the guarded register path once
+// after the loop.
 // OCC: waves per SIMD the register allocation must allow (1 lets a wave use
 // all 512 registers of a lane; 2 caps it at 256 so two workgroups share a CU).
-template <int BM, int BN, int WAVES_M, int WAVES_N, int TA, int TB, int STAGES, int DMAB, int OCC>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int MR, int TA, int TB, int STAGES,
+          int DMAB, int OCC>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 sgemm_mfma_kernel(GemmParams p) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int NT = 64 * NW;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-    constexpr int MB = WM / 32, NB = WN / 32;
+    constexpr int MB = WM / MR, NB = WN / MR;
     constexpr bool A_MN = (TA == 1);  // A stored K x M
     constexpr bool B_MN = (TB == 0);  // B stored K x N
     constexpr int NS = STAGES < 2 ? 2 : STAGES;
-    using OpA = Operand<BM, WM, MB, A_MN, NT>;
-    using OpB = Operand<BN, WN, NB, B_MN, NT>;
+    using OpA = Operand<BM, WM, MB, A_MN, NT, BK, MR>;
+    using OpB = Operand<BN, WN, NB, B_MN, NT, BK, MR>;
+    using acc_t = typename Mfma<MR>::acc_t;
+    constexpr int KPL = OpA::kKPL;
+    constexpr int NREG = Mfma<MR>::kRegs;
 
     __shared__ f4 smem[NS * (OpA::kStage + OpB::kStage) / 4];
     float* sA = reinterpret_cast<float*>(smem);
@@ -292,40 +348,39 @@ sgemm_mfma_kernel(GemmParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep in SGPRs
     const int wave_m = wave / WAVES_N, wave_n = wave % WAVES_N;
-    const int li = lane & 31, lh = lane >> 5;
+    const int li = lane % MR, lh = lane / MR;
 
     const bool vec_a = p.flags & FLAG_VEC_A, vec_b = p.flags & FLAG_VEC_B;
-    const bool mn_interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
     const bool a_rows_in = m0 + BM <= p.M, b_rows_in = n0 + BN <= p.N;
 
     // This workgroup's k range: k-tiles [kt0, kt0 + kt_per_split) of K, i.e.
-    // Kp elements of k starting at kt0 * 16 (all of K without split-K).
+    // Kp elements of k starting at kt0 * BK (all of K without split-K).
     const int kt0 = (int)blockIdx.y * p.kt_per_split;
-    const int Kp = min(p.K - kt0 * kBK, p.kt_per_split * kBK);
+    const int Kp = min(p.K - kt0 * BK, p.kt_per_split * BK);
 
     // Element offset of the tile origin (row m0 / column n0, first k of the
     // range) and of one k-tile step, per operand.
-    const int64_t a_kstep = A_MN ? (int64_t)kBK * p.lda : (int64_t)kBK;
-    const int64_t b_kstep = B_MN ? (int64_t)kBK * p.ldb : (int64_t)kBK;
+    const int64_t a_kstep = A_MN ? (int64_t)BK * p.lda : (int64_t)BK;
+    const int64_t b_kstep = B_MN ? (int64_t)BK * p.ldb : (int64_t)BK;
     const int64_t a_org = (A_MN ? (int64_t)m0 : (int64_t)m0 * p.lda) + kt0 * a_kstep;
     const int64_t b_org = (B_MN ? (int64_t)n0 : (int64_t)n0 * p.ldb) + kt0 * b_kstep;
 
-    f16v acc[MB][NB];
+    acc_t acc[MB][NB];
 #pragma unroll
     for (int a = 0; a < MB; ++a)
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+            for (int r = 0; r < NREG; ++r) acc[a][b][r] = 0.f;
 
     // Guarded register-path load of k-tile kt of the range (zero past M, N
     // and the end of the range).
     auto load_tiles = [&](OpA& opa, OpB& opb, int kt) {
-        const int k0 = kt * kBK;
+        const int k0 = kt * BK;
         const int64_t ao = a_org + kt * a_kstep, bo = b_org + kt * b_kstep;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + ao, p.a_extent - ao);
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + bo, p.b_extent - bo);
-        const bool k_in = k0 + kBK <= Kp;
+        const bool k_in = k0 + BK <= Kp;
         const int k_left = Kp - k0;
         if constexpr (A_MN)
             opa.load(ra, vec_a && k_in && a_rows_in, vec_a, k_left, p.M - m0);
@@ -338,10 +393,11 @@ sgemm_mfma_kernel(GemmParams p) {
     };
 
     if constexpr (STAGES >= 3) {
-        using DA = DmaOperand<BM, WM, MB, A_MN, NW, DMAB>;
-        using DB = DmaOperand<BN, WN, NB, B_MN, NW, DMAB>;
+        using DA = DmaOperand<BM, WM, MB, A_MN, NW, DMAB, BK, MR>;
+        using DB = DmaOperand<BN, WN, NB, B_MN, NW, DMAB, BK, MR>;
         constexpr int NI = DA::kPerWave + DB::kPerWave;  // DMA ops per wave per k-tile
-        const int nk = Kp / kBK;                          // full k-tiles
+        static_assert((NS - 3) * NI < 64, "loads left in flight must fit the vmcnt field");
+        const int nk = Kp / BK;                           // full k-tiles
         DA da;
         DB db;
         da.init(wave, lane, p.lda);
@@ -364,7 +420,7 @@ sgemm_mfma_kernel(GemmParams p) {
         wait_vm_lds<(NS - 3) * NI>();
         barrier_no_fence();
 
-        float f0a[kBK / 2][MB], f0b[kBK / 2][NB], f1a[kBK / 2][MB], f1b[kBK / 2][NB];
+        float f0a[KPL][MB], f0b[KPL][NB], f1a[KPL][MB], f1b[KPL][NB];
         OpA::read_frags(sA, wave_m * WM, li, lh, f0a);
         OpB::read_frags(sB, wave_n * WN, li, lh, f0b);
 
@@ -374,25 +430,26 @@ sgemm_mfma_kernel(GemmParams p) {
         // (t+NS-1)%NS last held k-tile t-1, whose fragments were read in
         // iteration t-2: the barriers closing iterations t-2 and t-1 separate
         // those reads from this DMA. The closing wait leaves k-tile t+NS-1's
-        // DMA in flight and completes k-tile t+2 (read in iteration t+1).
-        auto step = [&](int t, float (&ca)[kBK / 2][MB], float (&cb)[kBK / 2][NB],
-                        float (&na)[kBK / 2][MB], float (&nb)[kBK / 2][NB]) {
+        // DMA in flight (none when NS = 3) and completes k-tile t+2 (read in
+        // iteration t+1).
+        auto step = [&](int t, float (&ca)[KPL][MB], float (&cb)[KPL][NB],
+                        float (&na)[KPL][MB], float (&nb)[KPL][NB]) {
             const int st = (t + 1) % NS;
-            mfma_kstep<MB, NB>(acc, ca, cb, 0);
+            mfma_kstep<MR, MB, NB, KPL>(acc, ca, cb, 0);
             issue(t + NS - 1);
-            mfma_kstep<MB, NB>(acc, ca, cb, 1);
+            mfma_kstep<MR, MB, NB, KPL>(acc, ca, cb, 1);
             OpA::read_frags(sA + st * OpA::kStage, wave_m * WM, li, lh, na);
             OpB::read_frags(sB + st * OpB::kStage, wave_n * WN, li, lh, nb);
 #pragma unroll
-            for (int s = 2; s < kBK / 2; ++s) mfma_kstep<MB, NB>(acc, ca, cb, s);
+            for (int s = 2; s < KPL; ++s) mfma_kstep<MR, MB, NB, KPL>(acc, ca, cb, s);
             // Issue order for the scheduler: the DMA loads spread over the
             // first MFMAs, then the fragment reads one per MFMA, then the rest
             // of the MFMAs, so that the reads have landed long before the
-            // closing wait and the matrix core never waits on memory.
-            // Small wave tiles (32 x 32) have fewer MFMAs than memory
-            // instructions per k-tile; there the compiler's order stands.
-            constexpr int kMfma = (kBK / 2) * MB * NB;
-            constexpr int kReads = read_count<MB, A_MN>() + read_count<NB, B_MN>();
+            // closing wait and the matrix core never waits on memory. Where
+            // a k-tile has fewer MFMAs than memory instructions the
+            // compiler's order stands.
+            constexpr int kMfma = KPL * MB * NB;
+            constexpr int kReads = OpA::kReads + OpB::kReads;
             if constexpr (NI + kReads <= kMfma) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
@@ -418,7 +475,7 @@ sgemm_mfma_kernel(GemmParams p) {
         if (t < nk) step(t, f0a, f0b, f1a, f1b);
         wait_vm_lds<0>();  // no DMA (not even an empty one) outlives the loop
 
-        if (Kp % kBK) {
+        if (Kp % BK) {
             // Partial last k-tile: every wave has finished its DMA and LDS reads
             // (waited above); the barrier makes that true for all of them
             // before buffer 0 is rewritten.
@@ -433,10 +490,10 @@ sgemm_mfma_kernel(GemmParams p) {
             __syncthreads();
             OpA::read_frags(sA, wave_m * WM, li, lh, f0a);
             OpB::read_frags(sB, wave_n * WN, li, lh, f0b);
-            mfma_ktile<MB, NB>(acc, f0a, f0b);
+            mfma_ktile<MR, MB, NB, KPL>(acc, f0a, f0b);
         }
     } else {
-        const int nk = (Kp + kBK - 1) / kBK;
+        const int nk = (Kp + BK - 1) / BK;
         OpA opa;
         OpB opb;
         opa.init(tid, p.lda);
@@ -452,10 +509,10 @@ sgemm_mfma_kernel(GemmParams p) {
 
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
-            float fa[kBK / 2][MB], fb[kBK / 2][NB];
+            float fa[KPL][MB], fb[KPL][NB];
             OpA::read_frags(sA + cur * OpA::kStage, wave_m * WM, li, lh, fa);
             OpB::read_frags(sB + cur * OpB::kStage, wave_n * WN, li, lh, fb);
-            mfma_ktile<MB, NB>(acc, fa, fb);
+            mfma_ktile<MR, MB, NB, KPL>(acc, fa, fb);
             if (kt + 1 < nk) {
                 opa.store_lds(sA + (cur ^ 1) * OpA::kStage);
                 opb.store_lds(sB + (cur ^ 1) * OpB::kStage);
@@ -469,12 +526,12 @@ sgemm_mfma_kernel(GemmParams p) {
     // FLAG_EPI C = act(alpha * r_i * c_j * acc + beta * C + u_i + w_j). Wide
     // stores carry the non-temporal hint: C is written once (16384^2 x 256,
     // which writes 1 GiB of C: 1.122 -> 1.079 ms).
-    // Accumulator register r of a 32x32 block, lane (i = lane%32, h = lane/32),
-    // holds block row 8*(r/4) + 4*h + r%4 and block column i.
+    // Accumulator register r of a block, lane (i = lane % MR, h = lane / MR),
+    // holds block row Mfma<MR>::row(r, h) and block column i.
     // Lane position again from the hardware lane id (v_mbcnt): keeping the
     // earlier values live across the main loop cost a register spill.
     const int elane = (int)__lane_id();
-    const int eli = elane & 31, elh = elane >> 5;
+    const int eli = elane % MR, elh = elane / MR;
     // C, this split's slice of C, or (FLAG_TILE_WS) this tile's and split's
     // own BM x BN slot, addressed tile-locally with ldc = BN.
     const bool tile_ws = p.flags & FLAG_TILE_WS;
@@ -502,8 +559,8 @@ sgemm_mfma_kernel(GemmParams p) {
 #pragma unroll
         for (int a = 0; a < MB; ++a) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int brow = 8 * (r / 4) + 4 * elh + (r % 4);
+            for (int r = 0; r < NREG; ++r) {
+                const int brow = Mfma<MR>::row(r, elh);
                 const int row = wave_m * WM + MB * brow + a;
                 if (m0 + row >= p.M) continue;
                 const uint32_t off = (uint32_t)(row * p.ldc + col0) * 4u;
@@ -573,8 +630,8 @@ sgemm_mfma_kernel(GemmParams p) {
 #pragma unroll
             for (int a = 0; a < MB; ++a) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int brow = 8 * (r / 4) + 4 * elh + (r % 4);
+                for (int r = 0; r < NREG; ++r) {
+                    const int brow = Mfma<MR>::row(r, elh);
                     const int row = wave_m * WM + MB * brow + a;
                     if (m0 + row >= p.M) continue;
                     const uint32_t off = (uint32_t)(row * p.ldc + col0) * 4u;
@@ -622,74 +679,22 @@ sgemm_mfma_kernel(GemmParams p) {
             default: store_tile(ActTag<ACT_NONE>{}); break;
         }
     }
-    (void)mn_interior;
 }
 
-// Grid: x = tiles (all of them unless given), y = split-K slices.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int DMAB = 16, int OCC = 1>
-hipError_t launch_shape(int ta, int tb, const GemmParams& p, hipStream_t s, int32_t tiles = -1,
-                        int32_t splits = -1) {
+// Launch of one instance for one operand layout. Grid: x = tiles (all of
+// them unless given), y = split-K slices.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int MR, int STAGES, int DMAB, int OCC,
+          int TA, int TB>
+hipError_t launch_layout(const GemmParams& p, hipStream_t s, int32_t tiles, int32_t splits) {
     const dim3 grid(tiles >= 0 ? tiles : p.tiles_m * p.tiles_n,
                     splits >= 0 ? splits
-                                : (p.K + kBK * p.kt_per_split - 1) / (kBK * p.kt_per_split)),
+                                : (p.K + BK * p.kt_per_split - 1) / (BK * p.kt_per_split)),
         block(64 * WAVES_M * WAVES_N);
-    if (ta == 0 && tb == 0)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 0, STAGES, DMAB, OCC>), grid, block, 0, s, p);
-    else if (ta == 0 && tb == 1)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 0, 1, STAGES, DMAB, OCC>), grid, block, 0, s, p);
-    else if (ta == 1 && tb == 0)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 0, STAGES, DMAB, OCC>), grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL((sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, 1, 1, STAGES, DMAB, OCC>), grid, block, 0, s, p);
+    hipLaunchKernelGGL(
+        (sgemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, BK, MR, TA, TB, STAGES, DMAB, OCC>), grid,
+        block, 0, s, p);
     return hipGetLastError();
 }
 
-}  // namespace
-
-// Variants (must match the MFMA rows of the configuration table):
-//   0: 256 x 256, 2 x 2 waves of 128 x 128, 2 stages (register staged)
-//   1: 256 x 128, 2 x 1 waves of 128 x 128, 2 stages
-//   2: 128 x 128, 1 wave  of 128 x 128,     2 stages
-//   3:  64 x 128, 1 wave  of  64 x 128,     2 stages
-//   4:  32 x 128, 1 wave  of  32 x 128,     2 stages
-//   5: 256 x 256, 2 x 2 waves of 128 x 128, 4-stage direct-to-LDS ring
-//   6: 256 x 128, 2 x 1 waves of 128 x 128, 3-stage direct-to-LDS ring
-//   7: 128 x 128, 2 x 2 waves of  64 x  64, 4-stage direct-to-LDS ring
-//   8: as 7 with 4-byte direct-to-LDS loads (rows of any alignment)
-//   9: 256 x 256, 4 x 2 waves of  64 x 128, 4-stage direct-to-LDS ring
-//      (two waves per SIMD)
-//  10: 256 x 128, 2 x 2 waves of 128 x  64, 3-stage direct-to-LDS ring
-//      (two workgroups per CU)
-//  11:  64 x  64, 2 x 2 waves of  32 x  32, 4-stage direct-to-LDS ring
-//      (several workgroups per CU: grids too small for the large tiles)
-//  12: as 11 with 4-byte direct-to-LDS loads
-//  13: 128 x  64, 2 x 2 waves of  64 x  32, 4-stage direct-to-LDS ring
-//  14: 128 x 128, 4 x 2 waves of  32 x  64, 4-stage direct-to-LDS ring
-//      (two waves per SIMD from one workgroup per CU)
-hipError_t launch_mfma(int variant, int ta, int tb, const GemmParams& p, hipStream_t s) {
-    return launch_mfma_tiles(variant, ta, tb, p, -1, -1, s);
-}
-
-hipError_t launch_mfma_tiles(int variant, int ta, int tb, const GemmParams& p, int32_t tiles,
-                             int32_t splits, hipStream_t s) {
-    switch (variant) {
-        case 0: return launch_shape<256, 256, 2, 2, 2>(ta, tb, p, s, tiles, splits);
-        case 1: return launch_shape<256, 128, 2, 1, 2>(ta, tb, p, s, tiles, splits);
-        case 2: return launch_shape<128, 128, 1, 1, 2>(ta, tb, p, s, tiles, splits);
-        case 3: return launch_shape<64, 128, 1, 1, 2>(ta, tb, p, s, tiles, splits);
-        case 4: return launch_shape<32, 128, 1, 1, 2>(ta, tb, p, s, tiles, splits);
-        case 5: return launch_shape<256, 256, 2, 2, 4>(ta, tb, p, s, tiles, splits);
-        case 6: return launch_shape<256, 128, 2, 1, 3>(ta, tb, p, s, tiles, splits);
-        case 7: return launch_shape<128, 128, 2, 2, 4>(ta, tb, p, s, tiles, splits);
-        case 8: return launch_shape<128, 128, 2, 2, 4, 4>(ta, tb, p, s, tiles, splits);
-        case 9: return launch_shape<256, 256, 4, 2, 4>(ta, tb, p, s, tiles, splits);
-        case 10: return launch_shape<256, 128, 2, 2, 3, 16, 2>(ta, tb, p, s, tiles, splits);
-        case 11: return launch_shape<64, 64, 2, 2, 4, 16, 2>(ta, tb, p, s, tiles, splits);
-        case 12: return launch_shape<64, 64, 2, 2, 4, 4, 2>(ta, tb, p, s, tiles, splits);
-        case 13: return launch_shape<128, 64, 2, 2, 4, 16, 2>(ta, tb, p, s, tiles, splits);
-        case 14: return launch_shape<128, 128, 4, 2, 4, 16, 2>(ta, tb, p, s, tiles, splits);
-        default: return hipErrorInvalidValue;
-    }
-}
-
+}  // namespace mfma
 }  // namespace fg

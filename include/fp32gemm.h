@@ -10,7 +10,8 @@
  * B, ldB, beta, C, ldC, stream), extended by the two transpose flags.
  *
  * Arithmetic: binary32 inputs, binary32 products and accumulation on the
- * matrix cores (v_mfma_f32_32x32x2_f32) or on the vector ALU, binary32
+ * matrix cores (v_mfma_f32_32x32x2_f32, v_mfma_f32_16x16x4_f32) or on the
+ * vector ALU, binary32
  * output. Nothing is converted to a narrower format.
  *
  * Storage convention: ROW-MAJOR with explicit leading dimensions (elements).
@@ -62,7 +63,8 @@ typedef enum fg_status {
 
 /* Kernel families. */
 typedef enum fg_kind {
-    FG_KIND_MFMA = 1,  /* matrix-core contraction, v_mfma_f32_32x32x2_f32 */
+    FG_KIND_MFMA = 1,  /* matrix-core contraction, v_mfma_f32_32x32x2_f32 or
+                          v_mfma_f32_16x16x4_f32 (fg_config.mr) */
     FG_KIND_VALU = 2,  /* vector-ALU v_fma_f32 outer products (comparison path) */
     FG_KIND_SKINNY = 3 /* few rows of C: streams op(B) once per block of up to 8
                           rows, memory-bound (the GEMV shape) */
@@ -83,6 +85,9 @@ typedef struct fg_config {
     int32_t threads;   /* work-items per workgroup */
     int32_t stages;    /* LDS buffers in the k-tile ring */
     int32_t lds_bytes; /* LDS per workgroup */
+    int32_t mr;        /* FG_KIND_MFMA: edge of the instruction's output block,
+                          32 (v_mfma_f32_32x32x2_f32) or 16
+                          (v_mfma_f32_16x16x4_f32); 0 for the other kinds */
     char name[40];
 } fg_config;
 
@@ -139,7 +144,8 @@ fg_status fg_sgemm_ex(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t 
  * Arguments 1-13 as for fg_sgemm, then:
  *   14 splits          : 0 = choose (at most what the workspace holds),
  *                        1 = no split (same as fg_sgemm), S > 1 = S slices
- *                        (capped at the number of 16-deep k-tiles)
+ *                        (capped at the number of k-tiles of the
+ *                        entry used)
  *   15 workspace       : device memory owned by the caller, 4-byte aligned
  *                        (16-byte alignment enables 128-bit accesses); may be
  *                        NULL when splits == 1 (or splits == 0: then no split)

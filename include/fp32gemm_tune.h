@@ -12,8 +12,8 @@
  * module from timings of every entry on a grid of shapes), following the
  * empirical configuration search of "How to get a matmul kernel into the
  * top percentile (worklog)", section "Extra" (retune per GPU) and "Matmul
- * II: register blocking, warp tiling, tensor cores", section 8 (many
- * variants and a heuristic that picks one per call).
+ * II: register blocking, warp tiling, tensor cores", section 8 (a library
+ * carries a family of tile variants and chooses one per shape).
  *
  * Errors as in fp32gemm.h: fg_last_bad_arg() / fg_last_error().
  */
@@ -47,6 +47,24 @@ fg_status fg_get_efficiency(int32_t config_id, double* eff, double* eff1);
  * tuners: a production build takes its values from fg_tuned.inc.
  */
 fg_status fg_set_efficiency(int32_t config_id, double eff, double eff1);
+
+/*
+ * Raster order of the matrix-core kernels for every later call in this
+ * process (for measurements, e.g. of how much each part of the order saves;
+ * the defaults are what the library is tuned with):
+ *   1 group_m   : output tiles are visited in bands of group_m tile rows,
+ *                 column by column inside a band (0 = the default, 4;
+ *                 1 = plain row-major order); at most 4096
+ *   2 xcd_remap : 1 (default) renumbers workgroups so that each of the 8
+ *                 XCDs receives a contiguous run of tiles (when the grid is a
+ *                 multiple of 8); 0 keeps the hardware's round-robin order
+ * Process-wide; FG_ERR_INVALID_ARG outside these ranges. Results do not
+ * depend on it (every tile computes the same sums in any order).
+ */
+fg_status fg_set_raster(int32_t group_m, int32_t xcd_remap);
+
+/* The current raster settings (arguments 1, 2: outputs, non-NULL). */
+fg_status fg_get_raster(int32_t* group_m, int32_t* xcd_remap);
 
 /*
  * When fg_sgemm_streamk splits the last, partial round of tiles: policy 0
