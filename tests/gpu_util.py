@@ -66,6 +66,55 @@ def check_full(w, A, B, C, out):
     return info
 
 
+def row_blocks(M, block):
+    for r0 in range(0, M, block):
+        yield np.arange(r0, min(M, r0 + block), dtype=np.int64)
+
+
+class FullCheck:
+    """Every element of a large result against the oracle, one block of rows
+    at a time (host memory stays bounded): the per-element bound on each
+    block, the relative Frobenius bound on the whole result."""
+
+    def __init__(self, name):
+        self.name = name
+        self.n = self.n_bad = 0
+        self.worst = 0.0
+        self.worst_at = None
+        self.err2 = self.ref2 = 0.0
+
+    def add(self, rows, info):
+        self.n += info["n"]
+        self.n_bad += info["n_bad"]
+        if info["max_err_over_tol"] > self.worst:
+            self.worst = info["max_err_over_tol"]
+            i, j = info["worst_index"]
+            self.worst_at = (int(rows[i]), int(j))
+        self.err2 += info["frob_abs"] ** 2
+        self.ref2 += info["frob_ref"] ** 2
+
+    def finish(self):
+        frob = (self.err2 ** 0.5) / (self.ref2 ** 0.5) if self.ref2 > 0 else self.err2 ** 0.5
+        info = {"n": self.n, "n_bad": self.n_bad, "max_err_over_tol": self.worst,
+                "worst_index": self.worst_at, "frob_rel": frob}
+        log(f"  {self.name}: all {self.n} elements, max err/tol {self.worst:.3g} at "
+            f"{self.worst_at}, frob_rel {frob:.3g}, {self.n_bad} outside the bound")
+        assert self.n_bad == 0 and frob <= compare.FROB_REL, (self.name, info)
+        return info
+
+
+def check_full_blocked(w, A, B, C, out, block=1024, name=None):
+    """check_full for results too large to hold the whole oracle at once."""
+    fc = FullCheck(name or getattr(w, "name", "result"))
+    for rows in row_blocks(w.M, block):
+        cref, s = oracle.gemm_rows(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A, w.LDA, B,
+                                   w.LDB, w.beta, C, w.LDC, rows=rows)
+        cin = C[rows, :w.N] if (C is not None and w.beta != 0) else None
+        _, info = compare.check(out[rows], cref, s, w.K, w.alpha, w.beta, cin, frob=True)
+        fc.add(rows, info)
+    return fc.finish()
+
+
 def check_sampled(w, A, B, C, out, n=4000, seed=99, rows=(0, -1)):
     """Oracle at a seeded sample of elements plus a few whole rows."""
     ii, jj = workloads.sample_indices(w.M, w.N, n, seed=seed)

@@ -14,7 +14,7 @@ from fp32_gemm_tile_amd import workloads
 import oracle
 from oracle import compare
 from oracle import epilogue as ep
-from gpu_util import log, to_device
+from gpu_util import FullCheck, log, row_blocks, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -151,21 +151,27 @@ def test_fused_without_epilogue_equals_plain_call():
     assert np.array_equal(outs[0], outs[1])
 
 
-def test_fused_large_sampled():
+def test_fused_large_full():
     """8192^3 NN with every vector and gelu, in the launch configuration the
-    bench times, checked on a seeded sample of elements."""
+    bench times, every element against the epilogue oracle (row blocks)."""
     w = workloads.WORKLOADS["C5a"]
     A, B, _ = workloads.make_inputs(w)
     vecs = _vectors(np.random.default_rng(65), w.M, w.N)
     out = run_fused(w, A, B, None, vecs, "gelu")
-    ii, jj = workloads.sample_indices(w.M, w.N, 3000, seed=66)
-    s, S = oracle.gemm_elems(w.transA, w.transB, w.M, w.N, w.K, 1.0, A, w.LDA, B, w.LDB, 0.0,
-                             None, w.LDC, ii, jj)
-    d, v = ep.epilogue_elems(s, w.alpha, w.beta, None, ii, jj, *vecs, act="gelu")
-    gathered = [vecs[0][ii], vecs[1][jj], vecs[2][ii], vecs[3][jj]]
-    ok, info = compare.check_epilogue(out[ii, jj], d, v, S, w.K, w.alpha, w.beta, None,
-                                      *gathered, act="gelu", per_element=True)
-    assert ok, info
+    assert np.all(np.isfinite(out))
+    fc = FullCheck("fused 8192^3 gelu")
+    for rows in row_blocks(w.M, 1024):
+        s, S = oracle.gemm_rows(w.transA, w.transB, w.M, w.N, w.K, 1.0, A, w.LDA, B, w.LDB,
+                                0.0, None, w.LDC, rows=rows)
+        bv = [vecs[0][rows], vecs[1], vecs[2][rows], vecs[3]]
+        d, v = ep.epilogue(s, w.alpha, w.beta, None, *bv, act="gelu")
+        ok, info = compare.check_epilogue(out[rows], d, v, S, w.K, w.alpha, w.beta, None, *bv,
+                                          act="gelu", frob=False)
+        diff = out[rows].astype(np.float64) - d
+        info["frob_abs"] = float(np.linalg.norm(diff))
+        info["frob_ref"] = float(np.linalg.norm(d))
+        fc.add(rows, info)
+    fc.finish()
 
 
 def test_torch_wrapper_fused():

@@ -12,7 +12,7 @@ import fp32_gemm_tile_amd as fg
 from fp32_gemm_tile_amd import workloads as wl
 import oracle
 
-from gpu_util import check_full, check_sampled, log, run_fg
+from gpu_util import check_full, check_full_blocked, log, run_fg
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,13 @@ def all_ids():
     return [c["id"] for c in _configs()]
 
 
+def config_id(name):
+    return next(c["id"] for c in fg.configs() if c["name"] == name)
+
+
+HEADLINE = "mfma_256x256x16_w2x2_s4"  # the entry the 4096^3 and 8192^3 workloads run
+
+
 # --- the workloads the metric and the parity cases are quoted on ----------
 
 @pytest.mark.parametrize("name", ["C1", "C2", "C3"])
@@ -57,13 +64,38 @@ def test_workload_full_oracle(name):
 
 
 @pytest.mark.parametrize("name", ["C4", "C5a", "C5b", "C6"])
-def test_workload_sampled_oracle(name):
+def test_workload_full_oracle_large(name):
+    """The large workloads in the launch configuration the bench times
+    (automatic selection), every element against the oracle (in row blocks);
+    C starts as NaN, so an element never written fails too."""
     w = wl.WORKLOADS[name]
     A, B, C = wl.make_inputs(w)
     out, _ = run_fg(w, A, B, C)
     assert np.all(np.isfinite(out))
-    info = check_sampled(w, A, B, C, out)
-    log(f"  {name}: sampled max err/tol {info['max_err_over_tol']:.3g}")
+    check_full_blocked(w, A, B, C, out)
+
+
+@pytest.mark.parametrize("cfg", [-1, HEADLINE])
+@pytest.mark.parametrize("ta,tb", OPS)
+def test_layouts_4096_cubed_full(ta, tb, cfg):
+    """4096^3 in all four layouts, with the automatic pick and with the
+    headline entry forced (a grid of 256 tiles: the XCD renumbering is
+    active), every element against the oracle."""
+    w = wl.custom(4096, 4096, 4096, ta, tb, seed=50 + 2 * (ta == "T") + (tb == "T"))
+    A, B, _ = wl.make_inputs(w)
+    out, _ = run_fg(w, A, B, config=-1 if cfg == -1 else config_id(cfg))
+    check_full_blocked(w, A, B, None, out, name=f"4096^3 {ta}{tb} cfg={cfg}")
+
+
+@pytest.mark.parametrize("ta,tb", OPS)
+def test_headline_entry_remapped_grid(ta, tb):
+    """The headline entry on 2048 x 2048 x 512 (64 tiles, a multiple of 8:
+    XCD renumbering on) with alpha/beta, every element."""
+    w = wl.custom(2048, 2048, 512, ta, tb, alpha=0.75, beta=-1.25, dist="normal",
+                  seed=60 + 2 * (ta == "T") + (tb == "T"))
+    A, B, C = wl.make_inputs(w)
+    out, _ = run_fg(w, A, B, C, config=config_id(HEADLINE))
+    check_full(w, A, B, C, out)
 
 
 # --- exactness on integer-valued inputs: catches layout/predication bugs ---
@@ -262,11 +294,11 @@ def test_error_statistics_are_fp32_scale():
 
 
 @pytest.mark.parametrize("cfg", all_ids())
-def test_every_config_at_4096_cubed_sampled(cfg):
-    """Every table entry, forced, on the 4096^3 workload (sampled oracle):
-    the comparison paths must compute the whole product too."""
+def test_every_config_at_4096_cubed(cfg):
+    """Every table entry, forced, on the 4096^3 workload, every element
+    against the oracle: the comparison paths compute the whole product too."""
     w = wl.WORKLOADS["C6"]
     A, B, C = wl.make_inputs(w)
     out, _ = run_fg(w, A, B, C, config=cfg)
     assert np.all(np.isfinite(out))
-    check_sampled(w, A, B, C, out, n=3000, seed=cfg, rows=(0, 4095, 2049))
+    check_full_blocked(w, A, B, C, out, name=f"C6 cfg={cfg}")
