@@ -105,6 +105,10 @@ def load_library(path: str = LIB_PATH):
     lib.fg_sgemm_ex.restype = i32
     lib.fg_sgemm_splitk.argtypes = gemm_args[:13] + [i32, vp, ctypes.c_size_t, vp]
     lib.fg_sgemm_splitk.restype = i32
+    lib.fg_sgemm_splitk_noalloc.argtypes = gemm_args[:13] + [i32, vp]
+    lib.fg_sgemm_splitk_noalloc.restype = i32
+    lib.fg_sgemm_splitk_noalloc_max_bytes.argtypes = []
+    lib.fg_sgemm_splitk_noalloc_max_bytes.restype = ctypes.c_size_t
     lib.fg_sgemm_splitk_workspace_size.argtypes = [i64, i64, i32]
     lib.fg_sgemm_splitk_workspace_size.restype = ctypes.c_size_t
     lib.fg_num_configs.argtypes = []
@@ -189,6 +193,19 @@ def fg_sgemm_splitk(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc
     return load_library().fg_sgemm_splitk(_op(transA), _op(transB), M, N, K, alpha, A, lda,
                                           B, ldb, beta, C, ldc, splits, workspace or None,
                                           workspace_bytes, stream or None)
+
+
+def fg_sgemm_splitk_noalloc(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                            splits, stream=0):
+    """Split-K with the library's own device-resident scratch (no workspace
+    argument, nothing allocated); see include/fp32gemm.h."""
+    return load_library().fg_sgemm_splitk_noalloc(_op(transA), _op(transB), M, N, K, alpha, A,
+                                                  lda, B, ldb, beta, C, ldc, splits,
+                                                  stream or None)
+
+
+def fg_sgemm_splitk_noalloc_max_bytes() -> int:
+    return load_library().fg_sgemm_splitk_noalloc_max_bytes()
 
 
 def fg_sgemm_splitk_workspace_size(M, N, splits) -> int:

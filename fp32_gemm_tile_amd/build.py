@@ -33,7 +33,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp32gemm.so")
 INSTANCES = os.path.join(CSRC, "fg_mfma_instances.inc")
 SOURCES = ["fg_api.cpp", "fg_mfma_dispatch.cpp", "sgemm_valu.hip", "sgemm_skinny.hip",
-           "fg_elementwise.hip", "fg_probe.hip"]
+           "fg_elementwise.hip", "fg_probe.hip", "fg_noalloc.hip"]
 ENTRY_FIELDS = ("id", "bm", "bn", "waves_m", "waves_n", "bk", "mr", "stages", "dmab", "occ",
                 "wps", "fallback")
 

@@ -697,6 +697,38 @@ fg_status fg_sgemm_splitk(fg_op transA, fg_op transB, int64_t M, int64_t N, int6
                     splits, (float*)workspace, workspace ? workspace_bytes : 0);
 }
 
+fg_status fg_sgemm_splitk_noalloc(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                                  float alpha, const float* A, int64_t lda, const float* B,
+                                  int64_t ldb, float beta, float* C, int64_t ldc, int32_t splits,
+                                  hipStream_t stream) {
+    clear_error();
+    if (splits < 0) return fail(FG_ERR_INVALID_ARG, 14, "splits < 0");
+    // Requests that cannot fit are refused before any device call.
+    const size_t cap = FG_NOALLOC_SCRATCH_MAX;
+    if (splits > 1 && M > 0 && N > 0 &&
+        (double)M * (double)N * (double)splits * sizeof(float) > (double)cap)
+        return fail(FG_ERR_INVALID_ARG, 14,
+                    "%d slices of %lld x %lld floats need %.0f bytes of scratch; at most %zu",
+                    splits, (long long)M, (long long)N,
+                    (double)M * (double)N * (double)splits * sizeof(float), cap);
+    fg_status s = validate(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
+    if (s != FG_OK) return s;
+    if (splits == 1 || M == 0 || N == 0 || K == 0 || alpha == 0.0f)
+        return run_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1,
+                        1, nullptr, 0);
+    s = check_device();
+    if (s != FG_OK) return s;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    const hipError_t e = fg::noalloc_scratch(&ws, &ws_bytes);
+    if (e != hipSuccess)
+        return fail(FG_ERR_HIP, 0, "scratch address: %s", hipGetErrorString(e));
+    return run_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1,
+                    splits, (float*)ws, ws_bytes);
+}
+
+size_t fg_sgemm_splitk_noalloc_max_bytes(void) { return FG_NOALLOC_SCRATCH_MAX; }
+
 size_t fg_sgemm_streamk_workspace_size(fg_op transA, fg_op transB, int64_t M, int64_t N,
                                        int64_t K, const float* A, int64_t lda, const float* B,
                                        int64_t ldb) {

@@ -84,6 +84,11 @@ hipError_t launch_splitk_reduce(const float* W, int32_t splits, const GemmParams
 // written by an FLAG_TILE_WS launch (summed in ascending s).
 hipError_t launch_tile_reduce(const float* W, int32_t splits, int32_t count, int32_t bm,
                               int32_t bn, const GemmParams& p, hipStream_t stream);
+// Device address (this device's copy) and size of the scratch of
+// fg_sgemm_splitk_noalloc (FG_NOALLOC_SCRATCH_MAX bytes), looked up
+// once per device with the device current (fg_noalloc.hip).
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 // Machine probes (fg_probe.hip): an MFMA-only loop and a streaming read.
 hipError_t launch_probe_mfma(int workgroups, int iters, float* out, hipStream_t stream);
 hipError_t launch_probe_read(const float* x, int64_t n4, int workgroups, float* out,

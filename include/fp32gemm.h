@@ -161,6 +161,37 @@ fg_status fg_sgemm_splitk(fg_op transA, fg_op transB, int64_t M, int64_t N, int6
                           float* C, int64_t ldc, int32_t splits,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * fg_sgemm_splitk_noalloc: fg_sgemm_splitk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The partial slices go to a scratch array that is
+ * part of the library's device code: each GPU the library runs on holds one
+ * copy of FG_NOALLOC_SCRATCH_MAX bytes from module load until the process
+ * ends. The call itself allocates and frees nothing (no hipMalloc, no
+ * library routine that allocates).
+ *
+ * Arguments 1-13 as for fg_sgemm, then:
+ *   14 splits : 0 = choose (at most what the scratch holds), 1 = no split,
+ *               S > 1 = S slices; M * N * S * 4 bytes above
+ *               FG_NOALLOC_SCRATCH_MAX is FG_ERR_INVALID_ARG (bad argument
+ *               14), reported before any device call
+ *   15 stream
+ * Results are those of fg_sgemm_splitk with the same split count.
+ * Sharing: every call on one GPU uses that GPU's single scratch array, which
+ * keeps the last call's partial sums (each call writes every slice element
+ * it reads back, so nothing needs clearing). Calls that can overlap on one
+ * GPU -- on different streams, or from different host threads without
+ * ordering -- race on it; serialise them (one stream, or events).
+ */
+#define FG_NOALLOC_SCRATCH_MAX (32u << 20)
+fg_status fg_sgemm_splitk_noalloc(fg_op transA, fg_op transB, int64_t M, int64_t N,
+                                  int64_t K, float alpha, const float* A, int64_t lda,
+                                  const float* B, int64_t ldb, float beta,
+                                  float* C, int64_t ldc, int32_t splits, hipStream_t stream);
+
+/* FG_NOALLOC_SCRATCH_MAX as the library was built with it. Host only. */
+size_t fg_sgemm_splitk_noalloc_max_bytes(void);
+
 /* Activations of the fused epilogue (binary32). */
 typedef enum fg_activation {
     FG_ACT_NONE = 0,

@@ -392,6 +392,22 @@ def test_no_kernel_uses_scratch_memory():
     assert max(sizes) == 0
 
 
+def test_noalloc_limits_need_no_gpu():
+    """fg_sgemm_splitk_noalloc refuses splits that do not fit its scratch
+    before any device call; the limit is the one the header states."""
+    cap = fg.fg_sgemm_splitk_noalloc_max_bytes()
+    assert cap == 32 << 20
+    call = lambda M, N, s: fg.fg_sgemm_splitk_noalloc(0, 0, M, N, 64, 1.0, 16, 64, 16, N, 0.0,
+                                                      16, N, s, 0)
+    assert call(2048, 2048, 3) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 14
+    assert call(64, 64, -1) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 14
+    assert call(0, 64, 4) == fg.FG_OK  # nothing to compute
+    run_without_gpu("""
+st = fg.fg_sgemm_splitk_noalloc(0, 0, 1024, 1024, 64, 1.0, 16, 64, 16, 1024, 0.0, 16, 1024, 8, 0)
+assert st in NO_DEVICE, st
+""")
+
+
 def test_raster_setting_validation():
     """fg_set_raster changes the tile order only through an explicit call;
     nothing in the environment does."""
