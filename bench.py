@@ -16,7 +16,8 @@ MFMA and HBM-read rates with the library's probe kernels.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C5a]
                        [--suite] [--calibrate] [--splitk [S]] [--streamk] [--cold]
-                       [--no-cpu] [--no-probes] [--copy-probe]
+                       [--no-cpu] [--no-probes] [--no-extras] [--copy-probe]
+                       [--config ID] [--group-m G] [--xcd-remap 0|1]
 """
 from __future__ import annotations
 
@@ -409,6 +410,13 @@ def main():
                          "(reference for scaling HBM traffic counters)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time every table entry on every workload (one line each)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="with the default workload, skip the 4096^3 and row-block lines")
+    ap.add_argument("--group-m", type=int, default=0,
+                    help="raster band height in tile rows (fg_set_raster; 0 = library default)")
+    ap.add_argument("--xcd-remap", type=int, choices=(0, 1), default=1,
+                    help="1: renumber workgroups so each XCD gets a contiguous run of tiles "
+                         "(library default); 0: hardware round-robin order")
     ap.add_argument("--splitk", type=int, nargs="?", const=-1, default=None,
                     help="time fg_sgemm_splitk (256 MiB workspace) instead of fg_sgemm; "
                          "optional value = split count (default: library-chosen)")
@@ -425,6 +433,9 @@ def main():
         sys.exit(1)
     import fp32_gemm_tile_amd as fg
     fg.load_library()
+    if fg.fg_set_raster(args.group_m, args.xcd_remap) != fg.FG_OK:
+        print(f"bench.py: {fg.fg_last_error()}", file=sys.stderr)
+        sys.exit(2)
 
     if args.suite or args.calibrate:
         ids = range(fg.fg_num_configs()) if args.calibrate else [args.config]
@@ -453,7 +464,7 @@ def main():
                 streamk=args.streamk)
     # The 4096^3 shape of the metric, and one GPU's row block of 8192^3 split
     # over eight GPUs, timed in the same run.
-    if args.workload == "C5a":
+    if args.workload == "C5a" and not args.no_extras:
         r["also"] = {}
         for extra in ("C6", "S8"):
             r2 = run_one(extra, args.steps, args.warmup, False, args.config, cold=args.cold,

@@ -103,9 +103,31 @@ def jobs() -> int:
     return max(1, min(16, n))
 
 
+def _stale(obj: str, deps: list[str]) -> bool:
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def _deps(src: str, table_files: list[str]) -> list[str]:
+    """Files an object depends on: every header of the library; the table
+    files (instance list, efficiencies) too unless it is a kernel instance
+    (whose shape comes from its -D flags)."""
+    heads = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    heads += [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))]
+    own = [src] + heads
+    return own if src.endswith("sgemm_mfma_inst.hip") else own + table_files
+
+
 def build(verbose: bool = False, instances: str = INSTANCES, tuned: str | None = None,
-          lib: str = LIB, build_dir: str = BUILD) -> str:
-    """Compile every source and every instance of `instances` and link `lib`."""
+          lib: str = LIB, build_dir: str = BUILD, layouts: dict | None = None,
+          incremental: bool = False) -> str:
+    """Compile every source and every instance of `instances` and link `lib`.
+    layouts: {entry id: [(ta, tb), ...]} builds only those operand layouts of
+    an entry (the others report hipErrorNotSupported); default all four.
+    incremental: keep objects newer than everything they depend on (the tile
+    search rebuilds its library after changing only the table)."""
     os.makedirs(build_dir, exist_ok=True)
     defs = [f'-DFG_INSTANCES_INC="{os.path.abspath(instances)}"']
     if tuned:
@@ -116,12 +138,29 @@ def build(verbose: bool = False, instances: str = INSTANCES, tuned: str | None =
                      os.path.join(build_dir, os.path.splitext(s)[0] + ".o"), defs))
     entries = read_instances(instances)
     for e in entries:
+        want = set(map(tuple, (layouts or {}).get(e["id"], [(0, 0), (0, 1), (1, 0), (1, 1)])))
+        stubs = 0
         for ta in (0, 1):
             for tb in (0, 1):
+                if (ta, tb) not in want:
+                    stubs |= 1 << (2 * ta + tb)
+                    continue
                 work.append((os.path.join(CSRC, "sgemm_mfma_inst.hip"),
                              os.path.join(build_dir, f"sgemm_mfma_e{e['id']}_{ta}{tb}.o"),
                              [f"-DFG_ENTRY_ID={e['id']}", f"-DFG_ENTRY_TA={ta}",
                               f"-DFG_ENTRY_TB={tb}", f"-DFG_ENTRY_SHAPE={shape_macro(e)}"]))
+        if stubs:
+            work.append((os.path.join(CSRC, "sgemm_mfma_inst.hip"),
+                         os.path.join(build_dir, f"sgemm_mfma_e{e['id']}_stubs.o"),
+                         [f"-DFG_ENTRY_ID={e['id']}", f"-DFG_ENTRY_STUBS={stubs}"]))
+    table_files = [os.path.abspath(instances),
+                   os.path.abspath(tuned) if tuned else os.path.join(CSRC, "fg_tuned.inc")]
+    if incremental:
+        keep = [w for w in work if not _stale(w[1], _deps(w[0], table_files))]
+        work = [w for w in work if w not in keep]
+        kept_objs = [w[1] for w in keep]
+    else:
+        kept_objs = []
     # The slowest objects first (largest tiles), so the pool drains evenly.
     work.sort(key=lambda w: -int(next((d.split("=")[1].split(",")[0] for d in w[2]
                                        if d.startswith("-DFG_ENTRY_SHAPE=")), "0")))
@@ -129,7 +168,7 @@ def build(verbose: bool = False, instances: str = INSTANCES, tuned: str | None =
         print(f"compiling {len(work)} objects ({len(entries)} matrix-core entries) "
               f"with {jobs()} jobs", flush=True)
     with cf.ThreadPoolExecutor(max_workers=jobs()) as ex:
-        objs = list(ex.map(lambda w: _compile(w[0], w[1], w[2], verbose), work))
+        objs = list(ex.map(lambda w: _compile(w[0], w[1], w[2], verbose), work)) + kept_objs
     tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:

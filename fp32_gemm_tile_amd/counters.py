@@ -1,0 +1,290 @@
+"""Hardware-counter evidence for one workload of the bench: a kernel trace and
+separate rocprofv3 counter passes, summarised per GEMM kernel.
+
+Each pass is its own run of ``bench.py`` under ``rocprofv3`` (the bench is the
+program after ``--``; counter passes never combine with tracing), bounded by
+``timeout -s KILL``:
+
+  trace   --kernel-trace --stats             average kernel duration
+  fetch   --pmc FETCH_SIZE                   HBM bytes read (KiB per dispatch)
+  write   --pmc WRITE_SIZE                   HBM bytes written
+  mfma    --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
+                SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_BUSY_CYCLES
+  lds     --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS
+                SQ_WAIT_INST_LDS
+  wait    --pmc SQ_WAIT_ANY SQ_WAVE_CYCLES SQ_WAVES SQ_INSTS_VALU
+
+The fetch and write passes end with three plain device copies of 1 GiB
+(``bench.py --copy-probe``), whose counter values give the scale from
+FETCH_SIZE / WRITE_SIZE to bytes. Derived figures:
+
+  MfmaUtil   = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs)
+  MFMA FLOP  = SQ_INSTS_VALU_MFMA_MOPS_F32 x 512
+  conflicts  = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles per active cycle)
+  wait share = SQ_WAIT_ANY / SQ_WAVE_CYCLES
+
+Usage (on the GPU machine, from the repository root):
+    python -m fp32_gemm_tile_amd.counters --workload C3 --out gpurun_out/counters_C3 \
+        [--config ID] [--group-m G] [--xcd-remap 0|1] [--passes trace fetch ...]
+    python -m fp32_gemm_tile_amd.counters --summarize gpurun_out/counters_C3
+The summary (Markdown, with the commands) is printed and written to
+``<out>/summary.md`` and ``<out>/summary.json``.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import shlex
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PASSES = {
+    "trace": ["--kernel-trace", "--stats"],
+    "fetch": ["--pmc", "FETCH_SIZE"],
+    "write": ["--pmc", "WRITE_SIZE"],
+    "mfma": ["--pmc", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE",
+             "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_BUSY_CYCLES"],
+    "lds": ["--pmc", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS",
+            "SQ_WAIT_INST_LDS"],
+    "wait": ["--pmc", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", "SQ_WAVES", "SQ_INSTS_VALU"],
+}
+COPY_KERNEL = "copyBuffer"
+SIMDS = 1024
+XCDS = 8
+
+
+def bench_args(a):
+    out = ["--workload", a.workload, "--steps", str(a.steps), "--warmup", str(a.warmup),
+           "--no-cpu", "--no-probes", "--no-extras"]
+    if a.config >= 0:
+        out += ["--config", str(a.config)]
+    if a.group_m:
+        out += ["--group-m", str(a.group_m)]
+    if a.xcd_remap != 1:
+        out += ["--xcd-remap", str(a.xcd_remap)]
+    for flag in ("splitk", "streamk"):
+        if getattr(a, flag):
+            out.append(f"--{flag}")
+    return out
+
+
+def run_pass(name, a, out_dir):
+    """One rocprofv3 run of the bench; returns the command (as a string)."""
+    d = os.path.join(out_dir, name)
+    cmd = ["timeout", "-s", "KILL", str(a.timeout), "rocprofv3", *PASSES[name],
+           "--output-format", "csv", "-d", d, "-o", "run", "--",
+           sys.executable, os.path.join(ROOT, "bench.py"), *bench_args(a)]
+    if name in ("fetch", "write"):
+        cmd.append("--copy-probe")
+    print(f"[counters] {a.workload} pass {name}", flush=True)
+    env = dict(os.environ, TMPDIR="/tmp")
+    r = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True)
+    with open(os.path.join(out_dir, f"{name}.log"), "w") as f:
+        f.write(r.stdout + "\n---- stderr ----\n" + r.stderr)
+    bench_line = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    # rocprofv3 may end with a signal after the program has finished and its
+    # files are complete; the program's own last line says whether it ran.
+    if not bench_line:
+        raise RuntimeError(f"pass {name} failed (rc {r.returncode}); see {name}.log")
+    with open(os.path.join(out_dir, f"{name}.bench.json"), "w") as f:
+        f.write(bench_line[-1] + "\n")
+    return " ".join(shlex.quote(c) for c in cmd).replace(ROOT, "$REPO")
+
+
+def _rows(pattern):
+    rows = []
+    for path in glob.glob(pattern, recursive=True):
+        with open(path, newline="") as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def counters(out_dir, name):
+    """{kernel name: {counter: mean value per dispatch}} of one pass, plus the
+    number of dispatches and grid size per kernel."""
+    per = {}
+    for r in _rows(os.path.join(out_dir, name, "**", "*counter_collection.csv")):
+        k = r.get("Kernel_Name", "")
+        d = per.setdefault(k, {"dispatches": set(), "values": {}})
+        d["dispatches"].add(r.get("Dispatch_Id"))
+        d["grid"] = int(float(r.get("Grid_Size", 0) or 0))
+        d["values"].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = {}
+    for k, d in per.items():
+        n = max(1, len(d["dispatches"]))
+        out[k] = {c: sum(v) / n for c, v in d["values"].items()}
+        out[k]["_dispatches"] = n
+        out[k]["_grid"] = d.get("grid", 0)
+    return out
+
+
+def kernel_stats(out_dir):
+    out = {}
+    for r in _rows(os.path.join(out_dir, "trace", "**", "*kernel_stats.csv")):
+        out[r["Name"]] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                          "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
+    return out
+
+
+def _gemm_kernel(table):
+    """The GEMM kernel of a pass: the one with the most dispatches among
+    those that are not the copy probe, nor torch's own fill/rand kernels."""
+    cands = {k: v for k, v in table.items()
+             if COPY_KERNEL not in k and ("fg::" in k or "sgemm" in k or "gemm" in k.lower())}
+    if not cands:
+        return None
+    return max(cands, key=lambda k: (cands[k].get("_dispatches", cands[k].get("calls", 0)),
+                                     cands[k].get("_grid", 0)))
+
+
+def summarize(out_dir):
+    meta = json.load(open(os.path.join(out_dir, "meta.json")))
+    bench = {}
+    for p in PASSES:
+        path = os.path.join(out_dir, f"{p}.bench.json")
+        if os.path.exists(path):
+            bench[p] = json.load(open(path))
+    res = {"workload": meta["workload"], "commands": meta["commands"]}
+    stats = kernel_stats(out_dir) if "trace" in meta["commands"] else {}
+    k = _gemm_kernel(stats) if stats else None
+    any_bench = next(iter(bench.values()), {})
+    cfg = any_bench.get("config", {})
+    flops = 2.0 * cfg.get("M", 0) * cfg.get("N", 0) * cfg.get("K", 0)
+    res["kernel_config"] = cfg.get("kernel_config")
+    res["shape"] = {x: cfg.get(x) for x in ("M", "N", "K", "transA", "transB", "alpha", "beta")}
+    if k:
+        s = stats[k]
+        res["kernel"] = k
+        res["trace"] = dict(s, tflops=flops / (s["avg_us"] * 1e-6) / 1e12 if flops else None)
+        res["bench_ms_per_step"] = bench.get("trace", {}).get("ms_per_step")
+    copy_scale = {}
+    for p, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        if p not in meta["commands"]:
+            continue
+        t = counters(out_dir, p)
+        copy = next((v for kk, v in t.items() if COPY_KERNEL in kk), None)
+        g = _gemm_kernel(t)
+        if copy and ctr in copy:
+            copy_scale[ctr] = (1 << 30) / (copy[ctr] * 1024.0)
+        if g:
+            res.setdefault("counters", {})[ctr + "_KiB"] = t[g][ctr]
+            res.setdefault("kernel", g)
+    if copy_scale:
+        res["copy_scale"] = copy_scale
+        c = res.get("counters", {})
+        if "FETCH_SIZE_KiB" in c and "FETCH_SIZE" in copy_scale:
+            res["hbm_read_bytes"] = c["FETCH_SIZE_KiB"] * 1024 * copy_scale["FETCH_SIZE"]
+        if "WRITE_SIZE_KiB" in c and "WRITE_SIZE" in copy_scale:
+            res["hbm_write_bytes"] = c["WRITE_SIZE_KiB"] * 1024 * copy_scale["WRITE_SIZE"]
+    for p in ("mfma", "lds", "wait"):
+        if p not in meta["commands"]:
+            continue
+        t = counters(out_dir, p)
+        g = _gemm_kernel(t)
+        if g:
+            res.setdefault("counters", {}).update(
+                {kk: v for kk, v in t[g].items() if not kk.startswith("_")})
+    c = res.get("counters", {})
+    if c.get("GRBM_GUI_ACTIVE"):
+        res["mfma_util"] = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (
+            c["GRBM_GUI_ACTIVE"] / XCDS * SIMDS)
+    if "SQ_INSTS_VALU_MFMA_MOPS_F32" in c:
+        res["mfma_flop"] = c["SQ_INSTS_VALU_MFMA_MOPS_F32"] * 512
+        res["mfma_flop_over_2mnk"] = res["mfma_flop"] / flops if flops else None
+    if c.get("SQ_LDS_IDX_ACTIVE"):
+        res["lds_conflicts_per_active_cycle"] = c.get("SQ_LDS_BANK_CONFLICT", 0) / \
+            c["SQ_LDS_IDX_ACTIVE"]
+    if c.get("SQ_WAVE_CYCLES"):
+        res["wait_share"] = c.get("SQ_WAIT_ANY", 0) / c["SQ_WAVE_CYCLES"]
+    comp = 4.0 * (cfg.get("M", 0) * cfg.get("K", 0) + cfg.get("K", 0) * cfg.get("N", 0) +
+                  cfg.get("M", 0) * cfg.get("N", 0) * (1 + (cfg.get("beta", 0) != 0)))
+    res["compulsory_bytes"] = comp
+    if "hbm_read_bytes" in res and "trace" in res:
+        tot = res["hbm_read_bytes"] + res.get("hbm_write_bytes", 0)
+        res["hbm_bytes"] = tot
+        res["hbm_gbs"] = tot / (res["trace"]["avg_us"] * 1e-6) / 1e9
+        res["hbm_over_compulsory"] = tot / comp if comp else None
+    with open(os.path.join(out_dir, "summary.json"), "w") as f:
+        json.dump(res, f, indent=1)
+    md = render(res)
+    with open(os.path.join(out_dir, "summary.md"), "w") as f:
+        f.write(md)
+    return res, md
+
+
+def _f(v, fmt):
+    return "-" if v is None else format(v, fmt)
+
+
+def render(res):
+    sh = res["shape"]
+    lines = [f"### {res['workload']}: {sh['M']}x{sh['N']}x{sh['K']} "
+             f"{sh['transA']}{sh['transB']}, entry {res.get('kernel_config')}", ""]
+    t = res.get("trace", {})
+    lines.append("| kernel avg (us) | TFLOP/s (trace) | MfmaUtil | MFMA FLOP / 2MNK | "
+                 "LDS conflict cycles / active | wait share | HBM bytes / launch | "
+                 "x compulsory | HBM GB/s |")
+    lines.append("|---|---|---|---|---|---|---|---|---|")
+    lines.append("| " + " | ".join([
+        _f(t.get("avg_us"), ".1f"), _f(t.get("tflops"), ".1f"),
+        _f(res.get("mfma_util"), ".1%"), _f(res.get("mfma_flop_over_2mnk"), ".4f"),
+        _f(res.get("lds_conflicts_per_active_cycle"), ".3f"), _f(res.get("wait_share"), ".1%"),
+        _f(res.get("hbm_bytes"), ".4g"), _f(res.get("hbm_over_compulsory"), ".2f"),
+        _f(res.get("hbm_gbs"), ".0f")]) + " |")
+    lines.append("")
+    c = res.get("counters", {})
+    if c:
+        lines.append("Raw counters per dispatch: " + ", ".join(
+            f"{k} {v:.4g}" for k, v in sorted(c.items())) + ".")
+        lines.append("")
+    if res.get("copy_scale"):
+        lines.append("Copy-probe scale (bytes per counted byte): " + ", ".join(
+            f"{k} x{v:.3f}" for k, v in res["copy_scale"].items()) + ".")
+        lines.append("")
+    lines.append(f"Kernel: `{res.get('kernel')}`.")
+    lines.append("")
+    lines.append("Commands (from the repository root `$REPO`, run from /tmp):")
+    lines.append("")
+    for p, cmd in res["commands"].items():
+        lines.append(f"    {cmd}")
+    lines.append("")
+    return "\n".join(lines)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--workload", default="C5a")
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=-1)
+    ap.add_argument("--group-m", type=int, default=0)
+    ap.add_argument("--xcd-remap", type=int, choices=(0, 1), default=1)
+    ap.add_argument("--splitk", action="store_true")
+    ap.add_argument("--streamk", action="store_true")
+    ap.add_argument("--passes", nargs="+", default=list(PASSES), choices=list(PASSES))
+    ap.add_argument("--timeout", type=int, default=150, help="seconds per pass (SIGKILL)")
+    ap.add_argument("--summarize", default=None, help="only summarise an existing directory")
+    a = ap.parse_args(argv)
+    if a.summarize:
+        res, md = summarize(a.summarize)
+        print(md)
+        return 0
+    out = os.path.abspath(a.out or os.path.join(ROOT, "gpurun_out", f"counters_{a.workload}"))
+    os.makedirs(out, exist_ok=True)
+    meta = {"workload": a.workload, "commands": {}}
+    for p in a.passes:
+        meta["commands"][p] = run_pass(p, a, out)
+        with open(os.path.join(out, "meta.json"), "w") as f:
+            json.dump(meta, f, indent=1)
+    res, md = summarize(out)
+    print(md, flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

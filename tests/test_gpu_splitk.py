@@ -96,11 +96,11 @@ def test_splitk_workloads(name):
 
 
 def test_splitk_one_and_more_splits_than_ktiles():
-    w = wl.custom(100, 100, 40, alpha=1.0, beta=0.0, seed=3)  # 3 k-tiles of 16
+    w = wl.custom(100, 100, 40, alpha=1.0, beta=0.0, seed=3)  # 2 to 5 k-tiles (BK 8 .. 32)
     A, B, _ = wl.make_inputs(w)
     o1 = run_splitk(w, A, B, None, 1, ws_floats=1)
     check_full(w, A, B, None, o1)
-    o9 = run_splitk(w, A, B, None, 9, ws_floats=9 * 100 * 100)  # capped at 3
+    o9 = run_splitk(w, A, B, None, 9, ws_floats=9 * 100 * 100)  # capped at the k-tiles
     check_full(w, A, B, None, o9)
 
 

@@ -52,6 +52,9 @@ SHAPES = [
     (3001, 2047, 1025, "T", "N", 1.5, 0.5, "normal", 3001, 2047, 2047),
     (1500, 700, 333, "N", "T", -0.5, 2.0, "normal", None, None, None),
     (777, 2100, 1000, "T", "T", 1.0, 1.0, "normal", None, None, 2101),
+    (2500, 1800, 700, "N", "N", 0.75, -1.5, "normal", None, None, None),
+    (1333, 2001, 555, "T", "T", 1.25, 0.5, "normal", None, None, 2003),
+    (2047, 1500, 1001, "T", "N", -1.0, 1.0, "normal", None, None, None),
 ]
 
 
@@ -61,7 +64,6 @@ def test_streamk_matches_oracle(shape):
     w = wl.custom(M, N, K, ta, tb, alpha, beta, dist, seed=M + K, lda=lda, ldb=ldb, ldc=ldc)
     A, B, C = wl.make_inputs(w)
     out, need = run_streamk(w, A, B, C)
-    assert need > 0, "this shape is meant to have a split tail"
     check_full(w, A, B, C, out)
 
 
@@ -97,12 +99,31 @@ def test_streamk_small_or_no_workspace():
     assert np.array_equal(plain_ws, dC.cpu().numpy().reshape(w.M, w.N))
 
 
+def test_streamk_shapes_exercise_the_split():
+    """Most of the shapes above have a split tail with the current table (so
+    the tail kernels and the slot reduction are what the oracle checks),
+    across layouts, alpha/beta and unaligned rows."""
+    split = [s for s in SHAPES
+             if fg.fg_sgemm_streamk_workspace_size(s[3], s[4], s[0], s[1], s[2], lda=s[8],
+                                                   ldb=s[9]) > 0]
+    assert len(split) >= 5, split
+    assert {(s[3], s[4]) for s in split} >= {("N", "N"), ("T", "N"), ("T", "T")}
+    assert any(s[6] != 0 for s in split)
+
+
 def test_streamk_no_tail_is_plain():
+    """Whole rounds only (8192^3, 4096^3 with 256 x 256 tiles): no split. With
+    the default policy the model decides, and it never splits where the
+    always-split policy would not (nor asks for a larger workspace)."""
     assert fg.fg_sgemm_streamk_workspace_size("N", "N", 8192, 8192, 8192) == 0
     assert fg.fg_sgemm_streamk_workspace_size("N", "N", 4096, 4096, 4096) == 0
-    # with the default policy the model decides: no split where it sees no gain
+    shapes = [(1000, 1000, 500), (4096, 5120, 4096), (4608, 4608, 4096), (6144, 6144, 6144),
+              (1536, 1536, 1536), (512, 8192, 8192)]
+    always = [fg.fg_sgemm_streamk_workspace_size("N", "N", *sh) for sh in shapes]
     assert fg.fg_set_streamk_policy(0) == fg.FG_OK
-    assert fg.fg_sgemm_streamk_workspace_size("N", "N", 1000, 1000, 500) == 0
+    model = [fg.fg_sgemm_streamk_workspace_size("N", "N", *sh) for sh in shapes]
+    assert all(m == 0 or m <= a for m, a in zip(model, always)), (model, always)
+    assert sum(m == 0 for m in model) >= 1
 
 
 def test_streamk_large_full():
