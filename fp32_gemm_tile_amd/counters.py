@@ -27,7 +27,9 @@ Usage (on the GPU machine, from the repository root):
     python -m fp32_gemm_tile_amd.counters --workload C3 --out gpurun_out/counters_C3 \
         [--config ID] [--group-m G] [--xcd-remap 0|1] [--passes trace fetch ...]
     python -m fp32_gemm_tile_amd.counters --summarize gpurun_out/counters_C3
-The summary (Markdown, with the commands) is printed and written to
+    python -m fp32_gemm_tile_amd.counters --out gpurun_out/bench_trace --bench-trace [ARGS]
+(the last: bench.py with ARGS -- none for its default run -- under the
+kernel trace, summarised per kernel and launch size). The summary (Markdown, with the commands) is printed and written to
 ``<out>/summary.md`` and ``<out>/summary.json``.
 """
 from __future__ import annotations
@@ -130,6 +132,66 @@ def kernel_stats(out_dir):
     return out
 
 
+def dispatches(out_dir, pass_name="trace"):
+    """Per (kernel, launch size in work-items) of a kernel-trace pass: calls
+    and mean / median / min / max duration (us)."""
+    import statistics
+    groups = {}
+    for r in _rows(os.path.join(out_dir, pass_name, "**", "*kernel_trace.csv")):
+        n = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((r["Kernel_Name"], n), []).append(d)
+    return {k: {"calls": len(v), "avg_us": sum(v) / len(v), "median_us": statistics.median(v),
+                "min_us": min(v), "max_us": max(v)} for k, v in groups.items()}
+
+
+def bench_trace(out_dir, bench_argv, timeout):
+    """The bench as given (default: its default run) under rocprofv3's kernel
+    trace; a summary of every GEMM kernel per launch size beside the bench's
+    own line, whose mean time per call must agree with the trace's average
+    for the kernel and size it reports."""
+    os.makedirs(out_dir, exist_ok=True)
+    d = os.path.join(out_dir, "trace")
+    cmd = ["timeout", "-s", "KILL", str(timeout), "rocprofv3", "--kernel-trace", "--stats",
+           "--output-format", "csv", "-d", d, "-o", "run", "--",
+           sys.executable, os.path.join(ROOT, "bench.py"), *bench_argv]
+    print("[counters] bench under the kernel trace", flush=True)
+    r = subprocess.run(cmd, cwd="/tmp", env=dict(os.environ, TMPDIR="/tmp"), capture_output=True,
+                       text=True)
+    with open(os.path.join(out_dir, "trace.log"), "w") as f:
+        f.write(r.stdout + "\n---- stderr ----\n" + r.stderr)
+    line = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    if not line:
+        raise RuntimeError(f"bench under the trace failed (rc {r.returncode}); see trace.log")
+    b = json.loads(line[-1])
+    disp = dispatches(out_dir)
+    cmdline = " ".join(shlex.quote(c) for c in cmd).replace(ROOT, "$REPO")
+    L = ["Command (from the repository root `$REPO`, run from /tmp):", "", f"    {cmdline}", "",
+         f"Bench line: value {b['value']} {b['unit']}, ms_per_step {b['ms_per_step']} "
+         f"(workload {b['config']['workload']}, entry {b['config']['kernel_config']}).", "",
+         "| kernel | work-items per launch | calls | avg (us) | median (us) | min (us) | max (us) |",
+         "|---|---|---|---|---|---|---|"]
+    for (k, n), v in sorted(disp.items(), key=lambda kv: -kv[1]["calls"] * kv[1]["avg_us"]):
+        if COPY_KERNEL in k or not ("fg::" in k or "gemm" in k.lower()):
+            continue
+        L.append(f"| `{k}` | {n} | {v['calls']} | {v['avg_us']:.1f} | {v['median_us']:.1f} | "
+                 f"{v['min_us']:.1f} | {v['max_us']:.1f} |")
+    cfg = b["config"]
+    flops = 2.0 * cfg["M"] * cfg["N"] * cfg["K"]
+    head = max((kv for kv in disp.items() if "fg::" in kv[0][0]),
+               key=lambda kv: kv[1]["calls"] * kv[1]["avg_us"], default=None)
+    if head:
+        (k, n), v = head
+        L += ["", f"Dominant kernel `{k}` ({n} work-items): trace average {v['avg_us']:.1f} us "
+              f"= {flops / (v['avg_us'] * 1e-6) / 1e12:.2f} TFLOP/s; the bench's "
+              f"ms_per_step {b['ms_per_step'] * 1e3:.1f} us "
+              f"(ratio {b['ms_per_step'] * 1e3 / v['avg_us']:.4f}).", ""]
+    md = "\n".join(L) + "\n"
+    with open(os.path.join(out_dir, "trace_summary.md"), "w") as f:
+        f.write(md)
+    return md
+
+
 def _gemm_kernel(table):
     """The GEMM kernel of a pass: the one with the most dispatches among
     those that are not the copy probe, nor torch's own fill/rand kernels."""
@@ -210,6 +272,22 @@ def summarize(out_dir):
         res["hbm_over_compulsory"] = tot / comp if comp else None
     with open(os.path.join(out_dir, "summary.json"), "w") as f:
         json.dump(res, f, indent=1)
+    if "hbm_read_bytes" in res and "hbm_write_bytes" in res:
+        # the record bench.py reads for roofline.traffic (valid while the
+        # kernel sources hash to the same value)
+        sys.path.insert(0, ROOT)
+        import bench
+        rec = {"workload": meta["workload"], "kernel": res.get("kernel"),
+               "kernel_config": res.get("kernel_config"),
+               "kernel_source_sha": bench.kernel_source_sha(res.get("kernel_config") or "mfma_"),
+               "fetch_kib_per_dispatch": res["counters"]["FETCH_SIZE_KiB"],
+               "write_kib_per_dispatch": res["counters"]["WRITE_SIZE_KiB"],
+               "fetch_scale": res["copy_scale"]["FETCH_SIZE"],
+               "write_scale": res["copy_scale"]["WRITE_SIZE"],
+               "bytes_per_launch": int(round(res["hbm_read_bytes"] + res["hbm_write_bytes"])),
+               "source": f"profiles/counters_{meta['workload']}.md"}
+        with open(os.path.join(out_dir, f"traffic_{meta['workload']}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
     md = render(res)
     with open(os.path.join(out_dir, "summary.md"), "w") as f:
         f.write(md)
@@ -269,7 +347,14 @@ def main(argv=None):
     ap.add_argument("--passes", nargs="+", default=list(PASSES), choices=list(PASSES))
     ap.add_argument("--timeout", type=int, default=150, help="seconds per pass (SIGKILL)")
     ap.add_argument("--summarize", default=None, help="only summarise an existing directory")
+    ap.add_argument("--bench-trace", nargs=argparse.REMAINDER, default=None, metavar="BENCH_ARG",
+                    help="run bench.py with these arguments (none: its default run) under "
+                         "the kernel trace and summarise per kernel and launch size into --out")
     a = ap.parse_args(argv)
+    if a.bench_trace is not None:
+        out = os.path.abspath(a.out or os.path.join(ROOT, "gpurun_out", "bench_trace"))
+        print(bench_trace(out, a.bench_trace, max(a.timeout, 600)), flush=True)
+        return 0
     if a.summarize:
         res, md = summarize(a.summarize)
         print(md)
