@@ -70,7 +70,7 @@ def load_traffic(workload, kernel_config):
 
 
 def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock=False,
-             epilogue=None, streamk=False, min_warm_s=0.0):
+             epilogue=None, streamk=False, min_warm_s=0.0, keep_output=False):
     """Time `steps` calls on the current stream with a HIP event pair around
     each call. Warm (default): the calls run back to back and the mean is the
     whole range over `steps`. Cold: a 512 MiB device write runs before each
@@ -175,8 +175,18 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock
     cfg = fg.fg_select_config(w.transA, w.transB, w.M, w.N, w.K, dA.data_ptr(), w.LDA,
                               dB.data_ptr(), w.LDB, dC.data_ptr(), w.LDC) if config < 0 \
         else fg.fg_get_config(config)
+    output = None
+    if keep_output and epilogue is None:
+        # Outside every timed range: one more call on the original C (with
+        # beta != 0 the timed calls kept updating C), read back for the
+        # element-wise check against the oracle.
+        if C is not None:
+            dC.copy_(torch.from_numpy(C))
+        step()
+        torch.cuda.synchronize()
+        output = dC.cpu().numpy()[:, :w.N]
     return {"ms_per_launch": mean, "ms_median": statistics.median(per), "ms_min": min(per),
-            "wall_s": wall, "config": cfg["name"], "clock_mhz": clock}
+            "wall_s": wall, "config": cfg["name"], "clock_mhz": clock, "output": output}
 
 
 def measured_peaks():
@@ -258,32 +268,56 @@ def finish_clock_watch(proc):
             "samples": len(per_sample), "source": "amd-smi metric --clock, 1 s interval"}
 
 
-def cpu_baseline(w, target_s=15.0):
-    """The oracle as it is, on a bounded sample of output rows of the same
-    workload, scaled to TFLOP/s (2*N*K FLOP per output row)."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, gpu_out=None, block=1024):
+    """The oracle as it is, on the whole workload (every row of C), timed on
+    the host's cores; with `gpu_out` (the timed calls' C, host float32) every
+    element of it is checked against the same oracle rows, outside the timed
+    part (each block of rows is timed on its own)."""
     import numpy as np
     import oracle
     from fp32_gemm_tile_amd import workloads as wl
 
     A, B, C = wl.make_inputs(w)
     threads = oracle.num_threads()
-    rows = 8
-    t0 = time.perf_counter()
-    oracle.gemm_rows(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A, w.LDA, B, w.LDB,
-                     w.beta, C, w.LDC, rows=np.arange(rows))
-    dt = time.perf_counter() - t0
-    rows = int(max(8, min(w.M, rows * target_s / max(dt, 1e-3))))
-    rng = np.random.default_rng(0)
-    sel = np.sort(rng.choice(w.M, size=rows, replace=False))
-    t0 = time.perf_counter()
-    oracle.gemm_rows(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A, w.LDA, B, w.LDB,
-                     w.beta, C, w.LDC, rows=sel)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * w.N * w.K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{rows} of {w.M} output rows of {w.name} (binary64 oracle), {dt:.1f} s",
-            "single_thread_256cubed_s": oracle_single_thread_small()}
+    oracle_s = 0.0
+    worst, n_bad, err2, ref2 = 0.0, 0, 0.0, 0.0
+    for r0 in range(0, w.M, block):
+        rows = np.arange(r0, min(w.M, r0 + block), dtype=np.int64)
+        t0 = time.perf_counter()
+        cref, s = oracle.gemm_rows(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A, w.LDA, B,
+                                   w.LDB, w.beta, C, w.LDC, rows=rows)
+        oracle_s += time.perf_counter() - t0
+        if gpu_out is not None:
+            cin = C[rows, :w.N] if (C is not None and w.beta != 0) else None
+            _, info = oracle.compare.check(gpu_out[rows], cref, s, w.K, w.alpha, w.beta, cin,
+                                           frob=True)
+            worst = max(worst, info["max_err_over_tol"])
+            n_bad += info["n_bad"]
+            err2 += info["frob_abs"] ** 2
+            ref2 += info["frob_ref"] ** 2
+    out = {"value": w.flops / oracle_s / 1e12, "unit": "TFLOP/s", "cores": threads,
+           "cpu_model": cpu_model(), "kind": "oracle",
+           "sample": f"the whole product: all {w.M} rows of {w.name} "
+                     f"({w.M}x{w.N}x{w.K} {w.transA}{w.transB}), binary64 oracle, "
+                     f"{oracle_s:.1f} s",
+           "single_thread_256cubed_s": oracle_single_thread_small()}
+    if gpu_out is not None:
+        out["parity"] = {"elements": int(w.M) * int(w.N), "outside_bound": n_bad,
+                         "max_err_over_tol": worst,
+                         "frob_rel": (err2 ** 0.5) / (ref2 ** 0.5) if ref2 > 0 else None,
+                         "ok": n_bad == 0 and (ref2 == 0 or (err2 / ref2) ** 0.5 <= 1e-5)}
+    return out
 
 
 _ONE_THREAD_SNIPPET = """
@@ -327,11 +361,12 @@ def copy_probe(nbytes=1 << 30, reps=3):
 
 
 def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False, cold=False,
-            sample_clock=False, epilogue=None, streamk=False, min_warm_s=0.0):
+            sample_clock=False, epilogue=None, streamk=False, min_warm_s=0.0,
+            keep_output=False):
     from fp32_gemm_tile_amd import workloads as wl
     w = wl.WORKLOADS[name] if isinstance(name, str) else name
     g = time_gpu(w, steps, warmup, config, splitk, cold, sample_clock, epilogue, streamk,
-                 min_warm_s)
+                 min_warm_s, keep_output=with_cpu or keep_output)
     tflops = w.flops / (g["ms_per_launch"] * 1e-3) / 1e12
     gbs = w.compulsory_bytes / (g["ms_per_launch"] * 1e-3) / 1e9
     traffic = load_traffic(name, g["config"])
@@ -371,8 +406,10 @@ def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False, cold=False,
         "hbm_gbs_compulsory": round(gbs, 1),
         "roofline": roof,
     }
+    if keep_output:
+        out["_output"] = g["output"]
     if with_cpu:
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, g["output"])
     return out
 
 
@@ -459,9 +496,12 @@ def main():
                       flush=True)
         return
 
+    # The CPU baseline leg (the whole oracle, timed; every element of the
+    # timed calls' result checked against it) runs last, after the GPU work.
+    with_cpu = not args.no_cpu
     r = run_one(args.workload, args.steps, args.warmup, False, args.config, _splitk_arg(args),
                 args.cold, sample_clock=not args.no_probes, epilogue=args.epilogue,
-                streamk=args.streamk)
+                streamk=args.streamk, keep_output=with_cpu)
     # The 4096^3 shape of the metric, and one GPU's row block of 8192^3 split
     # over eight GPUs, timed in the same run.
     if args.workload == "C5a" and not args.no_extras:
@@ -477,9 +517,11 @@ def main():
         mp = measured_peaks()
         mp["pct_of_measured_mfma"] = round(100 * r["value"] / mp["mfma_tflops"], 2)
         r["measured_peaks"] = mp
-    if not args.no_cpu:
+    if with_cpu:
         from fp32_gemm_tile_amd import workloads as wl
-        r["cpu_baseline"] = cpu_baseline(wl.WORKLOADS[args.workload])
+        r["cpu_baseline"] = cpu_baseline(wl.WORKLOADS[args.workload], r.pop("_output", None))
+        # every element of the timed calls' result against the oracle
+        r["parity"] = r["cpu_baseline"].get("parity")
     if args.copy_probe:
         copy_probe()
     print(json.dumps(r), flush=True)

@@ -149,6 +149,8 @@ def load_library(path: str = LIB_PATH):
     lib.fg_probe_mfma.restype = i32
     lib.fg_probe_mfma_flops.argtypes = [i32, i32]
     lib.fg_probe_mfma_flops.restype = ctypes.c_double
+    lib.fg_probe_lds_dma.argtypes = [vp, i32, vp, vp]
+    lib.fg_probe_lds_dma.restype = i32
     lib.fg_probe_read.argtypes = [vp, i64, i32, vp, vp]
     lib.fg_probe_read.restype = i32
     _lib = lib
@@ -316,6 +318,13 @@ def fg_probe_mfma(workgroups, iterations, out, stream=0) -> int:
 
 def fg_probe_mfma_flops(workgroups, iterations) -> float:
     return load_library().fg_probe_mfma_flops(workgroups, iterations)
+
+
+def fg_probe_lds_dma(src, bytes_per_lane, out, stream=0) -> int:
+    """One direct-to-LDS load with lanes reversed, LDS copied to out
+    (fp32gemm_probe.h); src and out: 64 * bytes_per_lane / 4 floats."""
+    return load_library().fg_probe_lds_dma(src or None, bytes_per_lane, out or None,
+                                           stream or None)
 
 
 def fg_probe_read(x, n, workgroups, out, stream=0) -> int:

@@ -870,6 +870,20 @@ fg_status fg_probe_mfma(int32_t workgroups, int32_t iterations, float* out, hipS
     return FG_OK;
 }
 
+fg_status fg_probe_lds_dma(const float* src, int32_t bytes_per_lane, float* out,
+                           hipStream_t stream) {
+    clear_error();
+    if (!src) return fail(FG_ERR_INVALID_ARG, 1, "src is NULL");
+    if (bytes_per_lane != 4 && bytes_per_lane != 16)
+        return fail(FG_ERR_INVALID_ARG, 2, "bytes_per_lane must be 4 or 16");
+    if (!out) return fail(FG_ERR_INVALID_ARG, 3, "out is NULL");
+    fg_status s = check_device();
+    if (s != FG_OK) return s;
+    const hipError_t e = fg::launch_probe_lds_dma(src, bytes_per_lane, out, stream);
+    if (e != hipSuccess) return fail(FG_ERR_HIP, 0, "kernel launch: %s", hipGetErrorString(e));
+    return FG_OK;
+}
+
 fg_status fg_probe_read(const float* x, int64_t n, int32_t workgroups, float* out,
                         hipStream_t stream) {
     clear_error();

@@ -93,5 +93,8 @@ hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 hipError_t launch_probe_mfma(int workgroups, int iters, float* out, hipStream_t stream);
 hipError_t launch_probe_read(const float* x, int64_t n4, int workgroups, float* out,
                              hipStream_t stream);
+// One direct-to-LDS load of `bytes` (4 or 16) per lane, lanes reversed, LDS
+// copied out (fg_probe.hip).
+hipError_t launch_probe_lds_dma(const float* src, int bytes, float* out, hipStream_t stream);
 
 }  // namespace fg

@@ -8,6 +8,8 @@
 //     at the end so the chains cannot be removed.
 //   * read_probe_kernel: a grid-stride read of n floats with 128-bit loads,
 //     16 KiB per workgroup per pass, one partial sum per wave stored.
+//   * lds_dma_probe_kernel: the lane layout of one direct-to-LDS buffer load
+//     (the GEMM loader assumes lane L's W floats land at LDS float W L).
 #include "fg_device.h"
 
 namespace fg {
@@ -67,7 +69,44 @@ __global__ void __launch_bounds__(kProbeThreads) read_probe_kernel(const f4* __r
     if ((threadIdx.x & 63) == 0) out[(int64_t)blockIdx.x * (kProbeThreads / 64) + (threadIdx.x >> 6)] = s;
 }
 
+// One wave, one direct-to-LDS buffer load of BYTES per lane: lane L fetches
+// the W = BYTES / 4 floats at src[(63 - L) W ..] (lanes reversed, so that any
+// other placement shows), then the wave copies the 64 W floats of the LDS
+// buffer, prefilled with -1, to out.
+template <int BYTES>
+__global__ void __launch_bounds__(64) lds_dma_probe_kernel(const float* src, float* out) {
+    constexpr int W = BYTES / 4;
+    __shared__ float buf[64 * W];
+    const int lane = threadIdx.x;
+    for (int i = lane; i < 64 * W; i += 64) buf[i] = -1.f;
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src, 64 * W);
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t voff = (uint32_t)((63 - lane) * W) * 4u;
+    auto* lds = (__attribute__((address_space(3))) void*)buf;
+    if constexpr (BYTES == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, 0, 0, 0);
+#else
+    (void)r;
+#endif
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt and lgkmcnt all zero
+    __syncthreads();
+    for (int i = lane; i < 64 * W; i += 64) out[i] = buf[i];
+}
+
 }  // namespace
+
+hipError_t launch_probe_lds_dma(const float* src, int bytes, float* out, hipStream_t stream) {
+    if (bytes == 16)
+        hipLaunchKernelGGL(lds_dma_probe_kernel<16>, dim3(1), dim3(64), 0, stream, src, out);
+    else if (bytes == 4)
+        hipLaunchKernelGGL(lds_dma_probe_kernel<4>, dim3(1), dim3(64), 0, stream, src, out);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_probe_mfma(int workgroups, int iters, float* out, hipStream_t stream) {
     hipLaunchKernelGGL(mfma_probe_kernel, dim3(workgroups), dim3(kProbeThreads), 0, stream, iters,

@@ -47,6 +47,21 @@ double fg_probe_mfma_flops(int32_t workgroups, int32_t iterations);
 fg_status fg_probe_read(const float* x, int64_t n, int32_t workgroups, float* out,
                         hipStream_t stream);
 
+/*
+ * fg_probe_lds_dma: the lane layout of gfx950's direct-to-LDS buffer load,
+ * which the GEMM's loader relies on (lane L's W = bytes_per_lane / 4 floats
+ * written to LDS floats W L .. W L + W - 1 of the instruction's base). One
+ * wave issues one such load in which lane L reads src[(63 - L) W ..], then
+ * copies the 64 W floats of LDS to out; with that layout
+ * out[W L + e] = src[(63 - L) W + e].
+ *   1 src            : device memory, 64 * W floats
+ *   2 bytes_per_lane : 4 (buffer_load_dword ... lds) or 16 (dwordx4)
+ *   3 out            : device memory, 64 * W floats
+ *   4 stream
+ */
+fg_status fg_probe_lds_dma(const float* src, int32_t bytes_per_lane, float* out,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -298,6 +298,9 @@ def test_probe_validation_and_flop_count():
     assert fg.fg_probe_read(4100, 8, 4, 4096) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 1
     assert fg.fg_probe_read(4096, 8, 0, 4096) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 3
     assert fg.fg_probe_read(4096, 8, 4, 0) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 4
+    assert fg.fg_probe_lds_dma(0, 4, 4096) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 1
+    assert fg.fg_probe_lds_dma(4096, 8, 4096) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 2
+    assert fg.fg_probe_lds_dma(4096, 16, 0) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 3
 
 
 def test_fused_validation_and_quick_returns():

@@ -48,9 +48,26 @@ def test_traffic_records_are_keyed_by_kernel_sources():
 
 
 def test_cpu_baseline_leg():
+    """The oracle on the whole workload, timed; with a result given, every
+    element is checked against it (an element off by far more than the bound
+    is reported)."""
+    import numpy as np
+    import oracle
     from fp32_gemm_tile_amd import workloads as wl
-    r = bench.cpu_baseline(wl.WORKLOADS["C2"], target_s=0.3)
+    w = wl.WORKLOADS["C1"]
+    A, B, C = wl.make_inputs(w)
+    cref, _ = oracle.gemm(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A, w.LDA, B, w.LDB,
+                          w.beta, C, w.LDC)
+    good = cref.astype(np.float32)
+    r = bench.cpu_baseline(w, good, block=100)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
-    assert r["cores"] >= 1 and "output rows of C2" in r["sample"]
+    assert r["cores"] >= 1 and "all 256 rows" in r["sample"]
+    assert r["parity"]["ok"] and r["parity"]["elements"] == 256 * 256
+    assert r["parity"]["outside_bound"] == 0 and r["parity"]["max_err_over_tol"] < 1
+    bad = good.copy()
+    bad[200, 17] += 1.0   # far above the bound (8 K 2^-24 S + 1e-6, about 0.01 here)
+    r = bench.cpu_baseline(w, bad, block=64)
+    assert not r["parity"]["ok"] and r["parity"]["outside_bound"] == 1
     t = r["single_thread_256cubed_s"]
     assert t is None or 0 < t < 60
+    assert "parity" not in bench.cpu_baseline(w)

@@ -53,3 +53,22 @@ def test_read_probe_sums_what_it_reads():
         parts = out.cpu().numpy()
         assert np.all(np.isfinite(parts))
         assert parts.astype(np.float64).sum() == n  # integer partial sums are exact
+
+
+@pytest.mark.parametrize("nbytes", [4, 16])
+def test_lds_dma_lane_layout(nbytes):
+    """A direct-to-LDS buffer load writes lane L's W = bytes / 4 floats to LDS
+    floats W L .. W L + W - 1 of its base: the layout the GEMM's loader
+    assigns its global addresses by. Lanes read src reversed, so
+    out[W L + e] = src[(63 - L) W + e]; any other placement, or an LDS slot
+    left unwritten (prefilled -1), fails."""
+    import torch
+    W = nbytes // 4
+    log(f"lds dma probe bytes={nbytes}")
+    src = torch.arange(64 * W, dtype=torch.float32, device="cuda") + 1000.0
+    out = torch.full((64 * W,), float("nan"), dtype=torch.float32, device="cuda")
+    assert fg.fg_probe_lds_dma(src.data_ptr(), nbytes, out.data_ptr()) == fg.FG_OK
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(64, W)
+    want = (src.cpu().numpy().reshape(64, W))[::-1]
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
