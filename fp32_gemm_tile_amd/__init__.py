@@ -61,6 +61,23 @@ class fg_epilogue(ctypes.Structure):
                 ("activation", ctypes.c_int32)]
 
 
+FG_QUANT_NONE, FG_QUANT_BF16, FG_QUANT_INT8_ROW = 0, 1, 2
+_QUANTS = {"none": FG_QUANT_NONE, "bf16": FG_QUANT_BF16, "int8_row": FG_QUANT_INT8_ROW}
+
+
+class fg_quant(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("out", ctypes.c_void_p), ("ldq", ctypes.c_int64),
+                ("row_factor", ctypes.c_void_p)]
+
+
+def make_quant(kind, out, ldq, row_factor=0):
+    """fg_quant from a format ("bf16", "int8_row" or an fg_quant_kind), the
+    device address of Q, its leading dimension and (int8_row) the device
+    address of the M row factors."""
+    k = _QUANTS[kind] if isinstance(kind, str) else int(kind)
+    return fg_quant(k, out or None, ldq, row_factor or None)
+
+
 def activation_code(act) -> int:
     """fg_activation value of "none" / "relu" / "gelu" / "silu" (or an int)."""
     if isinstance(act, str):
@@ -132,6 +149,9 @@ def load_library(path: str = LIB_PATH):
     lib.fg_sgemm_streamk_workspace_size.restype = ctypes.c_size_t
     lib.fg_sgemm_fused.argtypes = gemm_args[:13] + [ctypes.POINTER(fg_epilogue), vp, i32]
     lib.fg_sgemm_fused.restype = i32
+    lib.fg_sgemm_quant.argtypes = gemm_args[:13] + [ctypes.POINTER(fg_epilogue),
+                                                    ctypes.POINTER(fg_quant), vp, i32]
+    lib.fg_sgemm_quant.restype = i32
     lib.fg_estimate_seconds.argtypes = [i64, i64, i64, i32, i32, i32]
     lib.fg_estimate_seconds.restype = ctypes.c_double
     lib.fg_get_efficiency.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
@@ -275,6 +295,16 @@ def fg_sgemm_fused(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
     ep = ctypes.byref(epilogue) if epilogue is not None else None
     return load_library().fg_sgemm_fused(_op(transA), _op(transB), M, N, K, alpha, A, lda,
                                          B, ldb, beta, C, ldc, ep, stream or None, config)
+
+
+def fg_sgemm_quant(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                   epilogue=None, quant=None, stream=0, config=-1):
+    """Raw call: the fused GEMM plus a quantised copy Q of C (an fg_quant, or
+    None for none); see include/fp32gemm.h."""
+    ep = ctypes.byref(epilogue) if epilogue is not None else None
+    q = ctypes.byref(quant) if quant is not None else None
+    return load_library().fg_sgemm_quant(_op(transA), _op(transB), M, N, K, alpha, A, lda,
+                                         B, ldb, beta, C, ldc, ep, q, stream or None, config)
 
 
 def fg_estimate_seconds(M, N, K, config_id, splits=1, beta_zero=True) -> float:

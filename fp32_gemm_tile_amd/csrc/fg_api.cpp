@@ -71,6 +71,9 @@ struct Entry {
     int fallback;  // entry used instead when A or B rows are not 16-byte
                    // aligned (entries with 16-byte direct-to-LDS loads only;
                    // -1 = any alignment is fine)
+    bool quant;    // writes the quantised second output of fg_sgemm_quant
+                   // (matrix-core kernels with at most 128 accumulators per
+                   // lane, as sgemm_mfma.h compiles it, and the few-row one)
 };
 
 constexpr int kNumCUs = 256;
@@ -96,6 +99,7 @@ Entry make_entry(int id, fg_kind kind, int variant, int bm, int bn, int bk, int 
     e.variant = variant;
     e.wps = wps;
     e.fallback = fallback;
+    e.quant = kind == FG_KIND_SKINNY || (kind == FG_KIND_MFMA && wm * wn / 64 <= 128);
     return e;
 }
 
@@ -311,13 +315,15 @@ double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0, double eff) {
 // fastest instance on geometric mean with a 1% margin, 0.995 with 2%.)
 constexpr double kPickMargin = 0.99;
 int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_splits,
-                 bool beta0, int64_t* best_splits, bool mfma_only = false) {
+                 bool beta0, int64_t* best_splits, bool mfma_only = false,
+                 bool need_quant = false) {
     static const int64_t kSplits[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
     int best = -1;
     double best_cost = 0;
     *best_splits = 1;
     for (int i = 0; i < num_entries(); ++i) {
         const Entry& e = table()[i];
+        if (need_quant && !e.quant) continue;
         if (e.cfg.kind == FG_KIND_SKINNY) {
             if (mfma_only) continue;
             const double c = skinny_cost(M, N, K, beta0, efficiencies()[i].eff.load());
@@ -530,14 +536,16 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
                    const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
                    float* C, int64_t ldc, hipStream_t stream, int32_t config_id,
                    int64_t splits, float* ws, size_t ws_bytes,
-                   const fg_epilogue* epi = nullptr, int config_arg = 15, bool streamk = false) {
+                   const fg_epilogue* epi = nullptr, int config_arg = 15, bool streamk = false,
+                   const fg_quant* quant = nullptr) {
     clear_error();
     fg_status s = validate(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
     if (s != FG_OK) return s;
     if (config_id < -1 || config_id >= num_entries())
         return fail(FG_ERR_INVALID_ARG, config_arg, "config id %d out of range", config_id);
-    const bool epi_on = epi && (epi->row_scale || epi->col_scale || epi->row_bias ||
-                                epi->col_bias || epi->activation != FG_ACT_NONE);
+    const bool quant_on = quant && quant->kind != FG_QUANT_NONE;
+    const bool epi_on = quant_on || (epi && (epi->row_scale || epi->col_scale || epi->row_bias ||
+                                             epi->col_bias || epi->activation != FG_ACT_NONE));
 
     // Quick returns.
     if (M == 0 || N == 0) return FG_OK;
@@ -566,11 +574,24 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
     p.flags = build_flags(A, lda, B, ldb, C, ldc, beta);
     if (epi_on) {
         p.flags |= fg::FLAG_EPI;
-        p.row_scale = epi->row_scale;
-        p.col_scale = epi->col_scale;
-        p.row_bias = epi->row_bias;
-        p.col_bias = epi->col_bias;
-        p.act = epi->activation;
+        if (epi) {
+            p.row_scale = epi->row_scale;
+            p.col_scale = epi->col_scale;
+            p.row_bias = epi->row_bias;
+            p.col_bias = epi->col_bias;
+            p.act = epi->activation;
+        }
+    }
+    if (quant_on) {
+        const int esize = quant->kind == FG_QUANT_BF16 ? 2 : 1;
+        p.flags |= fg::FLAG_QUANT;
+        p.qout = quant->out;
+        p.ldq = (int32_t)quant->ldq;
+        p.qkind = quant->kind == FG_QUANT_BF16 ? fg::QUANT_BF16 : fg::QUANT_INT8_ROW;
+        p.qscale = quant->row_factor;
+        p.q_extent = (M - 1) * quant->ldq + N;
+        if (quant->ldq % 4 == 0 && ((uintptr_t)quant->out % (uintptr_t)(4 * esize)) == 0)
+            p.flags |= fg::FLAG_VEC_Q;
     }
 
     if (no_product) {
@@ -631,16 +652,23 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
     if (config_id >= 0) {
         idx = config_id;
         if (want == 0) want = 1;
+        if (quant_on && !table()[idx].quant)
+            return fail(FG_ERR_INVALID_ARG, config_arg,
+                        "entry %s has no quantised output (another entry, or -1)",
+                        table()[idx].cfg.name);
     } else {
         int64_t auto_splits = 1;
         idx = select_entry(M, N, K, ab_aligned, want == 0 ? max_splits : want, beta == 0.0f,
-                           &auto_splits, want > 1);
+                           &auto_splits, want > 1, quant_on);
         if (want == 0) want = auto_splits;
     }
     if (idx < 0 || idx >= num_entries())
         return fail(FG_ERR_UNSUPPORTED, 0, "no table entry fits this call");
     if (table()[idx].fallback >= 0 && !ab_aligned) idx = table()[idx].fallback;
     const Entry& en = table()[idx];
+    if (quant_on && !en.quant)
+        return fail(FG_ERR_INVALID_ARG, config_arg, "entry %s has no quantised output",
+                    en.cfg.name);
     if (en.cfg.kind != FG_KIND_MFMA) want = 1;  // split-K runs on the MFMA kernels
 
     int64_t kps = 0;
@@ -790,6 +818,33 @@ fg_status fg_sgemm_fused(fg_op transA, fg_op transB, int64_t M, int64_t N, int64
                     epilogue->activation);
     return run_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
                     config_id, 1, nullptr, 0, epilogue, 16);
+}
+
+fg_status fg_sgemm_quant(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                         float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                         float beta, float* C, int64_t ldc, const fg_epilogue* epilogue,
+                         const fg_quant* quant, hipStream_t stream, int32_t config_id) {
+    clear_error();
+    if (epilogue && (epilogue->activation < FG_ACT_NONE || epilogue->activation > FG_ACT_SILU))
+        return fail(FG_ERR_INVALID_ARG, 14, "activation %d is not an fg_activation",
+                    epilogue->activation);
+    if (quant) {
+        if (quant->kind < FG_QUANT_NONE || quant->kind > FG_QUANT_INT8_ROW)
+            return fail(FG_ERR_INVALID_ARG, 15, "kind %d is not an fg_quant_kind", quant->kind);
+        if (quant->kind != FG_QUANT_NONE) {
+            if (quant->ldq < std::max<int64_t>(1, N))
+                return fail(FG_ERR_INVALID_ARG, 15, "ldq=%lld < N=%lld", (long long)quant->ldq,
+                            (long long)N);
+            if (quant->ldq > FG_MAX_LD)
+                return fail(FG_ERR_UNSUPPORTED, 0, "ldq above %d", FG_MAX_LD);
+            if (M > 0 && N > 0 && !quant->out)
+                return fail(FG_ERR_INVALID_ARG, 15, "quantised output is NULL");
+            if (M > 0 && N > 0 && quant->kind == FG_QUANT_INT8_ROW && !quant->row_factor)
+                return fail(FG_ERR_INVALID_ARG, 15, "row factors are NULL");
+        }
+    }
+    return run_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                    config_id, 1, nullptr, 0, epilogue, 17, false, quant);
 }
 
 double fg_estimate_seconds(int64_t M, int64_t N, int64_t K, int32_t config_id, int32_t splits,

@@ -17,6 +17,16 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 // no swizzle, no stride).
 constexpr int32_t kBufferWord3 = 0x00020000;
 
+// A raw buffer over [base, base + bytes) of any element type (clamped as
+// make_rsrc below).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_bytes(const void* base,
+                                                                  int64_t bytes) {
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0xFFFFFFFFll) bytes = 0xFFFFFFFFll;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             (int)(uint32_t)bytes, kBufferWord3);
+}
+
 // A raw buffer over [base, base + records_bytes). Loads whose byte offset is
 // at or past the end return 0 and stores there are dropped by the hardware;
 // the kernels still predicate every access themselves, so this is only a
@@ -144,14 +154,55 @@ __device__ __forceinline__ float epi_finish(const GemmParams& p, float o, int64_
     return activate(o, p.act);
 }
 
+// Quantised codes of a final binary32 value (the formats of fg_quant):
+//   bf16: the bfloat16 nearest to x, ties to even, computed on the bit
+//         pattern (adding 0x7FFF plus the kept half's lowest bit carries into
+//         the upper half exactly when the dropped half is above the tie, or at
+//         it with an odd upper half; infinities stay, overflow carries into
+//         the exponent and gives infinity); every NaN becomes 0x7FC0.
+//   int8_row: clamp(round_half_even(x * s), -128, 127) on the binary32
+//         product; NaN gives 0.
+__device__ __forceinline__ uint32_t bf16_code(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t int8_code(float x, float s) {
+    float y = __builtin_rintf(x * s);
+    y = (y == y) ? y : 0.f;  // NaN
+    y = fminf(fmaxf(y, -128.f), 127.f);
+    return (uint32_t)(int32_t)y & 0xFFu;
+}
+__device__ __forceinline__ uint32_t quant_code(const GemmParams& p, float x, float s) {
+    return p.qkind == QUANT_BF16 ? bf16_code(x) : int8_code(x, s);
+}
+
+// Q(i, j) of the final value v (plain global store; the callers' i < M,
+// j < N keep it inside the caller's Q).
+__device__ __forceinline__ void quant_store1(const GemmParams& p, int64_t i, int64_t j, float v) {
+    const int64_t e = i * p.ldq + j;
+    if (p.qkind == QUANT_BF16)
+        static_cast<uint16_t*>(p.qout)[e] = (uint16_t)bf16_code(v);
+    else
+        static_cast<uint8_t*>(p.qout)[e] = (uint8_t)int8_code(v, p.qscale[i]);
+}
+
 // C element (i, j) from its plain product sum `acc` and its old value (read
-// only when beta != 0), with or without the fused epilogue.
+// only when beta != 0), with or without the fused epilogue; with FLAG_QUANT
+// the quantised code of the result is stored to Q(i, j) as well (QUANT: the
+// caller's kernel takes quantised calls; the vector-ALU kernel, whose 64
+// accumulators per thread went to scratch memory with that code beside its
+// stores, does not).
+template <bool QUANT = true>
 __device__ __forceinline__ float epilogue_value(const GemmParams& p, float acc, float cin,
                                                 bool beta0, int64_t i, int64_t j) {
     if (p.flags & FLAG_EPI) {
         float o = epi_scale(p, i, j) * acc;
         if (!beta0) o += p.beta * cin;
-        return epi_finish(p, o, i, j);
+        o = epi_finish(p, o, i, j);
+        if constexpr (QUANT)
+            if (p.flags & FLAG_QUANT) quant_store1(p, i, j, o);
+        return o;
     }
     float o = p.alpha * acc;
     if (!beta0) o += p.beta * cin;

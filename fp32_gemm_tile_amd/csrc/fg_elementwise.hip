@@ -1,7 +1,7 @@
 // The memory-bound kernels around the GEMM proper:
 //   * scale: C = beta * C (C = 0 without reading C when beta == 0), the
 //     whole result when K == 0 or alpha == 0 (with the fused epilogue:
-//     C = act(beta * C + u_i + w_j));
+//     C = act(beta * C + u_i + w_j); with a quantised output, Q from it);
 //   * split-K reduction: C = alpha * (W_0 + W_1 + ... + W_{S-1}) + beta * C,
 //     summing the per-split partial products in ascending split order, so
 //     the result does not depend on scheduling; the fused epilogue, when
@@ -24,6 +24,7 @@ __global__ void __launch_bounds__(256) scale_kernel(GemmParams p) {
         float* c = p.C + i * p.ldc + j;
         float o = beta0 ? 0.f : p.beta * *c;
         if (p.flags & FLAG_EPI) o = epi_finish(p, o, i, j);
+        if (p.flags & FLAG_QUANT) quant_store1(p, i, j, o);
         *c = o;
     }
 }

@@ -39,7 +39,16 @@ struct GemmParams {
     const float* row_bias;   // u, M floats
     const float* col_bias;   // w, N floats
     int32_t act;             // ACT_* below
+    // Quantised second output (FLAG_QUANT, which comes with FLAG_EPI): Q(i, j)
+    // = quantize(final C(i, j)) at qout + (i * ldq + j) elements of QUANT_*.
+    void* qout;
+    int32_t ldq;
+    int32_t qkind;           // QUANT_* below
+    const float* qscale;     // QUANT_INT8_ROW: s_i, M floats
+    int64_t q_extent;        // elements from qout to one past the last one written
 };
+
+enum : int32_t { QUANT_NONE = 0, QUANT_BF16 = 1, QUANT_INT8_ROW = 2 };
 
 enum : int32_t { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_SILU = 3 };
 
@@ -54,6 +63,8 @@ enum : int32_t {
     FLAG_TILE_WS = 128,  // write each (tile, split) partial to its own dense
                          // BM x BN slot of C (ldc = BN): slot
                          // (tile id - tile_base) * splits + split
+    FLAG_QUANT = 256,  // also write Q = quantize(C) (set together with FLAG_EPI)
+    FLAG_VEC_Q = 512,  // Q rows start aligned to 4 elements: vector stores
 };
 
 // Launchers: enqueue one kernel on `stream`; return the HIP launch status.

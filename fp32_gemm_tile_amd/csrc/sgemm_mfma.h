@@ -337,6 +337,11 @@ sgemm_mfma_kernel(GemmParams p) {
     using acc_t = typename Mfma<MR>::acc_t;
     constexpr int KPL = OpA::kKPL;
     constexpr int NREG = Mfma<MR>::kRegs;
+    // The quantised second output (FLAG_QUANT) is compiled in only where the
+    // accumulators leave room for it: with 256 accumulator registers per
+    // lane its store loops pushed the accumulators to scratch memory. The
+    // host sends quantised calls to other entries (fg_api.cpp).
+    constexpr bool kQuant = MB * NB * NREG <= 128;
 
     __shared__ f4 smem[NS * (OpA::kStage + OpB::kStage) / 4];
     float* sA = reinterpret_cast<float*>(smem);
@@ -523,7 +528,8 @@ sgemm_mfma_kernel(GemmParams p) {
     }
 
     // Epilogue: C = alpha * acc + beta * C, 128-bit where possible, or with
-    // FLAG_EPI C = act(alpha * r_i * c_j * acc + beta * C + u_i + w_j). Wide
+    // FLAG_EPI C = act(alpha * r_i * c_j * acc + beta * C + u_i + w_j) (and,
+    // with FLAG_QUANT, Q = quantize(C) beside it). Wide
     // stores carry the non-temporal hint: C is written once (16384^2 x 256,
     // which writes 1 GiB of C: 1.122 -> 1.079 ms).
     // Accumulator register r of a block, lane (i = lane % MR, h = lane / MR),
@@ -600,15 +606,20 @@ sgemm_mfma_kernel(GemmParams p) {
         // element gets one inlined activation; the old C is read (and the
         // result stored) as one vector when the lane's columns allow, else
         // element by element.
-        static_assert(2 * (BM + BN) <= NS * (OpA::kStage + OpB::kStage), "vectors fit in LDS");
-        float* const vr = sA;           // r: BM, then u: BM, then c: BN, then w: BN
+        static_assert(3 * BM + 2 * BN <= NS * (OpA::kStage + OpB::kStage), "vectors fit in LDS");
+        // r: BM, then u: BM, then c: BN, then w: BN, then the quantiser's row
+        // factors s: BM
+        float* const vr = sA;
         __syncthreads();                // every wave is done with the operand ring
         const int etid = wave * 64 + elane;
+        const bool quant = kQuant && (p.flags & FLAG_QUANT);
+        const bool int8q = quant && p.qkind == QUANT_INT8_ROW;
         for (int t = etid; t < BM; t += NT) {
             const int64_t i = (int64_t)m0 + t;
             const bool in = i < p.M;
             vr[t] = (p.row_scale && in) ? p.row_scale[i] : 1.f;
             vr[BM + t] = (p.row_bias && in) ? p.row_bias[i] : 0.f;
+            vr[2 * BM + 2 * BN + t] = (int8q && in) ? p.qscale[i] : 1.f;
         }
         for (int t = etid; t < BN; t += NT) {
             const int64_t j = (int64_t)n0 + t;
@@ -623,10 +634,62 @@ sgemm_mfma_kernel(GemmParams p) {
             csc[b] = vr[2 * BM + col0 + b];
             cbi[b] = vr[2 * BM + BN + col0 + b];
         }
+        // Q of this tile: a buffer from the tile origin to the end of Q;
+        // element (row, col) of the tile at byte (row * ldq + col) * esize.
+        // A lane's NB codes are one store when Q's rows are aligned to 4
+        // elements (FLAG_VEC_Q; col0 is a multiple of NB) and all NB columns
+        // are inside N.
+        const int qes = p.qkind == QUANT_BF16 ? 2 : 1;
+        const int64_t q_org = (int64_t)m0 * p.ldq + n0;
+        const __amdgpu_buffer_rsrc_t rq =
+            make_rsrc_bytes(static_cast<char*>(p.qout) + (quant ? q_org * qes : 0),
+                            quant ? (p.q_extent - q_org) * qes : 0);
+        const bool vec_q = (p.flags & FLAG_VEC_Q) && cols_left >= NB;
+        auto store_q = [&](auto qtag, int row, const float (&v)[NB]) __attribute__((always_inline)) {
+            constexpr int QK = decltype(qtag)::value;
+            const float qs = vr[2 * BM + 2 * BN + row];
+            const uint32_t qoff = (uint32_t)(row * p.ldq + col0) * (uint32_t)qes;
+            uint32_t code[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                code[b] = QK == QUANT_BF16 ? bf16_code(v[b]) : int8_code(v[b], qs);
+            if constexpr (NB > 1) {
+                if (vec_q) {
+                    if constexpr (QK == QUANT_BF16) {
+                        if constexpr (NB == 4) {
+                            f2 w2 = {__builtin_bit_cast(float, code[0] | (code[1] << 16)),
+                                     __builtin_bit_cast(float, code[2] | (code[3] << 16))};
+                            st2(rq, qoff, w2);
+                        } else {
+                            __builtin_amdgcn_raw_buffer_store_b32(code[0] | (code[1] << 16), rq,
+                                                                  qoff, 0, 0);
+                        }
+                    } else {
+                        if constexpr (NB == 4)
+                            __builtin_amdgcn_raw_buffer_store_b32(
+                                code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24), rq,
+                                qoff, 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b16(
+                                (uint16_t)(code[0] | (code[1] << 8)), rq, qoff, 0, 0);
+                    }
+                    return;
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (b >= cols_left) continue;
+                if constexpr (QK == QUANT_BF16)
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)code[b], rq, qoff + 2 * b, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code[b], rq, qoff + b, 0, 0);
+            }
+        };
         // One copy of the store loop per activation, picked once (a per-element
         // choice cost a chain of branches around every element).
-        auto store_tile = [&](auto tag) {
+        auto store_tile = [&](auto tag, auto qtag) {
             constexpr int ACT = decltype(tag)::value;
+            constexpr int QK = decltype(qtag)::value;
 #pragma unroll
             for (int a = 0; a < MB; ++a) {
 #pragma unroll
@@ -660,6 +723,7 @@ sgemm_mfma_kernel(GemmParams p) {
                     }
 #pragma unroll
                     for (int b = 0; b < NB; ++b) v[b] = activate_t<ACT>((v[b] + rbi) + cbi[b]);
+                    if constexpr (QK != QUANT_NONE) store_q(qtag, row, v);
                     if constexpr (NB == 4) {
                         if (full_vec) {
                             st4_nt(rc, off, f4{v[0], v[1], v[2], v[3]});
@@ -672,12 +736,28 @@ sgemm_mfma_kernel(GemmParams p) {
                 }
             }
         };
-        switch (p.act) {
-            case ACT_RELU: store_tile(ActTag<ACT_RELU>{}); break;
-            case ACT_GELU: store_tile(ActTag<ACT_GELU>{}); break;
-            case ACT_SILU: store_tile(ActTag<ACT_SILU>{}); break;
-            default: store_tile(ActTag<ACT_NONE>{}); break;
+        // One copy of the store loop per activation and quantised format,
+        // chosen by plain switches (through a further generic lambda the
+        // compiler kept the accumulators in scratch memory).
+#define FG_STORE_BY_ACT(QK)                                                               \
+    switch (p.act) {                                                                     \
+        case ACT_RELU: store_tile(ActTag<ACT_RELU>{}, ActTag<QK>{}); break;              \
+        case ACT_GELU: store_tile(ActTag<ACT_GELU>{}, ActTag<QK>{}); break;              \
+        case ACT_SILU: store_tile(ActTag<ACT_SILU>{}, ActTag<QK>{}); break;              \
+        default: store_tile(ActTag<ACT_NONE>{}, ActTag<QK>{}); break;                    \
+    }
+        if constexpr (kQuant) {
+            if (!quant) {
+                FG_STORE_BY_ACT(QUANT_NONE)
+            } else if (p.qkind == QUANT_BF16) {
+                FG_STORE_BY_ACT(QUANT_BF16)
+            } else {
+                FG_STORE_BY_ACT(QUANT_INT8_ROW)
+            }
+        } else {
+            FG_STORE_BY_ACT(QUANT_NONE)
         }
+#undef FG_STORE_BY_ACT
     }
 }
 

@@ -181,7 +181,7 @@ sgemm_valu_kernel(GemmParams p) {
                 f4 o;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    o[j] = epilogue_value(p, acc[i][4 * g + j], cin[j], beta0, (int64_t)m0 + row,
+                    o[j] = epilogue_value<false>(p, acc[i][4 * g + j], cin[j], beta0, (int64_t)m0 + row,
                                           (int64_t)n0 + col + j);
                 st4(rc, off, o);
             } else {
@@ -190,7 +190,7 @@ sgemm_valu_kernel(GemmParams p) {
                     if (n0 + col + j < p.N) {
                         const float cin = beta0 ? 0.f : ld1(rc, off + 4 * j);
                         st1(rc, off + 4 * j,
-                            epilogue_value(p, acc[i][4 * g + j], cin, beta0, (int64_t)m0 + row,
+                            epilogue_value<false>(p, acc[i][4 * g + j], cin, beta0, (int64_t)m0 + row,
                                            (int64_t)n0 + col + j));
                     }
                 }

@@ -236,6 +236,57 @@ fg_status fg_sgemm_fused(fg_op transA, fg_op transB, int64_t M, int64_t N, int64
                          float* C, int64_t ldc, const fg_epilogue* epilogue,
                          hipStream_t stream, int32_t config_id);
 
+/* Formats of the quantised second output. */
+typedef enum fg_quant_kind {
+    FG_QUANT_NONE = 0,
+    FG_QUANT_BF16 = 1,    /* uint16 codes: the bfloat16 nearest to C(i,j), ties to
+                             even; overflow rounds to infinity, infinities stay,
+                             every NaN becomes 0x7FC0 */
+    FG_QUANT_INT8_ROW = 2 /* int8 codes: clamp(round_half_even(fl32(C(i,j) * s_i)),
+                             -128, 127) with the caller's factor s_i of row i
+                             (e.g. 127 / max_j |C(i,j)|); NaN gives 0 */
+} fg_quant_kind;
+
+/* Where and how fg_sgemm_quant writes Q. */
+typedef struct fg_quant {
+    int32_t kind;            /* fg_quant_kind */
+    void* out;               /* Q: device memory owned by the caller, M rows of
+                                ldq elements (2 bytes each for FG_QUANT_BF16, 1
+                                for FG_QUANT_INT8_ROW); must not overlap A, B, C */
+    int64_t ldq;             /* elements, >= max(1, N) */
+    const float* row_factor; /* FG_QUANT_INT8_ROW: s, M floats (device memory) */
+} fg_quant;
+
+/*
+ * fg_sgemm_quant: fg_sgemm_fused that also writes a quantised copy of the
+ * result to a second buffer, in the same store ("Optimising fp32 GEMM on
+ * A100", section "Performance comparison": quantisation is among the
+ * operations fused into a GEMM's epilogue). C is written exactly as
+ * fg_sgemm_fused writes it (binary32); then Q(i,j) = quantize(C(i,j)) for
+ * every 0 <= i < M, 0 <= j < N, from that binary32 value. Elements of Q's
+ * rows past N are not touched. 4-element-aligned rows of Q (ldq a multiple
+ * of 4, out aligned to 4 elements) are written with vector stores.
+ *
+ * Arguments 1-13 as for fg_sgemm, then:
+ *   14 epilogue  : NULL or as for fg_sgemm_fused
+ *   15 quant     : NULL or kind FG_QUANT_NONE: same as fg_sgemm_fused; else
+ *                  out non-NULL (when M, N > 0), ldq >= max(1, N) and at most
+ *                  FG_MAX_LD, row_factor non-NULL for FG_QUANT_INT8_ROW
+ *   16 stream
+ *   17 config_id : -1 = automatic among the entries that write Q, else a
+ *                  table index; the entries that do not (the vector-ALU
+ *                  kernels, and matrix-core tiles whose accumulators take more
+ *                  than 128 registers per lane: the 256 x 256 tile) are
+ *                  FG_ERR_INVALID_ARG here
+ * Quick returns as for fg_sgemm_fused, except that (K == 0 or alpha == 0)
+ * with beta == 1 still writes Q (from C as it is). No split-K here.
+ */
+fg_status fg_sgemm_quant(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                         float alpha, const float* A, int64_t lda,
+                         const float* B, int64_t ldb, float beta,
+                         float* C, int64_t ldc, const fg_epilogue* epilogue,
+                         const fg_quant* quant, hipStream_t stream, int32_t config_id);
+
 /*
  * fg_sgemm_streamk: fg_sgemm with stream-K style scheduling of the last,
  * partial round of output tiles ("Matmul II: register blocking, warp tiling,

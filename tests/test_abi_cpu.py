@@ -460,6 +460,32 @@ assert st in NO_DEVICE, st
 """)
 
 
+def test_quant_validation_needs_no_gpu():
+    """fg_sgemm_quant checks its quantised-output description (argument 15)
+    before any device work; an empty result needs nothing."""
+    q = fg.make_quant("bf16", 4096, 4)
+    call = lambda quant, M=4, N=4: fg.fg_sgemm_quant(0, 0, M, N, 4, 1.0, 16, 4, 16, N, 0.0, 16,
+                                                     N, None, quant, 0, -1)
+    assert call(fg.make_quant(7, 4096, 4)) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 15
+    assert call(fg.make_quant("bf16", 4096, 3)) == fg.FG_ERR_INVALID_ARG
+    assert fg.fg_last_bad_arg() == 15
+    assert call(fg.make_quant("bf16", 0, 4)) == fg.FG_ERR_INVALID_ARG
+    assert call(fg.make_quant("int8_row", 4096, 4, 0)) == fg.FG_ERR_INVALID_ARG
+    assert fg.fg_last_bad_arg() == 15
+    assert call(fg.make_quant("bf16", 4096, fg.FG_MAX_LD + 4)) == fg.FG_ERR_UNSUPPORTED
+    assert call(q, M=0) == fg.FG_OK
+    # a forced entry without the quantised store (the vector-ALU kernel) is
+    # refused before the device check, as argument 17
+    valu = next(c["id"] for c in fg.configs() if c["kind"] == fg.FG_KIND_VALU)
+    st = fg.fg_sgemm_quant(0, 0, 4, 4, 4, 1.0, 16, 4, 16, 4, 0.0, 16, 4, None, q, 0, valu)
+    assert st == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 17
+    run_without_gpu("""
+q = fg.make_quant("int8_row", 4096, 4, 8192)
+st = fg.fg_sgemm_quant(0, 0, 4, 4, 0, 1.0, 16, 4, 16, 4, 1.0, 16, 4, None, q, 0, -1)
+assert st in NO_DEVICE, st
+""")
+
+
 def test_raster_setting_validation():
     """fg_set_raster changes the tile order only through an explicit call;
     nothing in the environment does."""
