@@ -18,6 +18,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C5a]
                        [--suite] [--calibrate] [--splitk [S]] [--streamk] [--cold]
                        [--no-cpu] [--no-probes] [--no-extras] [--copy-probe]
                        [--config ID] [--group-m G] [--xcd-remap 0|1]
+                       [--epilogue ACT] [--quant bf16|int8_row]
 """
 from __future__ import annotations
 
@@ -70,7 +71,7 @@ def load_traffic(workload, kernel_config):
 
 
 def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock=False,
-             epilogue=None, streamk=False, min_warm_s=0.0, keep_output=False):
+             epilogue=None, streamk=False, min_warm_s=0.0, keep_output=False, quant=None):
     """Time `steps` calls on the current stream with a HIP event pair around
     each call. Warm (default): the calls run back to back and the mean is the
     whole range over `steps`. Cold: a 512 MiB device write runs before each
@@ -96,6 +97,15 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock
         sk_bytes = fg.fg_sgemm_streamk_workspace_size(w.transA, w.transB, w.M, w.N, w.K,
                                                       dA.data_ptr(), w.LDA, dB.data_ptr(), w.LDB)
         sk_ws = torch.empty(max(sk_bytes, 16) // 4, dtype=torch.float32, device="cuda")
+    qdesc, qbuf = None, None
+    if quant is not None:
+        # Q in its own buffer, rows aligned to 4 elements; int8 factors of
+        # order 127 / max |C| for these inputs (the codes' values do not
+        # change the work)
+        esize = 2 if quant == "bf16" else 1
+        qbuf = torch.empty(w.M * w.N * esize + 16, dtype=torch.uint8, device="cuda")
+        qs = torch.full((w.M,), 127.0 / max(1.0, 0.6 * w.K ** 0.5), device="cuda")
+        qdesc = fg.make_quant(quant, qbuf.data_ptr(), w.N, qs.data_ptr())
     epi = None
     if epilogue is not None:
         # every vector present: the most work the fused epilogue can do
@@ -113,6 +123,10 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock
             st = fg.fg_sgemm_streamk(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
                                      w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
                                      sk_ws.data_ptr(), sk_bytes, sp)
+        elif qdesc is not None:
+            st = fg.fg_sgemm_quant(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
+                                   w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
+                                   epi, qdesc, sp, config)
         elif epi is not None:
             st = fg.fg_sgemm_fused(w.transA, w.transB, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
                                    w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
@@ -362,11 +376,12 @@ def copy_probe(nbytes=1 << 30, reps=3):
 
 def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False, cold=False,
             sample_clock=False, epilogue=None, streamk=False, min_warm_s=0.0,
-            keep_output=False):
+            keep_output=False, quant=None):
     from fp32_gemm_tile_amd import workloads as wl
     w = wl.WORKLOADS[name] if isinstance(name, str) else name
     g = time_gpu(w, steps, warmup, config, splitk, cold, sample_clock, epilogue, streamk,
-                 min_warm_s, keep_output=with_cpu or keep_output)
+                 min_warm_s, keep_output=(with_cpu or keep_output) and quant is None,
+                 quant=quant)
     tflops = w.flops / (g["ms_per_launch"] * 1e-3) / 1e12
     gbs = w.compulsory_bytes / (g["ms_per_launch"] * 1e-3) / 1e9
     traffic = load_traffic(name, g["config"])
@@ -402,6 +417,7 @@ def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False, cold=False,
         "tflops_at_median": round(w.flops / (g["ms_median"] * 1e-3) / 1e12, 3),
         "caches": "cold (512 MiB written before each call)" if cold else "warm",
         "epilogue": epilogue or "alpha/beta only",
+        "quantised_output": quant,
         "gpu_clock_mhz_under_load": g["clock_mhz"],
         "hbm_gbs_compulsory": round(gbs, 1),
         "roofline": roof,
@@ -437,6 +453,8 @@ def main():
     ap.add_argument("--epilogue", choices=("none", "relu", "gelu", "silu"), default=None,
                     help="time fg_sgemm_fused with row/column scales and biases and this "
                          "activation")
+    ap.add_argument("--quant", choices=("bf16", "int8_row"), default=None,
+                    help="time fg_sgemm_quant: C plus a quantised copy Q in this format")
     ap.add_argument("--streamk", action="store_true",
                     help="time fg_sgemm_streamk (split tail round; workspace as the library "
                          "asks)")
@@ -449,6 +467,9 @@ def main():
                     help="time every table entry on every workload (one line each)")
     ap.add_argument("--no-extras", action="store_true",
                     help="with the default workload, skip the 4096^3 and row-block lines")
+    ap.add_argument("--few-row-threads", type=int, default=0, choices=(0, 256, 512, 1024),
+                    help="workgroup size of the few-row kernel, B stored K x N "
+                         "(fg_set_few_row_threads; 0 = library default)")
     ap.add_argument("--group-m", type=int, default=0,
                     help="raster band height in tile rows (fg_set_raster; 0 = library default)")
     ap.add_argument("--xcd-remap", type=int, choices=(0, 1), default=1,
@@ -470,14 +491,16 @@ def main():
         sys.exit(1)
     import fp32_gemm_tile_amd as fg
     fg.load_library()
-    if fg.fg_set_raster(args.group_m, args.xcd_remap) != fg.FG_OK:
+    if fg.fg_set_raster(args.group_m, args.xcd_remap) != fg.FG_OK or \
+            fg.fg_set_few_row_threads(args.few_row_threads) != fg.FG_OK:
         print(f"bench.py: {fg.fg_last_error()}", file=sys.stderr)
         sys.exit(2)
 
     if args.suite or args.calibrate:
         ids = range(fg.fg_num_configs()) if args.calibrate else [args.config]
         from fp32_gemm_tile_amd import workloads as wl
-        names = ("C1", "C2", "C3", "C4", "C5a", "C5b", "C6", "S8", "G1", "G1T", "G8")
+        names = ("C1", "C2", "C3", "C4", "C5a", "C5b", "C6", "S8", "G1", "G1T", "G8", "G8T",
+                 "G32")
         for name in names:
             for cid in ids:
                 # The few-row kernel re-reads op(B) once per 8 rows of C: far
@@ -486,10 +509,12 @@ def main():
                         and wl.WORKLOADS[name].M > 2048:
                     continue
                 r = run_one(name, args.steps, args.warmup, False, cid, _splitk_arg(args),
-                            epilogue=args.epilogue, streamk=args.streamk, min_warm_s=0.2)
+                            epilogue=args.epilogue, streamk=args.streamk, min_warm_s=0.2,
+                            quant=args.quant)
                 print(json.dumps({"workload": name, "config": r["config"]["kernel_config"],
                                   "forced": cid, "splitk": _splitk_arg(args),
                                   "epilogue": args.epilogue, "streamk": args.streamk,
+                                  "quant": args.quant,
                                   "tflops": r["value"],
                                   "ms": r["ms_per_step"], "pct": r["pct_of_fp32_peak"],
                                   "roofline": r["roofline"]}),
@@ -501,7 +526,7 @@ def main():
     with_cpu = not args.no_cpu
     r = run_one(args.workload, args.steps, args.warmup, False, args.config, _splitk_arg(args),
                 args.cold, sample_clock=not args.no_probes, epilogue=args.epilogue,
-                streamk=args.streamk, keep_output=with_cpu)
+                streamk=args.streamk, keep_output=with_cpu, quant=args.quant)
     # The 4096^3 shape of the metric, and one GPU's row block of 8192^3 split
     # over eight GPUs, timed in the same run.
     if args.workload == "C5a" and not args.no_extras:

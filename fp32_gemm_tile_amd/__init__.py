@@ -163,6 +163,8 @@ def load_library(path: str = LIB_PATH):
     lib.fg_set_raster.restype = i32
     lib.fg_get_raster.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.fg_get_raster.restype = i32
+    lib.fg_set_few_row_threads.argtypes = [i32]
+    lib.fg_set_few_row_threads.restype = i32
     lib.fg_set_streamk_policy.argtypes = [i32]
     lib.fg_set_streamk_policy.restype = i32
     lib.fg_probe_mfma.argtypes = [i32, i32, vp, vp]
@@ -332,6 +334,12 @@ def fg_set_raster(group_m, xcd_remap) -> int:
     """Raster order of the matrix-core kernels (fp32gemm_tune.h): band height
     in tile rows (0 = default) and the XCD renumbering (1 on, 0 off)."""
     return load_library().fg_set_raster(group_m, xcd_remap)
+
+
+def fg_set_few_row_threads(threads) -> int:
+    """Workgroup size of the few-row kernel, B stored K x N (fp32gemm_tune.h):
+    0 = automatic, else 256, 512 or 1024."""
+    return load_library().fg_set_few_row_threads(threads)
 
 
 def fg_get_raster():

@@ -354,6 +354,9 @@ int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_s
 // renumbered so each XCD gets a contiguous run of tiles.
 constexpr int kDefaultGroupM = 4;
 std::atomic<int> g_group_m{kDefaultGroupM};
+// Workgroup size of the few-row kernel's K x N form (fg_set_few_row_threads;
+// 0 = automatic).
+std::atomic<int> g_few_row_threads{0};
 std::atomic<int> g_xcd_remap{1};
 
 // ---------------------------------------------------------------------------
@@ -707,7 +710,7 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
     } else if (en.cfg.kind == FG_KIND_MFMA) {
         e = fg::launch_mfma(en.variant, transA, transB, p, stream);
     } else if (en.cfg.kind == FG_KIND_SKINNY) {
-        e = fg::launch_skinny(transA, transB, p, stream);
+        e = fg::launch_skinny(transA, transB, p, stream, g_few_row_threads.load());
     } else {
         e = fg::launch_valu(en.variant, transA, transB, p, stream);
     }
@@ -887,6 +890,14 @@ fg_status fg_set_raster(int32_t group_m, int32_t xcd_remap) {
         return fail(FG_ERR_INVALID_ARG, 2, "xcd_remap must be 0 or 1");
     g_group_m.store(group_m == 0 ? kDefaultGroupM : group_m);
     g_xcd_remap.store(xcd_remap);
+    return FG_OK;
+}
+
+fg_status fg_set_few_row_threads(int32_t threads) {
+    clear_error();
+    if (threads != 0 && threads != 256 && threads != 512 && threads != 1024)
+        return fail(FG_ERR_INVALID_ARG, 1, "threads must be 0, 256, 512 or 1024");
+    g_few_row_threads.store(threads);
     return FG_OK;
 }
 

@@ -80,8 +80,9 @@ hipError_t launch_mfma_tiles(int id, int trans_a, int trans_b, const GemmParams&
 hipError_t launch_valu(int variant, int trans_a, int trans_b, const GemmParams& p,
                        hipStream_t stream);
 // Few-row GEMM (memory-bound): blocks of up to 8 rows of C, op(B) streamed
-// once per block.
-hipError_t launch_skinny(int trans_a, int trans_b, const GemmParams& p, hipStream_t stream);
+// once per block. threads: workgroup size of the K x N form (0: automatic).
+hipError_t launch_skinny(int trans_a, int trans_b, const GemmParams& p, hipStream_t stream,
+                         int threads = 0);
 // C = beta * C (beta == 0: C = 0 without reading it); for K == 0 or alpha == 0.
 // With FLAG_EPI: C = act(beta * C + u_i + w_j).
 hipError_t launch_scale(const GemmParams& p, hipStream_t stream);

@@ -53,13 +53,17 @@ __device__ __forceinline__ float group_sum(float v) {
 // PIPE: software-pipelined k loop (two blocks of op(B) in flight per wave,
 // more registers); for grids of at most a few workgroups per CU, where the
 // loads' latency is not hidden by other workgroups.
-template <int MR, int TA, bool VEC, bool PIPE>
-__global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p) {
+// NT: work-items per workgroup (256, 512 or 1024): its NT / 8 k classes split
+// K inside the workgroup, so a larger workgroup keeps more of op(B) in flight
+// per CU when the grid has about one workgroup per CU.
+template <int MR, int TA, bool VEC, bool PIPE, int NT>
+__global__ void __launch_bounds__(NT) skinny_mn_kernel(GemmParams p) {
     // B stored K x N. Workgroup: columns [n0, n0 + 32), rows [m0, m0 + MR).
-    constexpr int NW = kSkinnyThreads / 64;
+    constexpr int NW = NT / 64;
+    constexpr int NCLS = NT / 8;  // k classes
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane & 7;                 // column group: 4 columns
-    const int rcls = (lane >> 3) + 8 * wave;  // k class 0..31
+    const int rcls = (lane >> 3) + 8 * wave;  // k class 0 .. NCLS-1
     const int n0 = blockIdx.x * 32, m0 = blockIdx.y * MR;
     const int rows_left = p.M - m0;
 
@@ -74,7 +78,7 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
     // each lane then reads the MR values of its k with 128-bit LDS reads,
     // instead of MR scattered global loads per k. Two buffers: one barrier
     // per k block.
-    constexpr int KB = 32 * kUnrollMN;  // k per block
+    constexpr int KB = NCLS * kUnrollMN;  // k per block
     constexpr bool STAGE_A = MR > 1;
     __shared__ __attribute__((aligned(16))) float sa[STAGE_A ? 2 : 1][KB][MR];
 
@@ -98,7 +102,7 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
         }
 #pragma unroll
         for (int u = 0; u < kUnrollMN; ++u) {
-            const int kk = rcls + 32 * u;  // k - kb
+            const int kk = rcls + NCLS * u;  // k - kb
             const uint32_t off = (uint32_t)(kk * p.ldb + 4 * g) * 4u;
             const f4 z = {0.f, 0.f, 0.f, 0.f};
             b[u] = kb + kk < p.K ? ld4_guard(rb, off, 4 * g, p.N - n0, VEC) : z;
@@ -117,7 +121,7 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
 #pragma unroll
         for (int u = 0; u < kUnrollMN; ++u) {
-            const int kk = rcls + 32 * u;
+            const int kk = rcls + NCLS * u;
             float a[MR];
             if constexpr (STAGE_A) {
                 const float* src = &sa[it & 1][kk][0];
@@ -173,7 +177,7 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
     // Reduce over the 8 k classes of a wave (lane bits 3-5), then over the
     // waves through LDS, always in the same order.
     __shared__ float red[NW][MR][32];
-    static_assert(KB == kSkinnyThreads, "one staged k per thread");
+    static_assert(KB == NT, "one staged k per thread");
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
@@ -184,7 +188,7 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_mn_kernel(GemmParams p)
     __syncthreads();
     // One element of the MR x 32 block per thread (row t / 32, column t % 32):
     // the wave sums in fixed order, then the epilogue and a coalesced store.
-    static_assert(MR * 32 <= kSkinnyThreads, "one thread per element");
+    static_assert(MR * 32 <= NT, "one thread per element");
     {
         const int m = threadIdx.x >> 5, col = threadIdx.x & 31;
         if (m < MR && m < rows_left && col < p.N - n0) {
@@ -292,38 +296,63 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_k_kernel(GemmParams p) 
     }
 }
 
+template <int MR, int NT>
+void launch_mn(int ta, bool vec_b, bool pipe_req, dim3 grid, const GemmParams& p, hipStream_t s) {
+    const dim3 block(NT);
+    constexpr bool kCanPipe = NT < 1024;  // see launch_mr
+    const bool pipe = kCanPipe && pipe_req;
+    if (ta == 0) {
+        if (vec_b) {
+            if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, true, kCanPipe, NT>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, true, false, NT>), grid, block, 0, s, p);
+        } else {
+            if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, false, kCanPipe, NT>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, false, false, NT>), grid, block, 0, s, p);
+        }
+    } else {
+        if (vec_b) {
+            if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, true, kCanPipe, NT>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, true, false, NT>), grid, block, 0, s, p);
+        } else {
+            if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, false, kCanPipe, NT>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, false, false, NT>), grid, block, 0, s, p);
+        }
+    }
+}
+
 template <int MR>
-hipError_t launch_mr(int ta, int tb, const GemmParams& p, hipStream_t s) {
+hipError_t launch_mr(int ta, int tb, const GemmParams& p, hipStream_t s, int threads) {
     const bool vec_b = p.flags & FLAG_VEC_B;
     const int rblocks = (p.M + MR - 1) / MR;
     const dim3 block(kSkinnyThreads);
     if (tb == 0) {  // B stored K x N
         const dim3 grid((p.N + 31) / 32, rblocks);
+        const int64_t wgs = (int64_t)grid.x * grid.y;
+        // Workgroup size: `threads` when the caller forces one, else 512
+        // work-items when the grid has at most one workgroup per CU (twice
+        // the waves split K and keep more loads in flight), else 256.
+        // Measured on one MI355X (GB/s at 256 / 512 / 1024 work-items):
+        // 8 x 8192 x 8192 4377 / 5377 / 5350; 1 x 8192 x 8192 6266 / 6492 /
+        // 6201; 32 x 8192 x 8192 (1024 workgroups) 2816 / 2145 / 1507.
+        const int nt = threads > 0 ? threads : (wgs <= 256 ? 512 : 256);
         // Pipelined while the whole grid is resident at once (up to 3
-        // workgroups per CU, the pipelined kernel's occupancy; measured:
-        // 8 x 4096 x 4096 36.5 -> 32.8 us, 8 x 8192 x 8192 67.6 -> 62.6 us);
-        // beyond that the extra registers cost a round of workgroups
-        // (64 x 4096 x 4096, 1024 workgroups: 49 us plain, 69 pipelined).
-        // With one row the loop is light enough that the plain one streams
-        // as fast (1 x 8192 x 8192: 44.1 us plain, 45.8 pipelined).
-        const bool pipe = MR > 1 && (int64_t)grid.x * grid.y <= 3 * 256;
-        if (ta == 0) {
-            if (vec_b) {
-                if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, true, true>), grid, block, 0, s, p);
-                else hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, true, false>), grid, block, 0, s, p);
-            } else {
-                if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, false, true>), grid, block, 0, s, p);
-                else hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, false, false>), grid, block, 0, s, p);
-            }
-        } else {
-            if (vec_b) {
-                if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, true, true>), grid, block, 0, s, p);
-                else hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, true, false>), grid, block, 0, s, p);
-            } else {
-                if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, false, true>), grid, block, 0, s, p);
-                else hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, false, false>), grid, block, 0, s, p);
-            }
-        }
+        // workgroups of 256 per CU, the pipelined kernel's occupancy, or two
+        // of 512;
+        // measured: 8 x 4096 x 4096 36.5 -> 32.8 us, 8 x 8192 x 8192 67.6 ->
+        // 62.6 us); beyond that the extra registers cost a round of
+        // workgroups (64 x 4096 x 4096, 1024 workgroups: 49 us plain, 69
+        // pipelined). With one row the loop is light enough that the plain
+        // one streams as fast (1 x 8192 x 8192: 44.1 us plain, 45.8 pipelined).
+        // (1024 work-items leave a wave 128 registers: too few for the
+        // second register set, so that size is never pipelined)
+        const int64_t resident = nt == 512 ? 512 : 3 * 256;
+        const bool pipe = MR > 1 && nt < 1024 && wgs <= resident;
+        if (nt == 1024)
+            launch_mn<MR, 1024>(ta, vec_b, pipe, grid, p, s);
+        else if (nt == 512)
+            launch_mn<MR, 512>(ta, vec_b, pipe, grid, p, s);
+        else
+            launch_mn<MR, 256>(ta, vec_b, pipe, grid, p, s);
     } else {  // B stored N x K
         const int cols_per_wg = 4 * (kSkinnyThreads / 64);
         const dim3 grid((p.N + cols_per_wg - 1) / cols_per_wg, rblocks);
@@ -341,11 +370,13 @@ hipError_t launch_mr(int ta, int tb, const GemmParams& p, hipStream_t s) {
 }  // namespace
 
 // Rows per block: 1, 2, 4 or 8 (the smallest power of two >= M, capped at 8).
-hipError_t launch_skinny(int ta, int tb, const GemmParams& p, hipStream_t s) {
-    if (p.M <= 1) return launch_mr<1>(ta, tb, p, s);
-    if (p.M <= 2) return launch_mr<2>(ta, tb, p, s);
-    if (p.M <= 4) return launch_mr<4>(ta, tb, p, s);
-    return launch_mr<8>(ta, tb, p, s);
+// threads: workgroup size of the K x N kernel (0 = automatic, else 256, 512
+// or 1024).
+hipError_t launch_skinny(int ta, int tb, const GemmParams& p, hipStream_t s, int threads) {
+    if (p.M <= 1) return launch_mr<1>(ta, tb, p, s, threads);
+    if (p.M <= 2) return launch_mr<2>(ta, tb, p, s, threads);
+    if (p.M <= 4) return launch_mr<4>(ta, tb, p, s, threads);
+    return launch_mr<8>(ta, tb, p, s, threads);
 }
 
 }  // namespace fg

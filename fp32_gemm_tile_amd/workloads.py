@@ -108,6 +108,9 @@ WORKLOADS = {
     "G1T": Workload("G1T", 1, 8192, 8192, transB="T", seed=6,
                     note="GEMV with B stored N x K"),
     "G8": Workload("G8", 8, 8192, 8192, seed=7, note="8 rows times 8192 x 8192"),
+    "G8T": Workload("G8T", 8, 8192, 8192, transB="T", seed=7,
+                    note="8 rows, B stored N x K"),
+    "G32": Workload("G32", 32, 8192, 8192, seed=9, note="32 rows times 8192 x 8192"),
 }
 
 

@@ -63,6 +63,14 @@ fg_status fg_set_efficiency(int32_t config_id, double eff, double eff1);
  */
 fg_status fg_set_raster(int32_t group_m, int32_t xcd_remap);
 
+/*
+ * Workgroup size of the few-row kernel for B stored K x N (for measurements):
+ * 0 (default) picks 512 work-items when the grid has at most one workgroup
+ * per CU and 256 otherwise; 256, 512 or 1024 force that size for every later
+ * call in this process. FG_ERR_INVALID_ARG otherwise.
+ */
+fg_status fg_set_few_row_threads(int32_t threads);
+
 /* The current raster settings (arguments 1, 2: outputs, non-NULL). */
 fg_status fg_get_raster(int32_t* group_m, int32_t* xcd_remap);
 

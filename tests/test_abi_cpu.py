@@ -500,6 +500,10 @@ def test_raster_setting_validation():
         fg.fg_set_raster(0, 1)
     src = open(os.path.join(ROOT, "fp32_gemm_tile_amd", "csrc", "fg_api.cpp")).read()
     assert "getenv" not in src
+    for t in (0, 256, 512, 1024):
+        assert fg.fg_set_few_row_threads(t) == fg.FG_OK
+    assert fg.fg_set_few_row_threads(128) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 1
+    fg.fg_set_few_row_threads(0)
 
 
 def test_streamk_plan_and_validation():

@@ -77,9 +77,9 @@ def test_skinny_repeatable():
 @pytest.mark.parametrize("ta", ["N", "T"])
 def test_skinny_both_k_loops(ta):
     """B stored K x N takes the software-pipelined k loop on grids of at most
-    768 workgroups with more than one row per block, and the plain one
-    otherwise: both, with a ragged last k block
-    and K shorter than one block, against the oracle."""
+    768 workgroups of 256 (512 of 512) with more than one row per block, and
+    the plain one otherwise: both, with a ragged last k block and K shorter
+    than one block, against the oracle."""
     cid = skinny_id()
     for i, (M, N, K) in enumerate([(8, 1000, 777), (200, 8192, 300), (130, 2047, 100),
                                    (1, 9000, 2000), (3, 4000, 1500)]):
@@ -89,3 +89,28 @@ def test_skinny_both_k_loops(ta):
         A, B, C = wl.make_inputs(w)
         out, _ = run_fg(w, A, B, C, config=cid)
         check_full(w, A, B, C, out)
+
+
+@pytest.mark.parametrize("threads", [256, 512, 1024])
+@pytest.mark.parametrize("ta", ["N", "T"])
+def test_skinny_workgroup_sizes(threads, ta):
+    """B stored K x N with each workgroup size the kernel is built for (the
+    K split inside a workgroup grows with it): ragged M, N and K, alpha and
+    beta, against the oracle; integer inputs bit for bit."""
+    cid = skinny_id()
+    assert fg.fg_set_few_row_threads(threads) == fg.FG_OK
+    try:
+        for i, (M, N, K) in enumerate([(1, 1000, 3000), (8, 4100, 1025), (5, 300, 100),
+                                       (2, 8192, 4096), (8, 257, 2049)]):
+            w = wl.custom(M, N, K, ta, "N", alpha=1.5, beta=0.5, dist="normal", seed=140 + i)
+            A, B, C = wl.make_inputs(w)
+            out, _ = run_fg(w, A, B, C, config=cid)
+            check_full(w, A, B, C, out)
+        w = wl.custom(8, 777, 1500, ta, "N", alpha=2.0, beta=-1.0, dist="int8", seed=150)
+        A, B, C = wl.make_inputs(w)
+        out, _ = run_fg(w, A, B, C, config=cid)
+        cref, _ = oracle.gemm(ta, "N", w.M, w.N, w.K, w.alpha, A, w.LDA, B, w.LDB, w.beta, C,
+                              w.LDC)
+        assert np.array_equal(out.astype(np.float64), cref)
+    finally:
+        assert fg.fg_set_few_row_threads(0) == fg.FG_OK
