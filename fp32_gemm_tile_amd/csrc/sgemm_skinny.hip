@@ -27,7 +27,6 @@ namespace {
 
 constexpr int kSkinnyThreads = 256;
 constexpr int kUnrollMN = 8;  // k steps in flight per lane (B stored K x N)
-constexpr int kUnrollK = 2;   // 256-deep k blocks in flight per column (B stored N x K)
 
 // op(A)(i, k) for the rows of this block; rows past M read as 0.
 template <int MR, bool TA>
@@ -56,12 +55,14 @@ __device__ __forceinline__ float group_sum(float v) {
 // NT: work-items per workgroup (256, 512 or 1024): its NT / 8 k classes split
 // K inside the workgroup, so a larger workgroup keeps more of op(B) in flight
 // per CU when the grid has about one workgroup per CU.
-template <int MR, int TA, bool VEC, bool PIPE, int NT>
+// BIG: buffer resources rebased per k step (see load_block).
+template <int MR, int TA, bool VEC, bool PIPE, int NT, bool BIG>
 __global__ void __launch_bounds__(NT) skinny_mn_kernel(GemmParams p) {
     // B stored K x N. Workgroup: columns [n0, n0 + 32), rows [m0, m0 + MR).
     constexpr int NW = NT / 64;
     constexpr int NCLS = NT / 8;  // k classes
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane & 7;                 // column group: 4 columns
     const int rcls = (lane >> 3) + 8 * wave;  // k class 0 .. NCLS-1
     const int n0 = blockIdx.x * 32, m0 = blockIdx.y * MR;
@@ -86,26 +87,37 @@ __global__ void __launch_bounds__(NT) skinny_mn_kernel(GemmParams p) {
     // first, so that waiting for them leaves the B loads in flight) and its
     // kUnrollMN 128-bit pieces of op(B). Past K both read as 0.
     auto load_block = [&](int kb, float (&astage)[MR], f4 (&b)[kUnrollMN]) {
-        // Buffer resources based at this k block keep the 32-bit offsets small.
-        const int64_t a_org = TA ? (int64_t)kb * p.lda + m0 : (int64_t)m0 * p.lda + kb;
-        const int64_t b_org = (int64_t)kb * p.ldb + n0;
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_org, p.b_extent - b_org);
+        // Buffer resources are based at this k block, or with BIG (a leading
+        // dimension so large that 32-bit byte offsets across a whole block
+        // could pass 2^32) close to each access: this wave's k range of
+        // op(A), each k step of op(B).
         if constexpr (STAGE_A) {
-            const int kk = threadIdx.x;
-            if (kb + kk < p.K) {
-                load_a<MR, TA>(ra, p.lda, rows_left, kk, astage);
+            const int ka = BIG ? kb + 64 * wave : kb;
+            const int kt = BIG ? lane : (int)threadIdx.x;  // k - ka
+            const int64_t a_org = TA ? (int64_t)ka * p.lda + m0 : (int64_t)m0 * p.lda + ka;
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
+            if (ka + kt < p.K) {
+                load_a<MR, TA>(ra, p.lda, rows_left, kt, astage);
             } else {
 #pragma unroll
                 for (int m = 0; m < MR; ++m) astage[m] = 0.f;
             }
         }
+        const int64_t b_blk = (int64_t)kb * p.ldb + n0;
+        const __amdgpu_buffer_rsrc_t rb_blk = make_rsrc(p.B + b_blk, p.b_extent - b_blk);
 #pragma unroll
         for (int u = 0; u < kUnrollMN; ++u) {
-            const int kk = rcls + NCLS * u;  // k - kb
-            const uint32_t off = (uint32_t)(kk * p.ldb + 4 * g) * 4u;
+            const int ku = kb + NCLS * u;  // first k of this step
             const f4 z = {0.f, 0.f, 0.f, 0.f};
-            b[u] = kb + kk < p.K ? ld4_guard(rb, off, 4 * g, p.N - n0, VEC) : z;
+            if constexpr (BIG) {
+                const int64_t b_org = (int64_t)ku * p.ldb + n0;
+                const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_org, p.b_extent - b_org);
+                const uint32_t off = (uint32_t)(rcls * p.ldb + 4 * g) * 4u;
+                b[u] = ku + rcls < p.K ? ld4_guard(rb, off, 4 * g, p.N - n0, VEC) : z;
+            } else {
+                const uint32_t off = (uint32_t)((ku - kb + rcls) * p.ldb + 4 * g) * 4u;
+                b[u] = ku + rcls < p.K ? ld4_guard(rb_blk, off, 4 * g, p.N - n0, VEC) : z;
+            }
         }
     };
     // The FMAs of k block kb (op(A) from LDS buffer `it & 1`, or from memory
@@ -117,8 +129,6 @@ __global__ void __launch_bounds__(NT) skinny_mn_kernel(GemmParams p) {
             for (int m = 0; m < MR; ++m) dst[m] = astage[m];
             lds_barrier();
         }
-        const int64_t a_org = TA ? (int64_t)kb * p.lda + m0 : (int64_t)m0 * p.lda + kb;
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
 #pragma unroll
         for (int u = 0; u < kUnrollMN; ++u) {
             const int kk = rcls + NCLS * u;
@@ -136,7 +146,10 @@ __global__ void __launch_bounds__(NT) skinny_mn_kernel(GemmParams p) {
                     }
                 }
             } else if (kb + kk < p.K) {
-                load_a<MR, TA>(ra, p.lda, rows_left, kk, a);
+                const int ku = BIG ? kb + NCLS * u : kb;
+                const int64_t a_org = TA ? (int64_t)ku * p.lda + m0 : (int64_t)m0 * p.lda + ku;
+                const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
+                load_a<MR, TA>(ra, p.lda, rows_left, kb + kk - ku, a);
             } else {
 #pragma unroll
                 for (int m = 0; m < MR; ++m) a[m] = 0.f;
@@ -205,87 +218,133 @@ __global__ void __launch_bounds__(NT) skinny_mn_kernel(GemmParams p) {
     }
 }
 
-template <int MR, int TA, bool VEC>
+// B stored N x K. CW: columns per wave; KW: waves that share those columns
+// and split K between them (k blocks taken round robin, partial sums reduced
+// in LDS in a fixed order); UK: 256-deep k steps per block; PIPE: the loads
+// of the next block are issued before the FMAs of this one (two register
+// sets).
+template <int MR, int TA, bool VEC, int CW, int KW, int UK, bool PIPE>
 __global__ void __launch_bounds__(kSkinnyThreads) skinny_k_kernel(GemmParams p) {
-    // B stored N x K. Wave w of the workgroup: columns n0 + 4w .. n0 + 4w + 3,
-    // rows [m0, m0 + MR); lane L reads k = kb + 4L .. 4L + 3 of each column.
+    // Wave w of the workgroup: columns n0 .. n0 + CW - 1 of column group
+    // w / KW, k blocks j with j % KW == w % KW; rows [m0, m0 + MR). Lane L
+    // reads k = kb + 256 u + 4L .. 4L + 3 of each column.
     constexpr int NW = kSkinnyThreads / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n0 = (blockIdx.x * NW + wave) * 4, m0 = blockIdx.y * MR;
+    static_assert(NW % KW == 0, "waves split evenly over column groups");
+    constexpr int NG = NW / KW;  // column groups per workgroup
+    constexpr int KB = 256 * UK;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave / KW, phase = wave % KW;
+    const int n0 = (blockIdx.x * NG + grp) * CW, m0 = blockIdx.y * MR;
     const int rows_left = p.M - m0, cols_left = p.N - n0;
-
     const bool vec_a = !TA && (p.flags & FLAG_VEC_A);
-    float acc[MR][4];
+
+    float acc[MR][CW];
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[m][c] = 0.f;
+        for (int c = 0; c < CW; ++c) acc[m][c] = 0.f;
 
-    for (int kb = 0; kb < p.K; kb += 256 * kUnrollK) {
-        // Buffer resources based at this k block keep the 32-bit offsets small.
-        const int64_t a_org = TA ? (int64_t)kb * p.lda + m0 : (int64_t)m0 * p.lda + kb;
-        const int64_t b_org = (int64_t)n0 * p.ldb + kb;
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_org, p.b_extent - b_org);
-        const int k_left = p.K - kb;
-        f4 b[kUnrollK][4];
+    // One block's loads: op(A) first, then op(B), so that waiting for this
+    // block leaves the next block's loads (issued later) in flight. Past K
+    // everything reads as 0. Buffer resources are based at each 256-deep k
+    // step, so the 32-bit offsets stay below 256 * lda * 4 bytes.
+    auto load_block = [&](int kb, f4 (&a)[UK][MR], f4 (&b)[UK][CW]) {
 #pragma unroll
-        for (int u = 0; u < kUnrollK; ++u) {
-            const int kk = 256 * u + 4 * lane;  // k - kb
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const f4 z = {0.f, 0.f, 0.f, 0.f};
-                const uint32_t off = (uint32_t)(c * p.ldb + kk) * 4u;
-                b[u][c] = c < cols_left ? ld4_guard(rb, off, kk, k_left, VEC) : z;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnrollK; ++u) {
-            const int kk = 256 * u + 4 * lane;
-            f4 a[MR];
+        for (int u = 0; u < UK; ++u) {
+            const int ku = kb + 256 * u, kk = 4 * lane, left = p.K - ku;
+            const int64_t a_org = TA ? (int64_t)ku * p.lda + m0 : (int64_t)m0 * p.lda + ku;
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
+            const f4 z = {0.f, 0.f, 0.f, 0.f};
             if (vec_a) {
 #pragma unroll
-                for (int m = 0; m < MR; ++m) {
-                    const f4 z = {0.f, 0.f, 0.f, 0.f};
-                    a[m] = m < rows_left ? ld4_guard(ra, (uint32_t)(m * p.lda + kk) * 4u, kk,
-                                                     k_left, true)
-                                         : z;
-                }
+                for (int m = 0; m < MR; ++m)
+                    a[u][m] = m < rows_left
+                                  ? ld4_guard(ra, (uint32_t)(m * p.lda + kk) * 4u, kk, left, true)
+                                  : z;
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float t[MR];
-                    if (kk + e < k_left) {
+                    if (kk + e < left) {
                         load_a<MR, TA>(ra, p.lda, rows_left, kk + e, t);
                     } else {
 #pragma unroll
                         for (int m = 0; m < MR; ++m) t[m] = 0.f;
                     }
 #pragma unroll
-                    for (int m = 0; m < MR; ++m) a[m][e] = t[m];
+                    for (int m = 0; m < MR; ++m) a[u][m][e] = t[m];
                 }
             }
+        }
+        const int64_t b_org = (int64_t)n0 * p.ldb + kb;
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_org, p.b_extent - b_org);
+        const int k_left = p.K - kb;
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+            const int kk = 256 * u + 4 * lane;  // k - kb
+#pragma unroll
+            for (int c = 0; c < CW; ++c) {
+                const f4 z = {0.f, 0.f, 0.f, 0.f};
+                const uint32_t off = (uint32_t)(c * p.ldb + kk) * 4u;
+                b[u][c] = c < cols_left ? ld4_guard(rb, off, kk, k_left, VEC) : z;
+            }
+        }
+    };
+    auto compute_block = [&](const f4 (&a)[UK][MR], const f4 (&b)[UK][CW]) {
+#pragma unroll
+        for (int u = 0; u < UK; ++u)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
                 for (int m = 0; m < MR; ++m)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        acc[m][c] = __builtin_fmaf(a[m][e], b[u][c][e], acc[m][c]);
+                    for (int c = 0; c < CW; ++c)
+                        acc[m][c] = __builtin_fmaf(a[u][m][e], b[u][c][e], acc[m][c]);
+    };
+
+    const int k0 = phase * KB;
+    constexpr int KSTEP = KW * KB;
+    if constexpr (PIPE) {
+        f4 a0[UK][MR], a1[UK][MR], b0[UK][CW], b1[UK][CW];
+        if (k0 < p.K) load_block(k0, a0, b0);
+        for (int kb = k0; kb < p.K; kb += 2 * KSTEP) {
+            if (kb + KSTEP < p.K) load_block(kb + KSTEP, a1, b1);
+            compute_block(a0, b0);
+            if (kb + KSTEP >= p.K) break;
+            if (kb + 2 * KSTEP < p.K) load_block(kb + 2 * KSTEP, a0, b0);
+            compute_block(a1, b1);
+        }
+    } else {
+        for (int kb = k0; kb < p.K; kb += KSTEP) {
+            f4 a[UK][MR], b[UK][CW];
+            load_block(kb, a, b);
+            compute_block(a, b);
         }
     }
 
-    // Every lane ends up with every sum; lane 4m + c keeps element (m, c) and
-    // the MR x 4 elements go through the epilogue side by side.
+    // Every lane ends up with every sum of its wave; lane CW m + c keeps
+    // element (m, c). With KW > 1 the waves of a column group add their
+    // partial sums in phase order through LDS; the first wave of the group
+    // then runs the MR x CW elements through the epilogue side by side.
+    static_assert(MR * CW <= 64, "one lane per element");
     float mine = 0.f;
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < CW; ++c) {
             const float s = group_sum<0x3F>(acc[m][c]);
-            if (lane == 4 * m + c) mine = s;
+            if (lane == CW * m + c) mine = s;
         }
-    const int m = lane >> 2, c = lane & 3;
+    if constexpr (KW > 1) {
+        __shared__ float red[NW][64];
+        red[wave][lane] = mine;
+        __syncthreads();
+        if (phase != 0) return;
+#pragma unroll
+        for (int w = 1; w < KW; ++w) mine += red[wave + w][lane];
+    }
+    const int m = lane / CW, c = lane % CW;
     if (m < MR && m < rows_left && c < cols_left) {
         const int64_t c_org = (int64_t)m0 * p.ldc + n0;
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c_org, p.c_extent - c_org);
@@ -296,26 +355,35 @@ __global__ void __launch_bounds__(kSkinnyThreads) skinny_k_kernel(GemmParams p) 
     }
 }
 
-template <int MR, int NT>
+template <int MR, int TA, int CW, int KW, int UK, bool PIPE>
+void launch_k(bool vec_b, const GemmParams& p, hipStream_t s) {
+    constexpr int cols_per_wg = CW * (kSkinnyThreads / 64) / KW;
+    const dim3 grid((p.N + cols_per_wg - 1) / cols_per_wg, (p.M + MR - 1) / MR);
+    const dim3 block(kSkinnyThreads);
+    if (vec_b) hipLaunchKernelGGL((skinny_k_kernel<MR, TA, true, CW, KW, UK, PIPE>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((skinny_k_kernel<MR, TA, false, CW, KW, UK, PIPE>), grid, block, 0, s, p);
+}
+
+template <int MR, int NT, bool BIG>
 void launch_mn(int ta, bool vec_b, bool pipe_req, dim3 grid, const GemmParams& p, hipStream_t s) {
     const dim3 block(NT);
-    constexpr bool kCanPipe = NT < 1024;  // see launch_mr
+    constexpr bool kCanPipe = NT < 1024 && !BIG;  // see launch_mr
     const bool pipe = kCanPipe && pipe_req;
     if (ta == 0) {
         if (vec_b) {
-            if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, true, kCanPipe, NT>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, true, false, NT>), grid, block, 0, s, p);
+            if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, true, kCanPipe, NT, BIG>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, true, false, NT, BIG>), grid, block, 0, s, p);
         } else {
-            if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, false, kCanPipe, NT>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, false, false, NT>), grid, block, 0, s, p);
+            if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, false, kCanPipe, NT, BIG>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 0, false, false, NT, BIG>), grid, block, 0, s, p);
         }
     } else {
         if (vec_b) {
-            if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, true, kCanPipe, NT>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, true, false, NT>), grid, block, 0, s, p);
+            if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, true, kCanPipe, NT, BIG>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, true, false, NT, BIG>), grid, block, 0, s, p);
         } else {
-            if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, false, kCanPipe, NT>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, false, false, NT>), grid, block, 0, s, p);
+            if (pipe) hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, false, kCanPipe, NT, BIG>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((skinny_mn_kernel<MR, 1, false, false, NT, BIG>), grid, block, 0, s, p);
         }
     }
 }
@@ -324,7 +392,6 @@ template <int MR>
 hipError_t launch_mr(int ta, int tb, const GemmParams& p, hipStream_t s, int threads) {
     const bool vec_b = p.flags & FLAG_VEC_B;
     const int rblocks = (p.M + MR - 1) / MR;
-    const dim3 block(kSkinnyThreads);
     if (tb == 0) {  // B stored K x N
         const dim3 grid((p.N + 31) / 32, rblocks);
         const int64_t wgs = (int64_t)grid.x * grid.y;
@@ -347,21 +414,38 @@ hipError_t launch_mr(int ta, int tb, const GemmParams& p, hipStream_t s, int thr
         // second register set, so that size is never pipelined)
         const int64_t resident = nt == 512 ? 512 : 3 * 256;
         const bool pipe = MR > 1 && nt < 1024 && wgs <= resident;
-        if (nt == 1024)
-            launch_mn<MR, 1024>(ta, vec_b, pipe, grid, p, s);
+        // Byte offsets inside one k block (8 nt rows of op(B), and of op(A)
+        // when it is stored K x M) must stay below 2^32; past that (ld of
+        // about 2^17 and up at 1024 work-items, 2^19 at 256) the kernel that
+        // rebases per k step runs instead, with 256 work-items.
+        const int64_t ld = std::max<int64_t>(p.ldb, ta ? p.lda : 0);
+        const bool fits = ((int64_t)nt * kUnrollMN + 1) * ld * 4 < (1ll << 32);
+        if (!fits)
+            launch_mn<MR, 256, true>(ta, vec_b, false, grid, p, s);
+        else if (nt == 1024)
+            launch_mn<MR, 1024, false>(ta, vec_b, pipe, grid, p, s);
         else if (nt == 512)
-            launch_mn<MR, 512>(ta, vec_b, pipe, grid, p, s);
+            launch_mn<MR, 512, false>(ta, vec_b, pipe, grid, p, s);
         else
-            launch_mn<MR, 256>(ta, vec_b, pipe, grid, p, s);
+            launch_mn<MR, 256, false>(ta, vec_b, pipe, grid, p, s);
     } else {  // B stored N x K
-        const int cols_per_wg = 4 * (kSkinnyThreads / 64);
-        const dim3 grid((p.N + cols_per_wg - 1) / cols_per_wg, rblocks);
+        // Columns per wave, waves per column group, k steps per block and
+        // pipelining, measured on one MI355X (us, B stored N x K):
+        //   one row: 4, 4, 1, pipelined: 1 x 8192 x 8192 50.8 -> 39.1
+        //     (4 columns on one wave, one k step, not pipelined, before);
+        //   2 or 4 rows: 4, 4, 2, plain: 4 x 8192 x 8192 54.9 -> 42.2;
+        //   8 rows: 4, 2, 1, pipelined: 8 x 8192 x 8192 65.4 -> 58.1,
+        //     8 x 4096 x 4096 29.5 -> 18.3;
+        //   8 rows, A stored K x M (one scalar load per element of op(A),
+        //   so more columns share each): 8, 1, 1, pipelined: 8 x 8192 x 8192
+        //   240.7 -> 128.7.
         if (ta == 0) {
-            if (vec_b) hipLaunchKernelGGL((skinny_k_kernel<MR, 0, true>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((skinny_k_kernel<MR, 0, false>), grid, block, 0, s, p);
+            if constexpr (MR == 1) launch_k<MR, 0, 4, 4, 1, true>(vec_b, p, s);
+            else if constexpr (MR < 8) launch_k<MR, 0, 4, 4, 2, false>(vec_b, p, s);
+            else launch_k<MR, 0, 4, 2, 1, true>(vec_b, p, s);
         } else {
-            if (vec_b) hipLaunchKernelGGL((skinny_k_kernel<MR, 1, true>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((skinny_k_kernel<MR, 1, false>), grid, block, 0, s, p);
+            if constexpr (MR < 8) launch_k<MR, 1, 8, 4, 1, true>(vec_b, p, s);
+            else launch_k<MR, 1, 8, 1, 1, true>(vec_b, p, s);
         }
     }
     return hipGetLastError();
