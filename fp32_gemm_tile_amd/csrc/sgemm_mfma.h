@@ -402,7 +402,14 @@ sgemm_mfma_kernel(GemmParams p) {
         using DB = DmaOperand<BN, WN, NB, B_MN, NW, DMAB, BK, MR>;
         constexpr int NI = DA::kPerWave + DB::kPerWave;  // DMA ops per wave per k-tile
         static_assert((NS - 3) * NI < 64, "loads left in flight must fit the vmcnt field");
-        const int nk = Kp / BK;                           // full k-tiles
+        // With both operands stored k-major by rows (A as K x M, B as K x N),
+        // a partial last k-tile goes through the ring like the others: its
+        // rows at and past K lie beyond the end of each matrix, where the
+        // buffer loads read zeros (a partial k-tile only ever ends at K).
+        // Otherwise the last k elements of a row would be followed by the
+        // next row's, so the partial k-tile takes the guarded path below.
+        constexpr bool kTailInRing = A_MN && B_MN;
+        const int nk = kTailInRing ? (Kp + BK - 1) / BK : Kp / BK;  // k-tiles in the ring
         DA da;
         DB db;
         da.init(wave, lane, p.lda);
@@ -480,7 +487,7 @@ sgemm_mfma_kernel(GemmParams p) {
         if (t < nk) step(t, f0a, f0b, f1a, f1b);
         wait_vm_lds<0>();  // no DMA (not even an empty one) outlives the loop
 
-        if (Kp % BK) {
+        if (!kTailInRing && Kp % BK) {
             // Partial last k-tile: every wave has finished its DMA and LDS reads
             // (waited above); the barrier makes that true for all of them
             // before buffer 0 is rewritten.
@@ -562,39 +569,87 @@ sgemm_mfma_kernel(GemmParams p) {
     // memory for the whole kernel.
     const bool epi = p.flags & FLAG_EPI;
     if (!epi) {
+        // With beta != 0 the old C is read in chunks of 8 values per lane
+        // (CH accumulator registers of one block row; two chunks in registers
+        // at a time, which keeps every entry at its occupancy), each in full
+        // before any of it is stored and the next chunk's reads issued before
+        // this one's stores: loads and stores share one counter and no load
+        // may pass an earlier store to the same buffer, so reading element by
+        // element between the stores would cost a memory round trip per row.
+        constexpr int CH = NB >= 8 ? 1 : (8 / NB < NREG ? 8 / NB : NREG);
+        constexpr int NQ = MB * (NREG / CH);  // chunks
+        static_assert(NREG % CH == 0, "whole chunks");
+        auto load_c = [&](int q, float (&cin)[CH][NB]) {
+            const int a = q / (NREG / CH), r0 = (q % (NREG / CH)) * CH;
 #pragma unroll
-        for (int a = 0; a < MB; ++a) {
+            for (int i = 0; i < CH; ++i) {
+                const int row = wave_m * WM + MB * Mfma<MR>::row(r0 + i, elh) + a;
 #pragma unroll
-            for (int r = 0; r < NREG; ++r) {
-                const int brow = Mfma<MR>::row(r, elh);
-                const int row = wave_m * WM + MB * brow + a;
+                for (int b = 0; b < NB; ++b) cin[i][b] = 0.f;
                 if (m0 + row >= p.M) continue;
                 const uint32_t off = (uint32_t)(row * p.ldc + col0) * 4u;
-                float v[NB];
-#pragma unroll
-                for (int b = 0; b < NB; ++b) v[b] = alpha * acc[a][b][r];
                 if constexpr (NB == 4) {
                     if (full_vec) {
-                        f4 o = {v[0], v[1], v[2], v[3]};
-                        if (!beta0) o = o + beta * ld4(rc, off);
-                        st4_nt(rc, off, o);
+                        const f4 c4 = ld4(rc, off);
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) cin[i][b] = c4[b];
                         continue;
                     }
                 } else if constexpr (NB == 2) {
                     if (full_vec) {
-                        f2 o = {v[0], v[1]};
-                        if (!beta0) o = o + beta * ld2(rc, off);
-                        st2_nt(rc, off, o);
+                        const f2 c2 = ld2(rc, off);
+                        cin[i][0] = c2[0];
+                        cin[i][1] = c2[1];
                         continue;
                     }
                 }
 #pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    if (b < cols_left) cin[i][b] = ld1(rc, off + 4 * b);
+            }
+        };
+        auto store_c = [&](int q, const float (&cin)[CH][NB], bool with_c) {
+            const int a = q / (NREG / CH), r0 = (q % (NREG / CH)) * CH;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int row = wave_m * WM + MB * Mfma<MR>::row(r0 + i, elh) + a;
+                if (m0 + row >= p.M) continue;
+                const uint32_t off = (uint32_t)(row * p.ldc + col0) * 4u;
+                float v[NB];
+#pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    if (b < cols_left) {
-                        float o = v[b];
-                        if (!beta0) o += beta * ld1(rc, off + 4 * b);
-                        st1(rc, off + 4 * b, o);
+                    v[b] = alpha * acc[a][b][r0 + i];
+                    if (with_c) v[b] += beta * cin[i][b];
+                }
+                if constexpr (NB == 4) {
+                    if (full_vec) {
+                        st4_nt(rc, off, f4{v[0], v[1], v[2], v[3]});
+                        continue;
                     }
+                } else if constexpr (NB == 2) {
+                    if (full_vec) {
+                        st2_nt(rc, off, f2{v[0], v[1]});
+                        continue;
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    if (b < cols_left) st1(rc, off + 4 * b, v[b]);
+            }
+        };
+        float c0[CH][NB] = {}, c1[CH][NB] = {};
+        if (beta0) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) store_c(q, c0, false);
+        } else {
+            load_c(0, c0);
+#pragma unroll
+            for (int q = 0; q < NQ; q += 2) {
+                if (q + 1 < NQ) load_c(q + 1, c1);
+                store_c(q, c0, true);
+                if (q + 1 < NQ) {
+                    if (q + 2 < NQ) load_c(q + 2, c0);
+                    store_c(q + 1, c1, true);
                 }
             }
         }
