@@ -40,7 +40,7 @@ METRIC = "fp32 SGEMM TFLOP/s and % of MI355X fp32 peak at 4096^3 and 8192^3"
 def kernel_source_sha(kernel_config="mfma_"):
     """Hash of the sources that define the kernel family of a table entry
     (matrix-core, few-row or vector-ALU kernel) and its launch."""
-    if kernel_config.startswith("valu_skinny"):
+    if kernel_config == "few_rows":
         family = "sgemm_skinny.hip"
     elif kernel_config.startswith("valu_"):
         family = "sgemm_valu.hip"

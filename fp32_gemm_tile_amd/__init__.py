@@ -165,6 +165,8 @@ def load_library(path: str = LIB_PATH):
     lib.fg_get_raster.restype = i32
     lib.fg_set_few_row_threads.argtypes = [i32]
     lib.fg_set_few_row_threads.restype = i32
+    lib.fg_set_few_row_kernel.argtypes = [i32]
+    lib.fg_set_few_row_kernel.restype = i32
     lib.fg_set_streamk_policy.argtypes = [i32]
     lib.fg_set_streamk_policy.restype = i32
     lib.fg_probe_mfma.argtypes = [i32, i32, vp, vp]
@@ -340,6 +342,12 @@ def fg_set_few_row_threads(threads) -> int:
     """Workgroup size of the few-row kernel, B stored K x N (fp32gemm_tune.h):
     0 = automatic, else 256, 512 or 1024."""
     return load_library().fg_set_few_row_threads(threads)
+
+
+def fg_set_few_row_kernel(kernel):
+    """Few-row kernel family: 0 automatic, 1 vector ALU, 2 matrix cores
+    (include/fp32gemm_tune.h)."""
+    return load_library().fg_set_few_row_kernel(kernel)
 
 
 def fg_get_raster():

@@ -209,9 +209,10 @@ SEARCH_INC = os.path.join(SEARCH_DIR, "fg_mfma_instances.inc")
 SEARCH_TUNED = os.path.join(SEARCH_DIR, "fg_tuned.inc")
 SEARCH_LIB = os.path.join(SEARCH_DIR, "libfp32gemm_search.so")
 SEARCH_BUILD = os.path.join(ROOT, "_build", "search")
-FIXED_NAMES = ("valu_128x128x8_t8x8", "valu_64x64x8_t4x4", "valu_skinny_m8")  # after the
+FIXED_NAMES = ("valu_128x128x8_t8x8", "valu_64x64x8_t4x4", "few_rows")  # after the
 # matrix-core rows, in this order (fg_api.cpp lists them itself)
-SKINNY = "valu_skinny_m8"
+SKINNY = "few_rows"
+SKINNY_OLD = "valu_skinny_m8"   # its name in reports written before it had a matrix-core kernel
 
 
 def fixed_ids():
@@ -220,7 +221,8 @@ def fixed_ids():
 
 
 def _skinny_id(report):
-    return report.get("fixed_ids", {}).get(SKINNY)
+    ids = report.get("fixed_ids", {})
+    return ids.get(SKINNY, ids.get(SKINNY_OLD))
 LDS_BYTES = 160 * 1024
 SHAPE_KEYS = ("bm", "bn", "waves_m", "waves_n", "bk", "mr", "stages", "dmab", "occ")
 
@@ -475,7 +477,7 @@ def run_search(report_path, shapes=None):
     report = {"date": datetime.datetime.now().isoformat(timespec="seconds"),
               "device": torch.cuda.get_device_name(0), "fixed_ids": fixed_ids(),
               "instances": [], "shapes": []}
-    skinny = report["fixed_ids"][SKINNY]
+    skinny = _skinny_id(report)
     ok_ids = []
     for n, e in enumerate(entries):
         if n % 10 == 0:
@@ -544,6 +546,63 @@ def refine_search(report_path, window=1.06, rounds=3, budget_s=0.25):
               f"{2 * sh[0] * sh[1] * sh[2] / rec['refined'][b] / 1e12:.1f} TFLOP/s", flush=True)
         with open(report_path, "w") as f:
             json.dump(report, f)
+    return report
+
+
+# Few-row shapes the few-row entry's efficiency is also fitted on (the tile
+# search's shapes start at 128 rows): the decode shapes of every layout of B,
+# 16 to 64 rows, and N = K = 4096.
+FEW_SHAPES = [(M, N, N, "N", tb, None, None, None) for M, N, tb in
+              [(1, 8192, "N"), (1, 8192, "T"), (4, 8192, "T"), (8, 8192, "N"), (8, 8192, "T"),
+               (16, 8192, "N"), (32, 8192, "N"), (32, 8192, "T"), (64, 8192, "N"),
+               (8, 4096, "N"), (32, 4096, "N"), (64, 4096, "N")]]
+
+
+def retime_few_rows(report_path, rounds=3, budget_s=0.25, write=True):
+    """On the GPU: the few-row entry's kernels change apart from the tile
+    search, so re-time that entry of the built library on every search shape
+    with at most 512 rows (best of `rounds` passes), put the times in the
+    report in place of the few-row times it holds, refit the entry's
+    efficiency from them and from FEW_SHAPES, and rewrite its row of
+    fg_tuned.inc."""
+    import torch  # noqa: F401
+    fg.load_library()
+    report = json.load(open(report_path))
+    sk_rep = _skinny_id(report)
+    sk = [c["id"] for c in fg.configs() if c["kind"] == fg.FG_KIND_SKINNY][0]
+    samples = []
+    for rec in report["shapes"]:
+        sh = tuple(rec["shape"])
+        if sh[0] > 512:
+            continue
+        time_entries(sh, [sk], budget_s=0.2)   # clock up
+        t = min(time_entries(sh, [sk], budget_s)[sk] for _ in range(rounds))
+        rec["seconds"][str(sk_rep)] = t
+        rec.setdefault("refined", {})[str(sk_rep)] = t
+        samples.append((sh[0], sh[1], sh[2], t))
+        print(f"[few-rows] {sh[:5]}: {t * 1e6:.1f} us, "
+              f"{2 * sh[0] * sh[1] * sh[2] / t / 1e12:.1f} TFLOP/s", flush=True)
+    few = []
+    for sh in FEW_SHAPES:
+        time_entries(sh, [sk], budget_s=0.2)
+        t = min(time_entries(sh, [sk], budget_s)[sk] for _ in range(rounds))
+        samples.append((sh[0], sh[1], sh[2], t))
+        few.append({"shape": list(sh[:5]), "seconds": t})
+        print(f"[few-rows] {sh[:5]}: {t * 1e6:.1f} us, "
+              f"{4 * sh[1] * sh[2] / t / 1e9:.0f} GB/s of op(B)", flush=True)
+    eff, eff1, rms = fit_entry(sk, samples, False)
+    report["few_rows"] = {"date": datetime.datetime.now().isoformat(timespec="seconds"),
+                          "eff": eff, "eff1": eff1, "rms_log_error": rms,
+                          "shapes": len(samples), "few_row_shapes": few}
+    print(f"[few-rows] fitted eff {eff:.2f}, rms log error {rms:.3f}", flush=True)
+    if write:
+        with open(report_path, "w") as f:
+            json.dump(report, f)
+        lines = open(INC_PATH).read().splitlines()
+        lines = [f"{{FG_ID_SKINNY, {eff:.3f}, {eff1:.3f}}},  // {SKINNY}"
+                 if l.startswith("{FG_ID_SKINNY,") else l for l in lines]
+        with open(INC_PATH, "w") as f:
+            f.write("\n".join(lines) + "\n")
     return report
 
 
@@ -689,9 +748,9 @@ def check_picks(report_path, write_md=True):
         best = min(t, key=t.get)
         kept_ids = [by_key[shape_key(e)] for e in table.values()] + [_skinny_id(report)]
         kbest = min((k for k in kept_ids if k in t), key=t.get)
-        rows.append({"shape": list(sh[:5]), "best": inst.get(best, {}).get("name", "valu_skinny_m8"),
+        rows.append({"shape": list(sh[:5]), "best": inst.get(best, {}).get("name", SKINNY),
                      "best_tflops": 2 * M * N * K / t[best] / 1e12,
-                     "kept_best": inst.get(kbest, {}).get("name", "valu_skinny_m8"),
+                     "kept_best": inst.get(kbest, {}).get("name", SKINNY),
                      "pick": pick["name"], "pick_tflops": 2 * M * N * K / t[rid] / 1e12,
                      "pick_over_best": t[best] / t[rid], "kept_over_best": t[best] / t[kbest]})
     worst = min(r["pick_over_best"] for r in rows)
@@ -767,6 +826,10 @@ def main(argv=None):
     ap.add_argument("--refine", default=None, metavar="REPORT",
                     help="on the GPU: re-time the near-fastest instances of every shape of "
                          "REPORT (updates it)")
+    ap.add_argument("--retime-few-rows", default=None, metavar="REPORT",
+                    help="on the GPU: re-time the built library's few-row entry on the search "
+                         "shapes of REPORT, refit its efficiency (updates REPORT and "
+                         "csrc/fg_tuned.inc)")
     ap.add_argument("--select", default=None, metavar="REPORT",
                     help="keep a cover of the search shapes from REPORT; rewrite "
                          "csrc/fg_mfma_instances.inc and csrc/fg_tuned.inc")
@@ -784,6 +847,9 @@ def main(argv=None):
         return 0
     if args.refine:
         refine_search(args.refine)
+        return 0
+    if args.retime_few_rows:
+        retime_few_rows(args.retime_few_rows)
         return 0
     if args.select:
         entries, _ = select_from_report(args.select)

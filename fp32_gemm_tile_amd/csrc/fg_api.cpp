@@ -131,7 +131,7 @@ constexpr int kNumMfma = 0
 #undef FG_MFMA_ENTRY
 constexpr int kIdValu128 = kNumMfma;      // valu_128x128x8_t8x8
 constexpr int kIdValu64 = kNumMfma + 1;   // valu_64x64x8_t4x4
-constexpr int kIdSkinny = kNumMfma + 2;   // valu_skinny_m8
+constexpr int kIdSkinny = kNumMfma + 2;   // few_rows
 // (fg_tuned.inc names the few-row row by this)
 #define FG_ID_SKINNY kIdSkinny
 
@@ -150,7 +150,7 @@ const Table& table_rows() {
             make_entry(kIdValu64, FG_KIND_VALU, 1, 64, 64, 8, 4, 4, 256, 2, 4, "valu_64x64x8_t4x4"),
             // Few-row kernel: bm = rows per block (up to 8), bn = columns per
             // workgroup for B stored K x N; memory-bound, costed separately.
-            make_entry(kIdSkinny, FG_KIND_SKINNY, 0, 8, 32, 0, 8, 4, 256, 0, 2, "valu_skinny_m8"),
+            make_entry(kIdSkinny, FG_KIND_SKINNY, 0, 8, 32, 0, 8, 4, 256, 0, 2, "few_rows"),
         };
         constexpr int nf = sizeof fixed / sizeof fixed[0];
         static Entry all[kNumMfma + nf];
@@ -284,24 +284,25 @@ double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, boo
     return t;
 }
 
-// Few-row kernel, modelled from measurements on one MI355X: a workgroup owns
-// 32 columns of C for one block of up to 8 rows and walks K in steps of 32
-// rows of op(B). One workgroup per CU is latency-bound (a step costs about
-// 0.12 + 0.01 * (rows - 1) us at efficiency 1); with several per CU the CU's
-// throughput (0.07 us per workgroup-step) takes over. The entry's efficiency
-// (0.7 by default, fitted by the tuner) divides both. op(B) crosses HBM at
-// least once. The fixed cost covers the launch and the final reduction.
+// Few-row entry, modelled from measurements on one MI355X: one pass over
+// op(B) per block of up to 64 rows, bound by the stream of op(B) (scaled down
+// when the grid has fewer than one workgroup per CU) or by the matrix cores,
+// which see the rows padded to 16, 32 or 64 and reach about half of peak here
+// (32 x 8192 x 8192: 58.6 us measured; 64 rows: 99.5). With B stored N x K
+// and at most 4 rows the vector-ALU kernel runs instead, at the same stream
+// rate. The entry's efficiency (fitted by the tuner) divides the matrix-core
+// term. The fixed cost covers the launch and the final reduction.
 constexpr double kSkinnyFixed = 5e-6;
+constexpr int64_t kFewRowsMax = 512;  // rows up to which the entry competes
 double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0, double eff) {
-    const int64_t rows = M < 8 ? M : 8;
-    const double blocks = (double)cdiv(M, 8);
-    const double wgs = blocks * (double)cdiv(N, 32);
-    const double steps = (double)cdiv(K, 32);
-    const double per_cu = std::ceil(wgs / kNumCUs);
-    const double t_lat = steps * (0.12e-6 + (double)(rows - 1) * 0.01e-6);
-    const double t_thr = per_cu * steps * 0.07e-6;
-    const double bytes = 4.0 * ((double)K * N + (double)M * K + (double)M * N * (beta0 ? 1 : 2));
-    return kSkinnyFixed + std::max(std::max(t_lat, t_thr) / eff, bytes / kHbmStream);
+    const double bytes_c = 4.0 * ((double)M * K + (double)M * N * (beta0 ? 1 : 2));
+    const int64_t rows = M <= 16 ? 16 : (M <= 32 ? 32 : 64);  // padded rows per pass
+    const double passes = (double)cdiv(M, rows);
+    const double wgs = passes * (double)cdiv(N, N >= 32 * kNumCUs ? 32 : 16);
+    const double fill = std::min(1.0, wgs / kNumCUs);
+    const double t_mem = (4.0 * (double)K * N * passes + bytes_c) / (kHbmStream * fill);
+    const double t_mfma = 2.0 * (double)rows * N * K * passes / (157.3e12 * 0.5);
+    return kSkinnyFixed + std::max(t_mem, t_mfma / eff);
 }
 
 // Best MFMA or few-row entry (and split count, at most max_splits). With
@@ -325,7 +326,10 @@ int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_s
         const Entry& e = table()[i];
         if (need_quant && !e.quant) continue;
         if (e.cfg.kind == FG_KIND_SKINNY) {
-            if (mfma_only) continue;
+            // The few-row model (one pass of op(B) per 64 rows) is fitted on
+            // at most 512 rows; past that the matrix-core tiles win on every
+            // measured shape.
+            if (mfma_only || M > kFewRowsMax) continue;
             const double c = skinny_cost(M, N, K, beta0, efficiencies()[i].eff.load());
             if (best < 0 || c < kPickMargin * best_cost) {
                 best = i;
@@ -357,6 +361,8 @@ std::atomic<int> g_group_m{kDefaultGroupM};
 // Workgroup size of the few-row kernel's K x N form (fg_set_few_row_threads;
 // 0 = automatic).
 std::atomic<int> g_few_row_threads{0};
+// Few-row kernel family (fg_set_few_row_kernel; 0 = automatic).
+std::atomic<int> g_few_row_kernel{0};
 std::atomic<int> g_xcd_remap{1};
 
 // ---------------------------------------------------------------------------
@@ -710,7 +716,8 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
     } else if (en.cfg.kind == FG_KIND_MFMA) {
         e = fg::launch_mfma(en.variant, transA, transB, p, stream);
     } else if (en.cfg.kind == FG_KIND_SKINNY) {
-        e = fg::launch_skinny(transA, transB, p, stream, g_few_row_threads.load());
+        e = fg::launch_skinny(transA, transB, p, stream, g_few_row_threads.load(),
+                              g_few_row_kernel.load());
     } else {
         e = fg::launch_valu(en.variant, transA, transB, p, stream);
     }
@@ -898,6 +905,14 @@ fg_status fg_set_few_row_threads(int32_t threads) {
     if (threads != 0 && threads != 256 && threads != 512 && threads != 1024)
         return fail(FG_ERR_INVALID_ARG, 1, "threads must be 0, 256, 512 or 1024");
     g_few_row_threads.store(threads);
+    return FG_OK;
+}
+
+fg_status fg_set_few_row_kernel(int32_t kernel) {
+    clear_error();
+    if (kernel < 0 || kernel > 2)
+        return fail(FG_ERR_INVALID_ARG, 1, "kernel must be 0, 1 or 2");
+    g_few_row_kernel.store(kernel);
     return FG_OK;
 }
 

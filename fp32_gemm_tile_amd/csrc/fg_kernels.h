@@ -79,10 +79,18 @@ hipError_t launch_mfma_tiles(int id, int trans_a, int trans_b, const GemmParams&
                              int32_t tiles, int32_t splits, hipStream_t stream);
 hipError_t launch_valu(int variant, int trans_a, int trans_b, const GemmParams& p,
                        hipStream_t stream);
-// Few-row GEMM (memory-bound): blocks of up to 8 rows of C, op(B) streamed
-// once per block. threads: workgroup size of the K x N form (0: automatic).
+// Few-row GEMM (memory-bound): op(B) streamed once per block of rows, on the
+// vector ALU (blocks of up to 8 rows) or on the matrix cores (blocks of up to
+// 64 rows). threads: workgroup size of the vector-ALU K x N form (0:
+// automatic); kernel: 0 automatic (few_rows_on_valu), 1 vector ALU, 2 matrix
+// cores.
+// The automatic choice, from measurements on one MI355X (us at N = K = 8192,
+// vector ALU / matrix cores): B stored K x N, one row 42.9 / 40.7, 4 rows
+// 46.1 / 41.7, 8 rows 51.3 / 43.3; B stored N x K, one row 40.1 / 44.0, 4
+// rows 41.6 / 43.9, 5 rows 55.0 / 43.6, 8 rows 57.0 / 44.1.
+inline bool few_rows_on_valu(int64_t M, int trans_b) { return trans_b && M <= 4; }
 hipError_t launch_skinny(int trans_a, int trans_b, const GemmParams& p, hipStream_t stream,
-                         int threads = 0);
+                         int threads = 0, int kernel = 0);
 // C = beta * C (beta == 0: C = 0 without reading it); for K == 0 or alpha == 0.
 // With FLAG_EPI: C = act(beta * C + u_i + w_j).
 hipError_t launch_scale(const GemmParams& p, hipStream_t stream);

@@ -451,12 +451,242 @@ hipError_t launch_mr(int ta, int tb, const GemmParams& p, hipStream_t s, int thr
     return hipGetLastError();
 }
 
+// ---- 5 to a few dozen rows on the matrix cores ------------------------------
+// With more than a handful of rows the vector-ALU kernels above are bound by
+// their FMAs and op(A) reads, not by HBM (8 x 8192 x 8192 NT: 58 us, 4.6
+// TB/s). Here every product goes through v_mfma_f32_16x16x4_f32 with the
+// rows of C padded to RB blocks of 16 (M <= 16 RB per grid row):
+//   * lane l gives op(A)(16 b + l % 16, k) and op(B)(k, column) for
+//     k = k0 + 4 (l / 16) + s at step s of a 16-deep k block; the four k of
+//     a lane are consecutive (the sum over k is order-free), so op(A) stored
+//     M x K and op(B) stored N x K are read with one 128-bit load per lane,
+//     row block or column set, and k block;
+//   * op(B) stored K x N: a lane's CS columns CS (l % 16) + c are one CS-wide
+//     load per k row (column set c of the instruction holds them);
+//   * lane l ends with rows 4 (l / 16) + r, r < 4, of its column.
+// A workgroup of 16 waves owns 16 CS columns; wave w takes k blocks w,
+// w + 16, ... (UB blocks per round of loads), and the 16 partial tiles are
+// added in LDS in wave order (deterministic), one element per work-item.
+constexpr int kFewWaves = 16;
+// k per lane per block (B stored K x N, N x K), registers of loaded operands
+// per round, pipelined rounds. Measured on one MI355X against 4, 4, 48, plain
+// (us): 8 x 8192^2 NN 44.8 -> 43.2, NT 57.7 -> 48.2; 32 x 8192^2 NN 67.6 ->
+// 60.6, NT 75.4 -> 67.9; 8 x 32000 x 4096 NT 125.1 -> 112.3; k per lane 16
+// was slower (NT 50.9) and pipelined 64-row blocks spill, so those run plain.
+constexpr int kFewKplMN = 8, kFewKplK = 8, kFewRegs = 64;
+constexpr bool kFewPipe = true;
+
+template <int RB, int CS, int TA, int TB, bool VEC, int KPL, int UB, bool PIPE>
+__global__ void __launch_bounds__(64 * kFewWaves) few_rows_mfma_kernel(GemmParams p) {
+    // KPL: k per lane per block (a block is 4 KPL deep: lane group g = l / 16
+    // holds k0 + KPL g .. KPL g + KPL - 1); UB: blocks per round of loads;
+    // PIPE: the next round's loads are issued before this round's MFMAs (two
+    // register sets).
+    constexpr int KB = 4 * KPL;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int li = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16 * CS, m0 = blockIdx.y * 16 * RB;
+    const int nblk = (p.K + KB - 1) / KB;
+    const bool vec_a = !TA && (p.flags & FLAG_VEC_A);
+
+    f4 acc[RB][CS];
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int c = 0; c < CS; ++c) acc[b][c] = f4{0.f, 0.f, 0.f, 0.f};
+
+    // Loads of the UB k blocks jb, jb + 16, ... (blocks past K read as 0).
+    // Buffer resources are based at each block, so offsets stay below
+    // 64 * ld * 4 bytes.
+    auto load_round = [&](int jb, float (&av)[UB][RB][KPL], float (&bv)[UB][CS][KPL]) {
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+            const int k0 = (jb + kFewWaves * u) * KB;
+            const int kl = p.K - k0 - KPL * g;  // this lane's k inside K: min(KPL, kl)
+            const int64_t a_org = TA ? (int64_t)k0 * p.lda + m0 : (int64_t)m0 * p.lda + k0;
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_org, p.a_extent - a_org);
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const int m = 16 * b + li;
+                if (m0 + m >= p.M) {
+#pragma unroll
+                    for (int s = 0; s < KPL; ++s) av[u][b][s] = 0.f;
+                } else if constexpr (TA == 0) {
+#pragma unroll
+                    for (int j = 0; j < KPL; j += 4) {
+                        const f4 v = ld4_guard(ra, (uint32_t)(m * p.lda + KPL * g + j) * 4u, j, kl,
+                                               vec_a);
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) av[u][b][j + s] = v[s];
+                    }
+                } else {
+#pragma unroll
+                    for (int s = 0; s < KPL; ++s)
+                        av[u][b][s] =
+                            s < kl ? ld1(ra, (uint32_t)((KPL * g + s) * p.lda + m) * 4u) : 0.f;
+                }
+            }
+            if constexpr (TB == 0) {  // op(B) stored K x N
+                const int64_t b_org = (int64_t)k0 * p.ldb + n0;
+                const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_org, p.b_extent - b_org);
+                const int cl = p.N - n0 - CS * li;  // this lane's columns inside N: min(CS, cl)
+#pragma unroll
+                for (int s = 0; s < KPL; ++s) {
+                    const uint32_t off = (uint32_t)((KPL * g + s) * p.ldb + CS * li) * 4u;
+                    const bool in = s < kl;
+                    if constexpr (CS == 4) {
+                        const f4 v = in ? ld4_guard(rb, off, 0, cl, VEC) : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) bv[u][c][s] = v[c];
+                    } else if constexpr (CS == 2) {
+                        f2 v = {0.f, 0.f};
+                        if (in && VEC && cl >= 2) {
+                            v = ld2(rb, off);
+                        } else if (in) {
+                            if (cl > 0) v[0] = ld1(rb, off);
+                            if (cl > 1) v[1] = ld1(rb, off + 4);
+                        }
+                        bv[u][0][s] = v[0];
+                        bv[u][1][s] = v[1];
+                    } else {
+                        bv[u][0][s] = in && cl > 0 ? ld1(rb, off) : 0.f;
+                    }
+                }
+            } else {  // op(B) stored N x K
+                const int64_t b_org = (int64_t)n0 * p.ldb + k0;
+                const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_org, p.b_extent - b_org);
+#pragma unroll
+                for (int c = 0; c < CS; ++c) {
+                    const int n = 16 * c + li;
+#pragma unroll
+                    for (int j = 0; j < KPL; j += 4) {
+                        const f4 v = n0 + n < p.N ? ld4_guard(rb, (uint32_t)(n * p.ldb + KPL * g + j) * 4u,
+                                                              j, kl, VEC)
+                                                  : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) bv[u][c][j + s] = v[s];
+                    }
+                }
+            }
+        }
+    };
+    auto mfma_round = [&](const float (&av)[UB][RB][KPL], const float (&bv)[UB][CS][KPL]) {
+#pragma unroll
+        for (int u = 0; u < UB; ++u)
+#pragma unroll
+            for (int s = 0; s < KPL; ++s)
+#pragma unroll
+                for (int b = 0; b < RB; ++b)
+#pragma unroll
+                    for (int c = 0; c < CS; ++c)
+                        acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][b][s], bv[u][c][s],
+                                                                         acc[b][c], 0, 0, 0);
+    };
+    constexpr int STEP = kFewWaves * UB;  // blocks per round of the workgroup
+    if constexpr (PIPE) {
+        float a0[UB][RB][KPL], b0[UB][CS][KPL], a1[UB][RB][KPL], b1[UB][CS][KPL];
+        if (wave < nblk) load_round(wave, a0, b0);
+        for (int jb = wave; jb < nblk; jb += 2 * STEP) {
+            if (jb + STEP < nblk) load_round(jb + STEP, a1, b1);
+            mfma_round(a0, b0);
+            if (jb + STEP >= nblk) break;
+            if (jb + 2 * STEP < nblk) load_round(jb + 2 * STEP, a0, b0);
+            mfma_round(a1, b1);
+        }
+    } else {
+        for (int jb = wave; jb < nblk; jb += STEP) {
+            float av[UB][RB][KPL], bv[UB][CS][KPL];
+            load_round(jb, av, bv);
+            mfma_round(av, bv);
+        }
+    }
+
+    // The 16 waves' partial tiles through LDS, added in wave order; element
+    // (q, l) = accumulator register r of (row block b, column set c) of lane l,
+    // q = 4 (CS b + c) + r.
+    constexpr int NQ = RB * CS * 4;
+    __shared__ float red[kFewWaves][NQ][64];
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int c = 0; c < CS; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][4 * (CS * b + c) + r][lane] = acc[b][c][r];
+    __syncthreads();
+    const int64_t c_org = (int64_t)m0 * p.ldc + n0;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + c_org, p.c_extent - c_org);
+    const bool beta0 = p.flags & FLAG_BETA0;
+    for (int t = threadIdx.x; t < NQ * 64; t += 64 * kFewWaves) {
+        const int q = t >> 6, l = t & 63;
+        const int r = q & 3, c = (q >> 2) % CS, b = (q >> 2) / CS;
+        const int row = 16 * b + 4 * (l >> 4) + r;
+        const int col = TB == 0 ? CS * (l & 15) + c : 16 * c + (l & 15);
+        if (m0 + row < p.M && n0 + col < p.N) {
+            float sum = red[0][q][l];
+#pragma unroll
+            for (int w = 1; w < kFewWaves; ++w) sum += red[w][q][l];
+            const uint32_t off = (uint32_t)(row * p.ldc + col) * 4u;
+            const float cin = beta0 ? 0.f : ld1(rc, off);
+            st1(rc, off, epilogue_value(p, sum, cin, beta0, (int64_t)m0 + row, (int64_t)n0 + col));
+        }
+    }
+}
+
+template <int RB, int CS, int TA, int TB>
+void launch_few_mfma_t(bool vec_b, const GemmParams& p, hipStream_t s) {
+    constexpr int KPL = TB == 0 ? kFewKplMN : kFewKplK;
+    constexpr bool PIPE = kFewPipe && RB < 4;
+    // Blocks per round: as many as kFewRegs registers of loaded operands
+    // hold (per register set).
+    constexpr int UB0 = kFewRegs / ((RB + CS) * KPL * (PIPE ? 2 : 1));
+    constexpr int UB = UB0 < 1 ? 1 : UB0;
+    const dim3 grid((p.N + 16 * CS - 1) / (16 * CS), (p.M + 16 * RB - 1) / (16 * RB));
+    const dim3 block(64 * kFewWaves);
+    if (vec_b) hipLaunchKernelGGL((few_rows_mfma_kernel<RB, CS, TA, TB, true, KPL, UB, PIPE>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((few_rows_mfma_kernel<RB, CS, TA, TB, false, KPL, UB, PIPE>), grid, block, 0, s, p);
+}
+
+template <int RB, int CS>
+void launch_few_mfma_cs(int ta, int tb, bool vec_b, const GemmParams& p, hipStream_t s) {
+    if (ta == 0) {
+        if (tb == 0) launch_few_mfma_t<RB, CS, 0, 0>(vec_b, p, s);
+        else launch_few_mfma_t<RB, CS, 0, 1>(vec_b, p, s);
+    } else {
+        if (tb == 0) launch_few_mfma_t<RB, CS, 1, 0>(vec_b, p, s);
+        else launch_few_mfma_t<RB, CS, 1, 1>(vec_b, p, s);
+    }
+}
+
+// Row blocks of 16 per grid row: one up to 16 rows, two up to 32, else four
+// (M past 64 runs ceil(M / 64) grid rows, each streaming op(B)). Two column sets per
+// wave (32 columns per workgroup) once that still gives 256 workgroups.
+hipError_t launch_few_mfma(int ta, int tb, const GemmParams& p, hipStream_t s) {
+    const bool vec_b = p.flags & FLAG_VEC_B;
+    const bool two_sets = p.N >= 32 * 256;
+    if (p.M <= 16) {
+        if (two_sets) launch_few_mfma_cs<1, 2>(ta, tb, vec_b, p, s);
+        else launch_few_mfma_cs<1, 1>(ta, tb, vec_b, p, s);
+    } else if (p.M <= 32) {
+        if (two_sets) launch_few_mfma_cs<2, 2>(ta, tb, vec_b, p, s);
+        else launch_few_mfma_cs<2, 1>(ta, tb, vec_b, p, s);
+    } else {
+        if (two_sets) launch_few_mfma_cs<4, 2>(ta, tb, vec_b, p, s);
+        else launch_few_mfma_cs<4, 1>(ta, tb, vec_b, p, s);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
-// Rows per block: 1, 2, 4 or 8 (the smallest power of two >= M, capped at 8).
-// threads: workgroup size of the K x N kernel (0 = automatic, else 256, 512
-// or 1024).
-hipError_t launch_skinny(int ta, int tb, const GemmParams& p, hipStream_t s, int threads) {
+// kernel: 0 = automatic (few_rows_on_valu), 1 = vector ALU, 2 = matrix
+// cores. Vector ALU rows per block: 1, 2, 4 or 8 (the smallest power of two
+// >= M, capped at 8). threads: workgroup size of its K x N kernel (0 =
+// automatic, else 256, 512 or 1024).
+hipError_t launch_skinny(int ta, int tb, const GemmParams& p, hipStream_t s, int threads,
+                         int kernel) {
+    if (kernel == 2 || (kernel == 0 && !few_rows_on_valu(p.M, tb)))
+        return launch_few_mfma(ta, tb, p, s);
     if (p.M <= 1) return launch_mr<1>(ta, tb, p, s, threads);
     if (p.M <= 2) return launch_mr<2>(ta, tb, p, s, threads);
     if (p.M <= 4) return launch_mr<4>(ta, tb, p, s, threads);

@@ -71,6 +71,14 @@ fg_status fg_set_raster(int32_t group_m, int32_t xcd_remap);
  */
 fg_status fg_set_few_row_threads(int32_t threads);
 
+/*
+ * Which kernel the few-row entry runs: 0 (the default) the vector-ALU kernel
+ * up to 4 rows of C and the matrix-core kernel (rows padded to blocks of 16)
+ * above; 1 always the vector-ALU kernel; 2 always the matrix-core kernel.
+ * Process-wide, for tests and measurements. FG_ERR_INVALID_ARG otherwise.
+ */
+fg_status fg_set_few_row_kernel(int32_t kernel);
+
 /* The current raster settings (arguments 1, 2: outputs, non-NULL). */
 fg_status fg_get_raster(int32_t* group_m, int32_t* xcd_remap);
 

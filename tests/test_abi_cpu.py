@@ -403,10 +403,10 @@ def test_autotune_candidates():
     names = lambda sh: {fg.fg_get_config(i)["name"] for i in autotune.candidates(sh)}
     aligned = names((4096, 4096, 4096, "N", "N", None, None, None))
     ragged = names((3001, 2047, 1025, "T", "N", 3001, 2047, 2047))
-    assert "mfma_256x256x16_w2x2_s4" in aligned and "valu_skinny_m8" not in aligned
+    assert "mfma_256x256x16_w2x2_s4" in aligned and "few_rows" not in aligned
     assert "mfma_256x256x16_w2x2_s4" not in ragged
     assert ragged and all("_dw" in n for n in ragged), ragged
-    assert "valu_skinny_m8" in names((64, 4096, 4096, "N", "N", None, None, None))
+    assert "few_rows" in names((64, 4096, 4096, "N", "N", None, None, None))
     assert not any(n.startswith("valu_") and "skinny" not in n for n in aligned | ragged)
 
 
@@ -503,6 +503,9 @@ def test_raster_setting_validation():
     for t in (0, 256, 512, 1024):
         assert fg.fg_set_few_row_threads(t) == fg.FG_OK
     assert fg.fg_set_few_row_threads(128) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 1
+    for k in (1, 2, 0):
+        assert fg.fg_set_few_row_kernel(k) == fg.FG_OK
+    assert fg.fg_set_few_row_kernel(3) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 1
     fg.fg_set_few_row_threads(0)
 
 

@@ -43,7 +43,7 @@ def test_traffic_records_are_keyed_by_kernel_sources():
         want = rec["bytes_per_launch"] if current else None
         assert bench.load_traffic(name, rec["kernel_config"]) == want, name
         assert bench.load_traffic(name, "mfma_64x64x16_w2x2_s4") is None  # another entry
-    assert bench.kernel_source_sha("mfma_x") != bench.kernel_source_sha("valu_skinny_m8")
+    assert bench.kernel_source_sha("mfma_x") != bench.kernel_source_sha("few_rows")
     assert bench.load_traffic("no_such_workload", "mfma_x") is None
 
 

@@ -27,43 +27,73 @@ def skinny_id():
     return [c["id"] for c in fg.configs() if c["kind"] == fg.FG_KIND_SKINNY][0]
 
 
+class few_kernel:
+    """Force the few-row kernel family (1 vector ALU, 2 matrix cores) for a
+    block of calls; automatic again afterwards."""
+
+    def __init__(self, kernel):
+        self.kernel = kernel
+
+    def __enter__(self):
+        assert fg.fg_set_few_row_kernel(self.kernel) == fg.FG_OK
+        log(f"  few-row kernel {self.kernel}")
+
+    def __exit__(self, *exc):
+        assert fg.fg_set_few_row_kernel(0) == fg.FG_OK
+
+
 def _pad4(n):
     return (n + 3) // 4 * 4
 
 
+RAGGED = [(1, 1, 1), (1, 33, 517), (2, 300, 1000), (3, 31, 7), (5, 130, 260), (8, 257, 2049),
+          (13, 70, 129), (16, 8197, 300), (17, 300, 100), (32, 8200, 513), (40, 100, 64),
+          (64, 33, 40)]
+
+
+@pytest.mark.parametrize("kernel", [1, 2])
 @pytest.mark.parametrize("ta,tb", OPS)
 @pytest.mark.parametrize("aligned", [False, True])
-def test_skinny_ragged(ta, tb, aligned):
+def test_skinny_ragged(ta, tb, aligned, kernel):
+    """Each few-row kernel family forced on ragged shapes (one to 64 rows;
+    N from 1 to past 8192, where the matrix-core kernel takes two column sets
+    per wave; K shorter than a block and not a multiple of one)."""
     cid = skinny_id()
-    for i, (M, N, K) in enumerate([(1, 1, 1), (1, 33, 517), (2, 300, 1000), (3, 31, 7),
-                                   (5, 130, 260), (8, 257, 2049), (13, 70, 129), (40, 100, 64)]):
-        w0 = wl.custom(M, N, K, ta, tb)
-        kw = dict(lda=_pad4(w0.LDA), ldb=_pad4(w0.LDB), ldc=_pad4(w0.LDC)) if aligned else {}
-        w = wl.custom(M, N, K, ta, tb, alpha=0.5, beta=1.25, dist="normal", seed=90 + i, **kw)
-        A, B, C = wl.make_inputs(w)
-        out, full = run_fg(w, A, B, C, config=cid)
-        check_full(w, A, B, C, out)
+    with few_kernel(kernel):
+        for i, (M, N, K) in enumerate(RAGGED):
+            w0 = wl.custom(M, N, K, ta, tb)
+            kw = dict(lda=_pad4(w0.LDA), ldb=_pad4(w0.LDB), ldc=_pad4(w0.LDC)) if aligned else {}
+            w = wl.custom(M, N, K, ta, tb, alpha=0.5, beta=1.25, dist="normal", seed=90 + i,
+                          **kw)
+            A, B, C = wl.make_inputs(w)
+            out, full = run_fg(w, A, B, C, config=cid)
+            check_full(w, A, B, C, out)
 
 
+@pytest.mark.parametrize("kernel", [1, 2])
 @pytest.mark.parametrize("ta,tb", OPS)
-def test_skinny_integer_exact(ta, tb):
+def test_skinny_integer_exact(ta, tb, kernel):
     cid = skinny_id()
-    for (M, N, K) in [(1, 512, 4096), (4, 65, 1000), (8, 8, 8)]:
-        w = wl.custom(M, N, K, ta, tb, -1.0, 0.5, dist="int8", seed=M + N)
-        A, B, C = wl.make_inputs(w)
-        out, _ = run_fg(w, A, B, C, config=cid)
-        cref, _ = oracle.gemm(ta, tb, M, N, K, -1.0, A, w.LDA, B, w.LDB, 0.5, C, w.LDC)
-        assert np.array_equal(out.astype(np.float64), cref)
+    with few_kernel(kernel):
+        for (M, N, K) in [(1, 512, 4096), (4, 65, 1000), (8, 8, 8), (12, 8200, 777),
+                          (30, 100, 1500)]:
+            w = wl.custom(M, N, K, ta, tb, -1.0, 0.5, dist="int8", seed=M + N)
+            A, B, C = wl.make_inputs(w)
+            out, _ = run_fg(w, A, B, C, config=cid)
+            cref, _ = oracle.gemm(ta, tb, M, N, K, -1.0, A, w.LDA, B, w.LDB, 0.5, C, w.LDC)
+            assert np.array_equal(out.astype(np.float64), cref)
 
 
-@pytest.mark.parametrize("name", ["G1", "G1T", "G8"])
+@pytest.mark.parametrize("name", ["G1", "G1T", "G8", "G8T", "G32"])
 def test_decode_workloads(name):
     """The few-row workloads as the library picks them (auto selection)."""
     w = wl.WORKLOADS[name]
     A, B, C = wl.make_inputs(w)
     out, _ = run_fg(w, A, B, C)
     check_full(w, A, B, C, out)
-    assert fg.fg_select_config(w.transA, w.transB, w.M, w.N, w.K)["kind"] == fg.FG_KIND_SKINNY
+    if w.M <= 8:
+        assert fg.fg_select_config(w.transA, w.transB, w.M, w.N, w.K)["kind"] == \
+            fg.FG_KIND_SKINNY
 
 
 def test_skinny_repeatable():
@@ -81,14 +111,16 @@ def test_skinny_both_k_loops(ta):
     the plain one otherwise: both, with a ragged last k block and K shorter
     than one block, against the oracle."""
     cid = skinny_id()
-    for i, (M, N, K) in enumerate([(8, 1000, 777), (200, 8192, 300), (130, 2047, 100),
-                                   (1, 9000, 2000), (3, 4000, 1500)]):
-        wgs = -(-N // 32) * -(-M // 8)
-        log(f"  grid {wgs} workgroups ({'pipelined' if wgs <= 768 and M > 1 else 'plain'} loop)")
-        w = wl.custom(M, N, K, ta, "N", alpha=1.5, beta=0.5, dist="normal", seed=120 + i)
-        A, B, C = wl.make_inputs(w)
-        out, _ = run_fg(w, A, B, C, config=cid)
-        check_full(w, A, B, C, out)
+    with few_kernel(1):
+        for i, (M, N, K) in enumerate([(8, 1000, 777), (200, 8192, 300), (130, 2047, 100),
+                                       (1, 9000, 2000), (3, 4000, 1500)]):
+            wgs = -(-N // 32) * -(-M // 8)
+            log(f"  grid {wgs} workgroups "
+                f"({'pipelined' if wgs <= 768 and M > 1 else 'plain'} loop)")
+            w = wl.custom(M, N, K, ta, "N", alpha=1.5, beta=0.5, dist="normal", seed=120 + i)
+            A, B, C = wl.make_inputs(w)
+            out, _ = run_fg(w, A, B, C, config=cid)
+            check_full(w, A, B, C, out)
 
 
 @pytest.mark.parametrize("threads", [256, 512, 1024])
@@ -99,6 +131,7 @@ def test_skinny_workgroup_sizes(threads, ta):
     beta, against the oracle; integer inputs bit for bit."""
     cid = skinny_id()
     assert fg.fg_set_few_row_threads(threads) == fg.FG_OK
+    assert fg.fg_set_few_row_kernel(1) == fg.FG_OK
     try:
         for i, (M, N, K) in enumerate([(1, 1000, 3000), (8, 4100, 1025), (5, 300, 100),
                                        (2, 8192, 4096), (8, 257, 2049)]):
@@ -114,3 +147,4 @@ def test_skinny_workgroup_sizes(threads, ta):
         assert np.array_equal(out.astype(np.float64), cref)
     finally:
         assert fg.fg_set_few_row_threads(0) == fg.FG_OK
+        assert fg.fg_set_few_row_kernel(0) == fg.FG_OK
