@@ -187,8 +187,8 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock
             torch.cuda.synchronize()
             clock = finish_clock_watch(watcher)
     cfg = fg.fg_select_config(w.transA, w.transB, w.M, w.N, w.K, dA.data_ptr(), w.LDA,
-                              dB.data_ptr(), w.LDB, dC.data_ptr(), w.LDC) if config < 0 \
-        else fg.fg_get_config(config)
+                              dB.data_ptr(), w.LDB, dC.data_ptr(), w.LDC, quant=quant) \
+        if config < 0 else fg.fg_get_config(config)
     output = None
     if keep_output and epilogue is None:
         # Outside every timed range: one more call on the original C (with

@@ -135,6 +135,9 @@ def load_library(path: str = LIB_PATH):
     lib.fg_select_config.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64,
                                      ctypes.POINTER(fg_config)]
     lib.fg_select_config.restype = i32
+    lib.fg_select_config_quant.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64,
+                                           i32, ctypes.POINTER(fg_config)]
+    lib.fg_select_config_quant.restype = i32
     lib.fg_last_bad_arg.argtypes = []
     lib.fg_last_bad_arg.restype = i32
     lib.fg_last_error.argtypes = []
@@ -249,14 +252,22 @@ def fg_get_config(i: int) -> dict:
 
 
 def fg_select_config(transA, transB, M, N, K, A=0, lda=None, B=0, ldb=None, C=0,
-                     ldc=None) -> dict:
+                     ldc=None, quant=None) -> dict:
+    """The entry fg_sgemm would run (with quant, a format name or FG_QUANT_*
+    code: the entry fg_sgemm_quant would run)."""
     ta, tb = _op(transA), _op(transB)
     lda = lda if lda is not None else max(1, K if ta == FG_OP_N else M)
     ldb = ldb if ldb is not None else max(1, N if tb == FG_OP_N else K)
     ldc = ldc if ldc is not None else max(1, N)
     c = fg_config()
-    _raise_if(load_library().fg_select_config(ta, tb, M, N, K, A or None, lda, B or None,
-                                              ldb, C or None, ldc, ctypes.byref(c)))
+    lib = load_library()
+    if quant is None:
+        _raise_if(lib.fg_select_config(ta, tb, M, N, K, A or None, lda, B or None, ldb,
+                                       C or None, ldc, ctypes.byref(c)))
+    else:
+        kind = quant if isinstance(quant, int) else _QUANTS[quant]
+        _raise_if(lib.fg_select_config_quant(ta, tb, M, N, K, A or None, lda, B or None, ldb,
+                                             C or None, ldc, kind, ctypes.byref(c)))
     return c.as_dict()
 
 

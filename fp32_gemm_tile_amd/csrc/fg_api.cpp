@@ -535,6 +535,27 @@ fg_status fg_select_config(fg_op transA, fg_op transB, int64_t M, int64_t N, int
     return FG_OK;
 }
 
+fg_status fg_select_config_quant(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                                 const float* A, int64_t lda, const float* B, int64_t ldb,
+                                 const float* C, int64_t ldc, int32_t quant_kind,
+                                 fg_config* out) {
+    clear_error();
+    fg_status s = validate(transA, transB, M, N, K, 1.0f, A, lda, B, ldb, C, ldc, false);
+    if (s != FG_OK) return s;
+    if (quant_kind != FG_QUANT_NONE && quant_kind != FG_QUANT_BF16 &&
+        quant_kind != FG_QUANT_INT8_ROW)
+        return fail(FG_ERR_INVALID_ARG, 12, "unknown quantised format %d", quant_kind);
+    if (!out) return fail(FG_ERR_INVALID_ARG, 13, "out is NULL");
+    const int32_t f = build_flags(A, lda, B, ldb, C, ldc, 0.0f);
+    const bool ab_aligned = (f & fg::FLAG_VEC_A) && (f & fg::FLAG_VEC_B);
+    int64_t splits = 1;
+    const int idx = select_entry(M, N, K, ab_aligned, 1, true, &splits, false,
+                                 quant_kind != FG_QUANT_NONE);
+    if (idx < 0) return fail(FG_ERR_UNSUPPORTED, 0, "no table entry fits this call");
+    *out = table()[idx].cfg;
+    return FG_OK;
+}
+
 }  // extern "C"
 
 namespace {

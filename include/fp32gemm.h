@@ -26,7 +26,8 @@
  * Ownership: the caller owns every buffer. A, B and C are device pointers
  * (e.g. from hipMalloc or a framework's allocator). The library allocates,
  * frees and copies nothing and keeps no workspace of its own (split-K takes
- * one from the caller). C must not overlap A or B.
+ * one from the caller), apart from the fixed device array that
+ * fg_sgemm_splitk_noalloc uses instead. C must not overlap A or B.
  *
  * Streams: work is enqueued on `stream` (NULL = the null stream) and the call
  * returns without synchronising; C is complete once the stream reaches that
@@ -66,8 +67,10 @@ typedef enum fg_kind {
     FG_KIND_MFMA = 1,  /* matrix-core contraction, v_mfma_f32_32x32x2_f32 or
                           v_mfma_f32_16x16x4_f32 (fg_config.mr) */
     FG_KIND_VALU = 2,  /* vector-ALU v_fma_f32 outer products (comparison path) */
-    FG_KIND_SKINNY = 3 /* few rows of C: streams op(B) once per block of up to 8
-                          rows, memory-bound (the GEMV shape) */
+    FG_KIND_SKINNY = 3 /* few rows of C (the GEMV shape, memory-bound): streams
+                          op(B) once per block of rows, up to 64 on the matrix
+                          cores (v_mfma_f32_16x16x4_f32, rows padded to 16) or
+                          up to 8 on the vector ALU */
 } fg_kind;
 
 /* Largest leading dimension (elements) the kernels address with 32-bit

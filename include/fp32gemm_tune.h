@@ -79,6 +79,17 @@ fg_status fg_set_few_row_threads(int32_t threads);
  */
 fg_status fg_set_few_row_kernel(int32_t kernel);
 
+/*
+ * As fg_select_config (fp32gemm.h), for a call that also writes a quantised
+ * output of kind quant_kind (fg_quant_kind, argument 12): the entry
+ * fg_sgemm_quant would run with config_id -1 (entries without the quantised
+ * store are passed over). Argument 13: output. Host only.
+ */
+fg_status fg_select_config_quant(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                                 const float* A, int64_t lda, const float* B, int64_t ldb,
+                                 const float* C, int64_t ldc, int32_t quant_kind,
+                                 fg_config* out);
+
 /* The current raster settings (arguments 1, 2: outputs, non-NULL). */
 fg_status fg_get_raster(int32_t* group_m, int32_t* xcd_remap);
 

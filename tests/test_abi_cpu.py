@@ -460,6 +460,23 @@ assert st in NO_DEVICE, st
 """)
 
 
+def test_select_config_quant_skips_entries_without_it():
+    """The entry a quantised call runs: never one built without the quantised
+    store; the same as the plain pick where that one has it."""
+    quant_names = set()
+    for kind in ("bf16", "int8_row"):
+        for shape in [(8192, 8192, 8192), (4096, 4096, 4096), (3001, 2047, 1025), (1, 8192, 8192),
+                      (256, 256, 256)]:
+            plain = fg.fg_select_config("N", "N", *shape)
+            q = fg.fg_select_config("N", "N", *shape, quant=kind)
+            quant_names.add(q["name"])
+            if plain["name"] != q["name"]:
+                assert plain["kind"] == fg.FG_KIND_MFMA and plain["bm"] * plain["bn"] >= 256 * 256
+    assert "mfma_256x256x16_w2x2_s4" not in quant_names
+    with pytest.raises(fg.FgError):
+        fg.fg_select_config("N", "N", 8, 8, 8, quant=7)
+
+
 def test_quant_validation_needs_no_gpu():
     """fg_sgemm_quant checks its quantised-output description (argument 15)
     before any device work; an empty result needs nothing."""
