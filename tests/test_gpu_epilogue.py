@@ -193,3 +193,29 @@ def test_torch_wrapper_fused():
     assert ok, info
     with pytest.raises(ValueError):
         fg.sgemm(A, B, C1, row_scale=torch.ones(149, device="cuda"))
+
+
+@pytest.mark.parametrize("kernel", [1, 2])
+@pytest.mark.parametrize("ops", ["NN", "NT", "TN", "TT"])
+def test_fused_few_row_kernels(kernel, ops):
+    """The fused epilogue in each few-row kernel family (1 vector ALU, 2
+    matrix cores), forced, on few-row shapes with integer operands: bit for
+    bit against the oracle."""
+    cfg = [c["id"] for c in fg.configs() if c["kind"] == fg.FG_KIND_SKINNY][0]
+    assert fg.fg_set_few_row_kernel(kernel) == fg.FG_OK
+    try:
+        for i, (M, N, K) in enumerate([(1, 300, 513), (5, 257, 130), (8, 8200, 64),
+                                       (20, 100, 700)]):
+            for act in ("relu", "silu"):
+                w = workloads.custom(M, N, K, ops[0], ops[1], alpha=-1.5, beta=0.5,
+                                     dist="int8", seed=60 + i)
+                A, B, C = workloads.make_inputs(w)
+                vecs = _vectors(np.random.default_rng(70 + i), M, N, kind="int")
+                out = run_fused(w, A, B, C, vecs, act, config=cfg)
+                if act == "relu":
+                    d, _, _, _ = reference(w, A, B, C, vecs, act)
+                    assert np.array_equal(out, d.astype(np.float32)), (kernel, ops, M, N, K)
+                else:
+                    check(w, A, B, C, vecs, act, out)
+    finally:
+        assert fg.fg_set_few_row_kernel(0) == fg.FG_OK

@@ -235,3 +235,27 @@ def test_quant_large_full(kind):
     cout, codes, _ = run_quant(w, A, B, None, kind, s)
     check_full_blocked(w, A, B, None, cout, name=f"4096^3 with {kind} Q")
     check_q(kind, cout, codes, s)
+
+
+@pytest.mark.parametrize("few_kernel", [1, 2])
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("ta,tb", OPS)
+def test_quant_few_row_kernels(few_kernel, kind, ta, tb):
+    """Q from each few-row kernel family (1 vector ALU, 2 matrix cores),
+    forced, in every layout, with the fused epilogue on: codes bit for bit
+    against the oracle quantiser of the kernel's own C, C within the bound."""
+    cfg = [c["id"] for c in fg.configs() if c["kind"] == fg.FG_KIND_SKINNY][0]
+    rng = np.random.default_rng(80)
+    assert fg.fg_set_few_row_kernel(few_kernel) == fg.FG_OK
+    try:
+        for M, N, K in [(1, 513, 700), (6, 300, 129), (24, 8200, 96)]:
+            w = wl.custom(M, N, K, ta, tb, alpha=1.0, beta=0.0, dist="uniform", seed=M + N)
+            A, B, _ = wl.make_inputs(w)
+            cref, _ = oracle.gemm(ta, tb, M, N, K, 1.0, A, w.LDA, B, w.LDB, 0.0)
+            s = row_factors(cref, rng) if kind == "int8_row" else None
+            cout, codes, raw = run_quant(w, A, B, None, kind, s, config=cfg)
+            check_full(w, A, B, None, cout)
+            check_q(kind, cout, codes, s)
+            check_guard(raw, w, w.N, kind, 0)
+    finally:
+        assert fg.fg_set_few_row_kernel(0) == fg.FG_OK
