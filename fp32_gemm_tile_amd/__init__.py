@@ -170,6 +170,10 @@ def load_library(path: str = LIB_PATH):
     lib.fg_set_few_row_threads.restype = i32
     lib.fg_set_few_row_kernel.argtypes = [i32]
     lib.fg_set_few_row_kernel.restype = i32
+    lib.fg_get_model_constant.argtypes = [i32, ctypes.POINTER(ctypes.c_double)]
+    lib.fg_get_model_constant.restype = i32
+    lib.fg_set_model_constant.argtypes = [i32, ctypes.c_double]
+    lib.fg_set_model_constant.restype = i32
     lib.fg_set_streamk_policy.argtypes = [i32]
     lib.fg_set_streamk_policy.restype = i32
     lib.fg_probe_mfma.argtypes = [i32, i32, vp, vp]
@@ -353,6 +357,23 @@ def fg_set_few_row_threads(threads) -> int:
     """Workgroup size of the few-row kernel, B stored K x N (fp32gemm_tune.h):
     0 = automatic, else 256, 512 or 1024."""
     return load_library().fg_set_few_row_threads(threads)
+
+
+MODEL_CONSTANTS = ("launch", "store_bw", "store_exposed", "stream_bw", "split_bw", "few_fixed",
+                   "few_mfma")   # fg_model_constant, in order
+
+
+def fg_get_model_constant(which) -> float:
+    """A constant of the cost model (index or name of MODEL_CONSTANTS)."""
+    w = which if isinstance(which, int) else MODEL_CONSTANTS.index(which)
+    v = ctypes.c_double()
+    _raise_if(load_library().fg_get_model_constant(w, ctypes.byref(v)))
+    return v.value
+
+
+def fg_set_model_constant(which, value) -> int:
+    w = which if isinstance(which, int) else MODEL_CONSTANTS.index(which)
+    return load_library().fg_set_model_constant(w, value)
 
 
 def fg_set_few_row_kernel(kernel):

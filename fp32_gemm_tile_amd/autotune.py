@@ -44,6 +44,7 @@ import datetime
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -145,16 +146,16 @@ def time_entries(shape, entries, budget_s=0.05):
     return out
 
 
-def fit_entry(entry, samples, wps_gt_1):
+def fit_entry(entry, samples, wps_gt_1, step=0.01):
     """Efficiencies of one modelled entry that minimise the squared log
     error of the model against `samples` = [(M, N, K, seconds), ...]: a grid
     search over eff in [0.30, 1.00] and, when several waves can share a SIMD,
-    eff1 in [0.20, eff] (steps of 0.01). Leaves the library holding the
+    eff1 in [0.20, eff] (steps of `step`). Leaves the library holding the
     best pair; returns (eff, eff1, rms log error)."""
     best = None
-    effs = [round(0.30 + 0.01 * i, 2) for i in range(71)]
+    effs = [round(0.30 + step * i, 2) for i in range(int(round(0.70 / step)) + 1)]
     for eff in effs:
-        ones = [round(0.20 + 0.01 * i, 2) for i in range(int(round((eff - 0.20) / 0.01)) + 1)] \
+        ones = [round(0.20 + step * i, 2) for i in range(int(round((eff - 0.20) / step)) + 1)] \
             if wps_gt_1 else [eff]
         for eff1 in ones:
             fg.fg_set_efficiency(entry, eff, eff1)
@@ -606,6 +607,156 @@ def retime_few_rows(report_path, rounds=3, budget_s=0.25, write=True):
     return report
 
 
+MODEL_INC = os.path.join(HERE, "csrc", "fg_model.inc")
+# Constants of the cost model the search's timings can fix (the split-K slice
+# rate has no timing in them and keeps its default), with the factors tried
+# around the current value in each sweep.
+FIT_CONSTANTS = ("launch", "store_bw", "store_exposed", "stream_bw", "few_fixed", "few_mfma")
+FIT_FACTORS = (0.5, 0.7, 0.85, 0.93, 1.0, 1.07, 1.18, 1.4, 2.0)
+
+
+def model_samples(report):
+    """{table entry id: [(M, N, K, seconds)]} of the built library's
+    modelled entries from a search report: each matrix-core entry's instance
+    times (matched by shape), and the few-row entry's times on the search
+    shapes and on FEW_SHAPES (written by retime_few_rows)."""
+    from fp32_gemm_tile_amd import build as fgbuild
+    by_key = {shape_key(r): r["id"] for r in report["instances"]}
+    out = {}
+    for e in fgbuild.read_instances(INSTANCES_PATH):
+        rid = by_key.get(shape_key(e))
+        out[e["id"]] = [(sh[0], sh[1], sh[2], t[rid]) for sh, t in _report_times(report)
+                        if rid in t]
+    sk = [c["id"] for c in fg.configs() if c["kind"] == fg.FG_KIND_SKINNY][0]
+    sk_rep = _skinny_id(report)
+    few = [(sh[0], sh[1], sh[2], t[sk_rep]) for sh, t in _report_times(report)
+           if sh[0] <= 512 and sk_rep in t]
+    few += [(r["shape"][0], r["shape"][1], r["shape"][2], r["seconds"])
+            for r in report.get("few_rows", {}).get("few_row_shapes", [])]
+    out[sk] = few
+    return out
+
+
+def _fit_all(samples, step):
+    """Refit every entry's efficiencies; total squared log error."""
+    total = 0.0
+    fitted = {}
+    for entry, smp in samples.items():
+        if not smp:
+            continue
+        eff, eff1, rms = fit_entry(entry, smp, eff1_matters(entry), step)
+        fitted[entry] = (eff, eff1, rms)
+        total += rms * rms * len(smp)
+    return total, fitted
+
+
+def _objective(samples, n, report_path, step):
+    """(mean squared log error of the model + mean log loss of the picks,
+    rms log error, geometric-mean pick / fastest, worst pick / fastest,
+    fitted efficiencies): the entries' efficiencies refitted first. The pick
+    term is what the model is for: a lower error that makes the library pick
+    slower entries is no better."""
+    total, fitted = _fit_all(samples, step)
+    rows, worst, geo = check_picks(report_path, write_md=False)
+    return total / n - math.log(geo), math.sqrt(total / n), geo, worst, fitted
+
+
+def _evaluate(samples, n, report_path):
+    """_objective for the library as loaded (no refit): (objective, rms log
+    error, geometric-mean pick / fastest, worst pick / fastest)."""
+    total = 0.0
+    for entry, smp in samples.items():
+        for M, N, K, t in smp:
+            total += math.log(fg.fg_estimate_seconds(M, N, K, entry) / t) ** 2
+    rows, worst, geo = check_picks(report_path, write_md=False)
+    return total / n - math.log(geo), math.sqrt(total / n), geo, worst
+
+
+def fit_model(report_path, sweeps=2, write=True):
+    """Host only: the cost model's shared constants (FIT_CONSTANTS) and the
+    entries' efficiencies, fitted together to the search report's timings by
+    coordinate descent on _objective (each constant tried at FIT_FACTORS of
+    its current value with every entry's efficiencies refitted on a 0.02
+    grid, two sweeps; then a final 0.01 fit). Writes csrc/fg_model.inc and
+    csrc/fg_tuned.inc only if the fit beats the library as built (its
+    compiled constants and efficiencies); records the comparison in the
+    report either way and returns it."""
+    fg.load_library()
+    report = json.load(open(report_path))
+    samples = model_samples(report)
+    n = sum(len(v) for v in samples.values())
+    j0, rms0, geo0, worst0 = _evaluate(samples, n, report_path)
+    cur = {c: fg.fg_get_model_constant(c) for c in FIT_CONSTANTS}
+    start = dict(cur)
+    best = _objective(samples, n, report_path, 0.02)[0]
+    for sweep in range(sweeps):
+        for c in FIT_CONSTANTS:
+            base = cur[c]
+            for f in FIT_FACTORS:
+                v = base * f
+                if fg.fg_set_model_constant(c, v) != fg.FG_OK:
+                    continue
+                j = _objective(samples, n, report_path, 0.02)[0]
+                if j < best - 1e-12:
+                    best, cur[c] = j, v
+            fg.fg_set_model_constant(c, cur[c])
+            print(f"[fit-model] sweep {sweep}: {c} = {cur[c]:.4g}, objective {best:.5f}",
+                  flush=True)
+    j1, rms1, geo1, worst1, fitted = _objective(samples, n, report_path, 0.01)
+    result = {"constants": cur, "samples": n,
+              "before": {"objective": j0, "rms_log_error": rms0, "geomean_pick": geo0,
+                         "worst_pick": worst0, "constants": start},
+              "after": {"objective": j1, "rms_log_error": rms1, "geomean_pick": geo1,
+                        "worst_pick": worst1}}
+    print(f"[fit-model] objective {j0:.5f} -> {j1:.5f}; rms log error {rms0:.4f} -> "
+          f"{rms1:.4f}; picks (geo mean, worst) {geo0:.4f}, {worst0:.4f} -> {geo1:.4f}, "
+          f"{worst1:.4f} over {n} timings", flush=True)
+    if j1 >= j0:
+        print("[fit-model] no improvement on the library as built; constants and "
+              "efficiencies unchanged", flush=True)
+        result["written"] = False
+        if write:
+            report["model_fit"] = result
+            with open(report_path, "w") as f:
+                json.dump(report, f)
+        return result
+    result["written"] = True
+    rmsb, rmsa = rms0, rms1
+    result["rms_log_error_before"], result["rms_log_error_after"] = rmsb, rmsa
+    if write:
+        lines = ["// Fitted constants of the cost model: FG_MODEL(fg_model_constant, value).",
+                 "// Written by fp32_gemm_tile_amd/autotune.py --fit-model from the tile search's",
+                 f"// timings ({n} timings of the table's entries, one MI355X, "
+                 f"{report['date'][:10]}): rms log error",
+                 f"// {rmsb:.4f} -> {rmsa:.4f}, the library's pick on the search shapes "
+                 f"{geo0:.4f} -> {geo1:.4f} of the",
+                 f"// fastest instance on geometric mean ({worst0:.4f} -> {worst1:.4f} at "
+                 "worst). The split-K slice",
+                 "// rate (FG_MODEL_SPLIT_BW) has no timing there and keeps its default."]
+        for c in FIT_CONSTANTS:
+            lines.append(f"FG_MODEL(FG_MODEL_{c.upper()}, {cur[c]:.6g})")
+        with open(MODEL_INC, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        old = open(INC_PATH).read().splitlines()
+        new = []
+        for l in old:
+            m = re.match(r"\{(\w+), [0-9.]+, [0-9.]+\},(.*)", l)
+            if m:
+                key = m.group(1)
+                eid = [c["id"] for c in fg.configs() if c["kind"] == fg.FG_KIND_SKINNY][0] \
+                    if key == "FG_ID_SKINNY" else int(key)
+                if eid in fitted:
+                    eff, eff1, _ = fitted[eid]
+                    l = f"{{{key}, {eff:.3f}, {eff1:.3f}}},{m.group(2)}"
+            new.append(l)
+        with open(INC_PATH, "w") as f:
+            f.write("\n".join(new) + "\n")
+        report["model_fit"] = result
+        with open(report_path, "w") as f:
+            json.dump(report, f)
+    return result
+
+
 REPORT_PATH = os.path.join(HERE, "tuning", "tile_search.json")
 SEARCH_MD = os.path.join(ROOT, "profiles", "tile_search.md")
 COVER_MARGIN = 0.01
@@ -826,6 +977,10 @@ def main(argv=None):
     ap.add_argument("--refine", default=None, metavar="REPORT",
                     help="on the GPU: re-time the near-fastest instances of every shape of "
                          "REPORT (updates it)")
+    ap.add_argument("--fit-model", default=None, metavar="REPORT",
+                    help="host only: fit the cost model's shared constants and the entries' "
+                         "efficiencies to REPORT's timings (rewrites csrc/fg_model.inc and "
+                         "csrc/fg_tuned.inc)")
     ap.add_argument("--retime-few-rows", default=None, metavar="REPORT",
                     help="on the GPU: re-time the built library's few-row entry on the search "
                          "shapes of REPORT, refit its efficiency (updates REPORT and "
@@ -847,6 +1002,9 @@ def main(argv=None):
         return 0
     if args.refine:
         refine_search(args.refine)
+        return 0
+    if args.fit_model:
+        fit_model(args.fit_model)
         return 0
     if args.retime_few_rows:
         retime_few_rows(args.retime_few_rows)

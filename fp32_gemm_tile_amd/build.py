@@ -154,7 +154,8 @@ def build(verbose: bool = False, instances: str = INSTANCES, tuned: str | None =
                          os.path.join(build_dir, f"sgemm_mfma_e{e['id']}_stubs.o"),
                          [f"-DFG_ENTRY_ID={e['id']}", f"-DFG_ENTRY_STUBS={stubs}"]))
     table_files = [os.path.abspath(instances),
-                   os.path.abspath(tuned) if tuned else os.path.join(CSRC, "fg_tuned.inc")]
+                   os.path.abspath(tuned) if tuned else os.path.join(CSRC, "fg_tuned.inc"),
+                   os.path.join(CSRC, "fg_model.inc")]
     if incremental:
         keep = [w for w in work if not _stale(w[1], _deps(w[0], table_files))]
         work = [w for w in work if w not in keep]

@@ -34,6 +34,9 @@
 #ifndef FG_TUNED_INC
 #define FG_TUNED_INC "fg_tuned.inc"
 #endif
+#ifndef FG_MODEL_INC
+#define FG_MODEL_INC "fg_model.inc"
+#endif
 
 namespace {
 
@@ -214,9 +217,36 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // split-K slices: the rounds of resident waves the grid needs, plus, with
 // split-K, the partial slices written, read back and reduced at HBM speed.
 constexpr double kSimdFlops = 157.3e12 / (kNumCUs * kSimdsPerCU);  // fp32 MFMA per SIMD
-constexpr double kHbmBytes = 5.0e12;                              // sustained, not peak
-constexpr double kHbmStream = 6.3e12;                             // best streaming rate measured
-constexpr double kLaunch = 3e-6;                                  // one more kernel
+
+// Constants shared by the entries' cost models (fg_model_constant): the
+// defaults below are first estimates from measurements on one MI355X; the
+// values fitted by the tuner to the tile search's timings (fg_model.inc)
+// replace them; a tuner may set them at run time (fg_set_model_constant).
+struct ModelConstants {
+    std::atomic<double> v[FG_MODEL_COUNT];
+};
+ModelConstants& model_constants() {
+    static ModelConstants m;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        const double defaults[FG_MODEL_COUNT] = {
+            3e-6,    // FG_MODEL_LAUNCH: one more kernel
+            6.4e12,  // FG_MODEL_STORE_BW: C tiles leaving the CUs (non-temporal stores)
+            0.25,    // FG_MODEL_STORE_EXPOSED: share of those stores not hidden by another
+                     //   workgroup's main loop when several share a SIMD
+            6.3e12,  // FG_MODEL_STREAM_BW: a stream of the operands, compulsory bytes
+            5.0e12,  // FG_MODEL_SPLIT_BW: split-K partial slices, sustained
+            5e-6,    // FG_MODEL_FEW_FIXED: launch and reduction of the few-row entry
+            0.5,     // FG_MODEL_FEW_MFMA: matrix-core efficiency of the few-row kernel
+        };
+        for (int i = 0; i < FG_MODEL_COUNT; ++i) m.v[i].store(defaults[i]);
+#define FG_MODEL(which, value) m.v[which].store(value);
+#include FG_MODEL_INC
+#undef FG_MODEL
+    });
+    return m;
+}
+double mc(int which) { return model_constants().v[which].load(std::memory_order_relaxed); }
 
 int64_t effective_splits(int64_t K, int64_t bk, int64_t splits, int64_t* kt_per_split) {
     const int64_t kt_total = cdiv(K, bk);
@@ -255,17 +285,16 @@ double rounds_time(const Entry& e, int64_t workgroups, int64_t kps) {
 // share each SIMD, the SIMDs of a storing workgroup idle meanwhile; when they
 // do, one workgroup's stores overlap another's main loop (counted at a
 // quarter).
-constexpr double kHbmWrite = 6.4e12;  // C stores with the non-temporal hint
 double store_time(const Entry& e, int64_t workgroups) {
     const int64_t w = e.cfg.threads / 64;
     const int64_t slots = std::max<int64_t>(1, (int64_t)e.wps * kSimdsPerCU / w);
     const double tile_bytes = 4.0 * e.cfg.bm * e.cfg.bn;
     const int64_t per_simd = slots * std::min<int64_t>(w, kSimdsPerCU) / kSimdsPerCU;
-    const double exposed = per_simd > 1 ? 0.25 : 1.0;
+    const double exposed = per_simd > 1 ? mc(FG_MODEL_STORE_EXPOSED) : 1.0;
     double t = 0.0;
     for (int64_t left = workgroups; left > 0; left -= (int64_t)kNumCUs * slots)
         t += exposed * (double)std::min<int64_t>(left, (int64_t)kNumCUs * slots) * tile_bytes /
-             kHbmWrite;
+             mc(FG_MODEL_STORE_BW);
     return t;
 }
 
@@ -273,26 +302,27 @@ double cost(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t splits, boo
     int64_t kps = 0;
     const int64_t s = effective_splits(K, e.cfg.bk, splits, &kps);
     const int64_t tiles = cdiv(M, e.cfg.bm) * cdiv(N, e.cfg.bn);
-    double t = kLaunch + rounds_time(e, tiles * s, kps) + store_time(e, tiles * s);
+    const double launch = mc(FG_MODEL_LAUNCH);
+    double t = launch + rounds_time(e, tiles * s, kps) + store_time(e, tiles * s);
     // Every operand byte crosses HBM at least once (what bounds few-row
     // shapes whatever the tile).
     const double compulsory =
         4.0 * ((double)M * K + (double)K * N + (double)M * N * (beta0 ? 1 : 2));
-    t = std::max(t, kLaunch + compulsory / kHbmStream);
+    t = std::max(t, launch + compulsory / mc(FG_MODEL_STREAM_BW));
     if (s > 1)
-        t += ((double)(2 * s + (beta0 ? 1 : 2)) * M * N * 4.0) / kHbmBytes + kLaunch;
+        t += ((double)(2 * s + (beta0 ? 1 : 2)) * M * N * 4.0) / mc(FG_MODEL_SPLIT_BW) + launch;
     return t;
 }
 
 // Few-row entry, modelled from measurements on one MI355X: one pass over
 // op(B) per block of up to 64 rows, bound by the stream of op(B) (scaled down
 // when the grid has fewer than one workgroup per CU) or by the matrix cores,
-// which see the rows padded to 16, 32 or 64 and reach about half of peak here
-// (32 x 8192 x 8192: 58.6 us measured; 64 rows: 99.5). With B stored N x K
-// and at most 4 rows the vector-ALU kernel runs instead, at the same stream
-// rate. The entry's efficiency (fitted by the tuner) divides the matrix-core
-// term. The fixed cost covers the launch and the final reduction.
-constexpr double kSkinnyFixed = 5e-6;
+// which see the rows padded to 16, 32 or 64 and reach a fraction
+// FG_MODEL_FEW_MFMA of their peak (about half: 32 x 8192 x 8192 takes 58.6 us,
+// 64 rows 99.5). With B stored N x K and at most 4 rows the vector-ALU kernel
+// runs instead, at the same stream rate. The entry's efficiency (fitted by
+// the tuner) divides the matrix-core term. The fixed cost covers the launch
+// and the final reduction.
 constexpr int64_t kFewRowsMax = 512;  // rows up to which the entry competes
 double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0, double eff) {
     const double bytes_c = 4.0 * ((double)M * K + (double)M * N * (beta0 ? 1 : 2));
@@ -300,9 +330,9 @@ double skinny_cost(int64_t M, int64_t N, int64_t K, bool beta0, double eff) {
     const double passes = (double)cdiv(M, rows);
     const double wgs = passes * (double)cdiv(N, N >= 32 * kNumCUs ? 32 : 16);
     const double fill = std::min(1.0, wgs / kNumCUs);
-    const double t_mem = (4.0 * (double)K * N * passes + bytes_c) / (kHbmStream * fill);
-    const double t_mfma = 2.0 * (double)rows * N * K * passes / (157.3e12 * 0.5);
-    return kSkinnyFixed + std::max(t_mem, t_mfma / eff);
+    const double t_mem = (4.0 * (double)K * N * passes + bytes_c) / (mc(FG_MODEL_STREAM_BW) * fill);
+    const double t_mfma = 2.0 * (double)rows * N * K * passes / (157.3e12 * mc(FG_MODEL_FEW_MFMA));
+    return mc(FG_MODEL_FEW_FIXED) + std::max(t_mem, t_mfma / eff);
 }
 
 // Best MFMA or few-row entry (and split count, at most max_splits). With
@@ -467,9 +497,9 @@ bool plan_streamk(int64_t M, int64_t N, int64_t K, bool ab_aligned, bool beta0, 
     // Only when the model expects a gain: full rounds + the split tail + the
     // slot traffic of the reduction against the plain call.
     const int64_t kt_total = cdiv(K, e.cfg.bk);
-    const double t_split = 3 * kLaunch + rounds_time(e, full, kt_total) + store_time(e, full) +
+    const double t_split = 3 * mc(FG_MODEL_LAUNCH) + rounds_time(e, full, kt_total) + store_time(e, full) +
                            rounds_time(e, tail * splits, kps) + store_time(e, tail * splits) +
-                           (double)tail * (splits + (beta0 ? 1 : 2)) * slot_bytes / kHbmBytes;
+                           (double)tail * (splits + (beta0 ? 1 : 2)) * slot_bytes / mc(FG_MODEL_SPLIT_BW);
     if (g_streamk_policy.load() == 0 && t_split > 0.97 * cost(e, M, N, K, 1, beta0)) return false;
     out->tiles = tiles;
     out->full = full;
@@ -926,6 +956,26 @@ fg_status fg_set_few_row_threads(int32_t threads) {
     if (threads != 0 && threads != 256 && threads != 512 && threads != 1024)
         return fail(FG_ERR_INVALID_ARG, 1, "threads must be 0, 256, 512 or 1024");
     g_few_row_threads.store(threads);
+    return FG_OK;
+}
+
+fg_status fg_get_model_constant(int32_t which, double* value) {
+    clear_error();
+    if (which < 0 || which >= FG_MODEL_COUNT)
+        return fail(FG_ERR_INVALID_ARG, 1, "model constant %d out of range", which);
+    if (!value) return fail(FG_ERR_INVALID_ARG, 2, "value is NULL");
+    *value = mc(which);
+    return FG_OK;
+}
+
+fg_status fg_set_model_constant(int32_t which, double value) {
+    clear_error();
+    if (which < 0 || which >= FG_MODEL_COUNT)
+        return fail(FG_ERR_INVALID_ARG, 1, "model constant %d out of range", which);
+    const bool fraction = which == FG_MODEL_STORE_EXPOSED || which == FG_MODEL_FEW_MFMA;
+    if (!(value > 0.0) || (fraction && value > 1.0) || !(value < 1e300))
+        return fail(FG_ERR_INVALID_ARG, 2, "value %g outside its domain", value);
+    model_constants().v[which].store(value);
     return FG_OK;
 }
 

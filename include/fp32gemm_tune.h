@@ -90,6 +90,27 @@ fg_status fg_select_config_quant(fg_op transA, fg_op transB, int64_t M, int64_t 
                                  const float* C, int64_t ldc, int32_t quant_kind,
                                  fg_config* out);
 
+/*
+ * Constants shared by the cost models of the table entries (fitted together
+ * with the entries' efficiencies by the tuner and compiled in; settable for
+ * a refit). FG_ERR_INVALID_ARG for an unknown constant (argument 1) or a
+ * value outside its domain (argument 2: positive; at most 1 for fractions).
+ */
+typedef enum fg_model_constant {
+    FG_MODEL_LAUNCH = 0,        /* seconds per further kernel launch */
+    FG_MODEL_STORE_BW = 1,      /* bytes/s at which C tiles leave the CUs */
+    FG_MODEL_STORE_EXPOSED = 2, /* fraction of those stores not hidden when several
+                                   workgroups share a SIMD */
+    FG_MODEL_STREAM_BW = 3,     /* bytes/s of one pass over the operands */
+    FG_MODEL_SPLIT_BW = 4,      /* bytes/s of split-K and stream-K partial slices */
+    FG_MODEL_FEW_FIXED = 5,     /* seconds of fixed cost of the few-row entry */
+    FG_MODEL_FEW_MFMA = 6,      /* fraction of the matrix peak the few-row matrix-core
+                                   kernel reaches on its padded rows */
+    FG_MODEL_COUNT = 7
+} fg_model_constant;
+fg_status fg_get_model_constant(int32_t which, double* value);
+fg_status fg_set_model_constant(int32_t which, double value);
+
 /* The current raster settings (arguments 1, 2: outputs, non-NULL). */
 fg_status fg_get_raster(int32_t* group_m, int32_t* xcd_remap);
 

@@ -460,6 +460,31 @@ assert st in NO_DEVICE, st
 """)
 
 
+def test_model_constants_hooks():
+    """The cost model's shared constants: readable, settable within their
+    domain (fractions at most 1), and they move the estimates."""
+    assert len(fg.MODEL_CONSTANTS) == 7
+    old = {c: fg.fg_get_model_constant(c) for c in fg.MODEL_CONSTANTS}
+    assert all(v > 0 for v in old.values())
+    big = [c["id"] for c in fg.configs() if c["name"] == "mfma_256x256x16_w2x2_s4"][0]
+    few = [c["id"] for c in fg.configs() if c["kind"] == fg.FG_KIND_SKINNY][0]
+    try:
+        t = fg.fg_estimate_seconds(256, 256, 256, big)
+        assert fg.fg_set_model_constant("launch", old["launch"] + 1e-3) == fg.FG_OK
+        assert abs(fg.fg_estimate_seconds(256, 256, 256, big) - (t + 1e-3)) < 1e-9
+        t = fg.fg_estimate_seconds(8, 8192, 8192, few)
+        assert fg.fg_set_model_constant("stream_bw", old["stream_bw"] / 2) == fg.FG_OK
+        assert fg.fg_estimate_seconds(8, 8192, 8192, few) > 1.5 * t - 1e-5
+        for bad in (("store_exposed", 1.5), ("few_mfma", 0.0), ("launch", -1.0)):
+            assert fg.fg_set_model_constant(*bad) == fg.FG_ERR_INVALID_ARG
+            assert fg.fg_last_bad_arg() == 2
+        assert fg.fg_set_model_constant(7, 1.0) == fg.FG_ERR_INVALID_ARG
+        assert fg.fg_last_bad_arg() == 1
+    finally:
+        for c, v in old.items():
+            assert fg.fg_set_model_constant(c, v) == fg.FG_OK
+
+
 def test_select_config_quant_skips_entries_without_it():
     """The entry a quantised call runs: never one built without the quantised
     store; the same as the plain pick where that one has it."""
