@@ -2,22 +2,19 @@
 // blocking, warp tiling, tensor cores", section 8, where the kernel is a
 // memory-bound GEMV and the game is bytes).
 //
-// With M <= 8 the product reads every element of op(B) once and does only
-// 2*M flops per element, so the bound is HBM bandwidth, not the matrix
-// cores: this kernel streams op(B) with coalesced 128-bit loads, keeps MR
-// (1, 2, 4 or 8) rows of results per thread in registers, and reduces the
-// per-thread partial sums in a fixed order (deterministic results). Larger M
-// runs as ceil(M / MR) row blocks (blockIdx.y), each streaming op(B) again.
-//
-// Two layouts of op(B):
-//   * B stored K x N (n contiguous): a workgroup owns 32 columns; lane
-//     (g = lane % 8) loads columns 4g..4g+3 of one k row, the 32 lane-rows
-//     of the workgroup (8 per wave) step through k together, so each wave
-//     load covers 8 rows x 128 contiguous bytes. Partial sums over the 32
-//     k classes are reduced with lane shuffles, then across waves in LDS.
-//   * B stored N x K (k contiguous): a wave owns 4 columns and its 64 lanes
-//     read 256 consecutive k of each (one 1 KiB load per column); the 64
-//     lane partials of every (row, column) are reduced with shuffles.
+// With a few rows the product reads every element of op(B) once and does only
+// 2M flops per element, so the bound is HBM bandwidth: every kernel here
+// streams op(B) once per block of rows with coalesced 128-bit loads and
+// reduces partial sums in a fixed order (deterministic results).
+//   * few_rows_mfma_kernel (the default): the products on
+//     v_mfma_f32_16x16x4_f32 with the rows padded to blocks of 16 (up to 64
+//     rows per pass), 16 waves of a workgroup splitting K for the same
+//     columns, for either layout of op(B);
+//   * skinny_mn_kernel (vector ALU, B stored K x N): 32 columns per
+//     workgroup, 4 per lane, k-row classes down K, op(A) staged in LDS;
+//   * skinny_k_kernel (vector ALU, B stored N x K; the automatic choice for
+//     at most 4 rows): each wave reads 256 consecutive k of a column per
+//     load, several waves split K for the same columns.
 // op(A) is read with ordinary (cached) loads: it is M x K, small next to B.
 // Every global access goes through a buffer resource bounded by the matrix.
 #include "fg_device.h"
@@ -457,16 +454,15 @@ hipError_t launch_mr(int ta, int tb, const GemmParams& p, hipStream_t s, int thr
 // TB/s). Here every product goes through v_mfma_f32_16x16x4_f32 with the
 // rows of C padded to RB blocks of 16 (M <= 16 RB per grid row):
 //   * lane l gives op(A)(16 b + l % 16, k) and op(B)(k, column) for
-//     k = k0 + 4 (l / 16) + s at step s of a 16-deep k block; the four k of
-//     a lane are consecutive (the sum over k is order-free), so op(A) stored
-//     M x K and op(B) stored N x K are read with one 128-bit load per lane,
-//     row block or column set, and k block;
+//     k = k0 + KPL (l / 16) + s at step s of a 4 KPL-deep k block; the KPL k
+//     of a lane are consecutive (the sum over k is order-free), so op(A)
+//     stored M x K and op(B) stored N x K are read with 128-bit loads along k;
 //   * op(B) stored K x N: a lane's CS columns CS (l % 16) + c are one CS-wide
 //     load per k row (column set c of the instruction holds them);
 //   * lane l ends with rows 4 (l / 16) + r, r < 4, of its column.
 // A workgroup of 16 waves owns 16 CS columns; wave w takes k blocks w,
 // w + 16, ... (UB blocks per round of loads), and the 16 partial tiles are
-// added in LDS in wave order (deterministic), one element per work-item.
+// added in LDS in wave order (deterministic) before the epilogue.
 constexpr int kFewWaves = 16;
 // k per lane per block (B stored K x N, N x K), registers of loaded operands
 // per round, pipelined rounds. Measured on one MI355X against 4, 4, 48, plain
