@@ -55,21 +55,46 @@ def _run(ta, tb, M, N, K, lda, ldb, ldc, config, alpha=1.5, beta=0.5, seed=0):
     assert ok, info
 
 
+class _few_kernel:
+    """Force a few-row kernel family (1 vector ALU: for B stored K x N the
+    instance that rebases per k step; 2 matrix cores) for a block of calls."""
+
+    def __init__(self, kernel):
+        self.kernel = kernel
+
+    def __enter__(self):
+        assert fg.fg_set_few_row_kernel(self.kernel) == fg.FG_OK
+
+    def __exit__(self, *exc):
+        assert fg.fg_set_few_row_kernel(0) == fg.FG_OK
+
+
+@pytest.mark.parametrize("kernel", [1, 2])
 @pytest.mark.parametrize("M", [1, 8])
-def test_few_rows_b_kxn_at_max_ld(M):
+def test_few_rows_b_kxn_at_max_ld(M, kernel):
     # B stored K x N: 700 rows of ldb = 2^21 (5.9 GB); byte offsets from the
     # block's first row pass 2^32 at row 512.
-    _run("N", "N", M, 300, 700, 700, LD, LD, _config(kind=fg.FG_KIND_SKINNY))
+    with _few_kernel(kernel):
+        _run("N", "N", M, 300, 700, 700, LD, LD, _config(kind=fg.FG_KIND_SKINNY))
 
 
+@pytest.mark.parametrize("kernel", [1, 2])
+@pytest.mark.parametrize("M", [3, 8])
 @pytest.mark.parametrize("tb", ["N", "T"])
-def test_few_rows_a_kxm_at_max_ld(tb):
+def test_few_rows_a_kxm_at_max_ld(tb, M, kernel):
     # A stored K x M with lda = 2^21 (5.9 GB), B in either layout.
-    _run("T", tb, 8, 300, 700, LD, 300 if tb == "N" else 700, 300,
-         _config(kind=fg.FG_KIND_SKINNY))
+    with _few_kernel(kernel):
+        _run("T", tb, M, 300, 700, LD, 300 if tb == "N" else 700, 300,
+             _config(kind=fg.FG_KIND_SKINNY))
 
 
 @pytest.mark.parametrize("ta,tb", [("N", "N"), ("T", "T")])
 def test_mfma_tiles_at_max_ld(ta, tb):
     # 256-row tiles: row offsets up to 255 * 2^21 * 4 bytes inside a tile.
     _run(ta, tb, 300, 200, 150, LD, LD, LD, _config(name="mfma_256x256x16_w2x2_s4"))
+
+
+@pytest.mark.parametrize("ta,tb", [("N", "N"), ("T", "T")])
+def test_valu_tiles_at_max_ld(ta, tb):
+    # The vector-ALU comparison kernel's 128-row tiles at the same leading dimensions.
+    _run(ta, tb, 300, 200, 150, LD, LD, LD, _config(name="valu_128x128x8_t8x8"))
