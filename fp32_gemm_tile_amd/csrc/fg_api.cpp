@@ -730,6 +730,10 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
         return fail(FG_ERR_INVALID_ARG, config_arg, "entry %s has no quantised output",
                     en.cfg.name);
     if (en.cfg.kind != FG_KIND_MFMA) want = 1;  // split-K runs on the MFMA kernels
+    // The few-row kernels put their blocks of rows (8 on the vector ALU, at
+    // least 16 on the matrix cores) on the grid's y dimension (at most 65535).
+    if (en.cfg.kind == FG_KIND_SKINNY && cdiv(M, 8) > 65535)
+        return fail(FG_ERR_UNSUPPORTED, 0, "the few-row entry takes at most %d rows", 65535 * 8);
 
     int64_t kps = 0;
     // k-tile depth of the MFMA kernels; the other kinds ignore the split.

@@ -460,6 +460,17 @@ assert st in NO_DEVICE, st
 """)
 
 
+def test_few_rows_entry_refuses_too_many_rows():
+    """The few-row entry forced on more rows than its grid can hold: refused
+    on the host (run with the GPU hidden, so nothing could launch anyway)."""
+    run_without_gpu(f"""
+few = [c["id"] for c in fg.configs() if c["kind"] == fg.FG_KIND_SKINNY][0]
+st = fg.fg_sgemm_ex(0, 0, 65535 * 8 + 1, 4, 4, 1.0, 16, 4, 16, 4, 0.0, 16, 4, None, few)
+assert st == fg.FG_ERR_UNSUPPORTED, st
+assert "few-row entry" in fg.fg_last_error()
+""")
+
+
 def test_model_constants_hooks():
     """The cost model's shared constants: readable, settable within their
     domain (fractions at most 1), and they move the estimates."""
