@@ -70,7 +70,9 @@ typedef enum fg_kind {
     FG_KIND_SKINNY = 3 /* few rows of C (the GEMV shape, memory-bound): streams
                           op(B) once per block of rows, up to 64 on the matrix
                           cores (v_mfma_f32_16x16x4_f32, rows padded to 16) or
-                          up to 8 on the vector ALU */
+                          up to 8 on the vector ALU; chosen automatically only
+                          up to 512 rows, and forced calls with more than
+                          524280 rows return FG_ERR_UNSUPPORTED */
 } fg_kind;
 
 /* Largest leading dimension (elements) the kernels address with 32-bit
