@@ -688,6 +688,7 @@ def fit_model(report_path, sweeps=2, write=True):
     j0, rms0, geo0, worst0 = _evaluate(samples, n, report_path)
     cur = {c: fg.fg_get_model_constant(c) for c in FIT_CONSTANTS}
     start = dict(cur)
+    built_eff = {e: fg.fg_get_efficiency(e) for e in samples}
     best = _objective(samples, n, report_path, 0.02)[0]
     for sweep in range(sweeps):
         for c in FIT_CONSTANTS:
@@ -715,6 +716,11 @@ def fit_model(report_path, sweeps=2, write=True):
         print("[fit-model] no improvement on the library as built; constants and "
               "efficiencies unchanged", flush=True)
         result["written"] = False
+        # the loaded library's model back to what it was built with
+        for c, v in start.items():
+            fg.fg_set_model_constant(c, v)
+        for e, (eff, eff1) in built_eff.items():
+            fg.fg_set_efficiency(e, eff, eff1)
         if write:
             report["model_fit"] = result
             with open(report_path, "w") as f:

@@ -7,6 +7,7 @@ process with the GPUs hidden (run_without_gpu), so even on a machine with a
 GPU none of them can enqueue work on those addresses."""
 import ctypes
 import glob
+import json
 import os
 import re
 import subprocess
@@ -582,3 +583,27 @@ def test_streamk_plan_and_validation():
     st = fg.fg_sgemm_streamk(0, 0, 64, 64, 64, 1.0, 16, 63, 16, 64, 0.0, 16, 64, 0, 0, 0)
     assert st == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 8
     assert fg.fg_sgemm_streamk(0, 0, 0, 64, 64, 1.0, 16, 64, 16, 64, 0.0, 16, 64, 0, 0, 0) == 0
+
+
+def test_model_fit_runs_and_keeps_the_better_model(tmp_path):
+    """autotune --fit-model on a copy of the search report, without sweeps:
+    it reads the table's timings, compares the refitted model with the
+    library as built, and writes nothing unless the refit is better."""
+    import shutil
+    from fp32_gemm_tile_amd import autotune
+    rep = tmp_path / "report.json"
+    shutil.copy(autotune.REPORT_PATH, rep)
+    inc_before = open(autotune.INC_PATH).read()
+    model_before = open(autotune.MODEL_INC).read()
+    ids = [i for i in autotune.model_samples(json.load(open(rep)))]
+    eff_before = {i: fg.fg_get_efficiency(i) for i in ids}
+    const_before = {c: fg.fg_get_model_constant(c) for c in autotune.FIT_CONSTANTS}
+    r = autotune.fit_model(str(rep), sweeps=0, write=False)
+    assert r["samples"] >= 200
+    assert r["before"]["geomean_pick"] > 0.99 and r["after"]["rms_log_error"] < 0.2
+    assert open(autotune.INC_PATH).read() == inc_before
+    assert open(autotune.MODEL_INC).read() == model_before
+    if not r["written"]:
+        # the loaded library's model is the one it was built with again
+        assert {i: fg.fg_get_efficiency(i) for i in ids} == eff_before
+        assert {c: fg.fg_get_model_constant(c) for c in autotune.FIT_CONSTANTS} == const_before
