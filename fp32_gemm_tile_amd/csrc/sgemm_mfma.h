@@ -342,6 +342,9 @@ sgemm_mfma_kernel(GemmParams p) {
     // lane its store loops pushed the accumulators to scratch memory. The
     // host sends quantised calls to other entries (fg_api.cpp).
     constexpr bool kQuant = MB * NB * NREG <= 128;
+    // The same limit for the epilogue that stages C through LDS when C's rows
+    // are unaligned (with 256 accumulators its registers spilled).
+    constexpr bool kStageC = NB >= 2 && MB * NB * NREG <= 128;
 
     __shared__ f4 smem[NS * (OpA::kStage + OpB::kStage) / 4];
     float* sA = reinterpret_cast<float*>(smem);
@@ -579,6 +582,96 @@ sgemm_mfma_kernel(GemmParams p) {
         constexpr int CH = NB >= 8 ? 1 : (8 / NB < NREG ? 8 / NB : NREG);
         constexpr int NQ = MB * (NREG / CH);  // chunks
         static_assert(NREG % CH == 0, "whole chunks");
+        if (kStageC && !vec_c) {
+            // C's rows are not aligned for a lane's NB adjacent columns to be
+            // one access, and NB single stores per row would each scatter over
+            // the row with a stride of NB elements. Instead each chunk passes
+            // through a slice of the idle operand ring that belongs to this
+            // wave: the lanes write their accumulators there, then read it
+            // back so that lane l holds element l + 64 j of the chunk (local
+            // row e / WN, column e % WN), and one single-element store (or old
+            // C read) covers 64 consecutive elements of a row of C (WN = 32:
+            // two rows of 32).
+            constexpr int HR = 64 / MR;  // lane groups = rows per register
+            constexpr int V = CH * NB;   // elements per lane per chunk
+            static_assert(NW * 64 * V <= NS * (OpA::kStage + OpB::kStage), "slices fit in LDS");
+            float* const slice = sA + wave * (64 * V);
+            const int nrow = p.M - m0, ncol = p.N - n0 - wave_n * WN;
+            // Elements past M or N get a byte offset past the end of a
+            // resource that spans at most 2^31 bytes from the tile origin
+            // (every element of a tile lies below that: at most 255 rows of
+            // at most 2^21 elements), so that their loads read 0 and their
+            // stores are dropped with no branch: a branch around each access
+            // made the compiler wait for every earlier store before each use
+            // of the old C.
+            constexpr uint32_t kOut = 0xFFFFFFF0u;
+            const int64_t c_ext = tile_ws ? (int64_t)BM * BN : p.c_extent - c_org;
+            const __amdgpu_buffer_rsrc_t rt =
+                make_rsrc(Cs + c_org, c_ext < (int64_t(1) << 29) ? c_ext : (int64_t(1) << 29));
+            // Local row and column of element j: with WN >= 64 the row is the
+            // same for the whole wave (a scalar) and the column is the lane's
+            // plus a constant; with WN = 32 the two halves of the wave take
+            // two consecutive local rows.
+            const int lsub = WN >= 64 ? 0 : elane / WN, lcol = WN >= 64 ? elane : elane % WN;
+            auto elem = [&](int q, int j) -> uint32_t {
+                const int a = q / (NREG / CH), r0 = (q % (NREG / CH)) * CH;
+                const int lr = WN >= 64 ? (64 * j) / WN : (64 / WN) * j + lsub;
+                const int col = WN >= 64 ? lcol + (64 * j) % WN : lcol;
+                const int row = wave_m * WM + MB * Mfma<MR>::row(r0 + lr / HR, lr % HR) + a;
+                return row < nrow && col < ncol
+                           ? (uint32_t)(row * p.ldc + wave_n * WN + col) * 4u
+                           : kOut;
+            };
+            auto load_cs = [&](int q, float (&cin)[V]) {
+#pragma unroll
+                for (int j = 0; j < V; ++j) cin[j] = ld1(rt, elem(q, j));
+            };
+            auto store_cs = [&](int q, const float (&cin)[V], bool with_c) {
+                const int a = q / (NREG / CH), r0 = (q % (NREG / CH)) * CH;
+#pragma unroll
+                for (int i = 0; i < CH; ++i) {
+                    float* const d = slice + (i * HR + elh) * WN + NB * eli;
+                    if constexpr (NB == 4) {
+                        *reinterpret_cast<f4*>(d) = f4{acc[a][0][r0 + i], acc[a][1][r0 + i],
+                                                       acc[a][2][r0 + i], acc[a][3][r0 + i]};
+                    } else if constexpr (NB == 2) {
+                        *reinterpret_cast<f2*>(d) = f2{acc[a][0][r0 + i], acc[a][1][r0 + i]};
+                    } else {
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) d[b] = acc[a][b][r0 + i];
+                    }
+                }
+                wave_lds_sync();
+                float sv[V];
+#pragma unroll
+                for (int j = 0; j < V; ++j) sv[j] = slice[elane + 64 * j];
+                wave_lds_sync();  // read before the next chunk rewrites the slice
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    float v = alpha * sv[j];
+                    if (with_c) v += beta * cin[j];
+                    st1_nt(rt, elem(q, j), v);
+                }
+            };
+            lds_barrier();  // every wave is done reading the operand ring
+            float s0[V] = {}, s1[V] = {};
+            if (beta0) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) store_cs(q, s0, false);
+            } else {
+                load_cs(0, s0);
+#pragma unroll
+                for (int q = 0; q < NQ; q += 2) {
+                    if (q + 1 < NQ) load_cs(q + 1, s1);
+                    store_cs(q, s0, true);
+                    if (q + 1 < NQ) {
+                        if (q + 2 < NQ) load_cs(q + 2, s0);
+                        store_cs(q + 1, s1, true);
+                    }
+                }
+            }
+            return;
+        }
         auto load_c = [&](int q, float (&cin)[CH][NB]) {
             const int a = q / (NREG / CH), r0 = (q % (NREG / CH)) * CH;
 #pragma unroll

@@ -193,6 +193,28 @@ def test_padded_and_misaligned(ta, tb):
         assert np.all(full[:, N:] == 12345.0), "C padding was written"
 
 
+@pytest.mark.parametrize("cfg", mfma_ids())
+@pytest.mark.parametrize("ta,tb", OPS)
+def test_unaligned_c_rows_every_config(cfg, ta, tb):
+    """Rows of C that are not 16-byte aligned (odd ldc, or the base 1-3 floats
+    off alignment): the matrix-core entries then stage each chunk of the
+    result through LDS so that a store covers consecutive elements of a row.
+    Ragged M and N; the padding of C is a guard band that must stay
+    untouched; with beta = 0 the old C (NaN) must not be read."""
+    for i, (M, N, K, pad, coff) in enumerate([(97, 131, 45, 2, 0), (300, 257, 100, 4, 1),
+                                              (129, 64, 33, 1, 3), (513, 190, 1025, 5, 2)]):
+        for beta in (0.0, 0.5):
+            w = wl.custom(M, N, K, ta, tb, alpha=1.5, beta=beta, dist="normal", seed=70 + i,
+                          ldc=N + pad)
+            A, B, C = wl.make_inputs(w)
+            if C is None:
+                C = np.full((M, w.LDC), np.nan, dtype=np.float32)
+            C[:, N:] = 2468.0
+            out, full = run_fg(w, A, B, C, config=cfg, offsets=(0, 0, coff))
+            check_full(w, A, B, C, out)
+            assert np.all(full[:, N:] == 2468.0), (cfg, ta, tb, M, N, K, beta)
+
+
 def test_guard_rows_outside_c():
     """Nothing is written past the last row of C (the buffer continues)."""
     import torch
