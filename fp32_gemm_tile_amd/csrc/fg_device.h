@@ -57,9 +57,6 @@ __device__ __forceinline__ void st4_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_o
 __device__ __forceinline__ void st1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
 }
-__device__ __forceinline__ void st1_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 2);
-}
 __device__ __forceinline__ f2 ld2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
 }
@@ -92,12 +89,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);
     asm volatile("s_barrier" ::: "memory");
 }
-
-// Orders one wave's LDS accesses across its own lanes (a value one lane wrote
-// and another lane of the same wave reads, or the reverse): all of the wave's
-// LDS operations have completed, and the "memory" clobber keeps the compiler
-// from moving any access across this point. No other wave takes part.
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // erf(x) for binary32, branch free: formula 7.1.26 of Abramowitz and Stegun,
 // "Handbook of Mathematical Functions" (after Hastings),

@@ -279,6 +279,17 @@ __device__ __forceinline__ void wait_vm_lds() {
     __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));
 }
 
+// Orders one wave's LDS accesses across its own lanes (a value one lane wrote
+// and another lane of the same wave reads, or the reverse): all of the wave's
+// LDS operations have completed, and the "memory" clobber keeps the compiler
+// from moving any access across this point. No other wave takes part.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Single-element store with the non-temporal hint, like the wide stores of C.
+__device__ __forceinline__ void st1_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 2);
+}
+
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
 // would make the compiler wait for every outstanding direct-to-LDS load,
 // including the ones meant to stay in flight across the barrier. The caller
