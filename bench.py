@@ -8,7 +8,8 @@ resident in device memory before timing starts.
 
 Prints ONE JSON line (rank 0) with the metric, the roofline of the dominant
 kernel (timed with HIP events on the stream the kernel is launched on) and
-the CPU oracle timed on a bounded sample of the same workload.
+the CPU oracle timed on the whole workload, with every element of the timed
+result checked against it.
 
 With the default workload it also times 4096^3 NN and the 1024 x 8192 x 8192
 row block one of eight GPUs would own, and measures the device's attainable
@@ -18,7 +19,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C5a]
                        [--suite] [--calibrate] [--splitk [S]] [--streamk] [--cold]
                        [--no-cpu] [--no-probes] [--no-extras] [--copy-probe]
                        [--config ID] [--group-m G] [--xcd-remap 0|1]
-                       [--epilogue ACT] [--quant bf16|int8_row]
+                       [--epilogue ACT] [--quant bf16|int8_row] [--launch-floor]
 """
 from __future__ import annotations
 
@@ -186,9 +187,20 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock
                 step()
             torch.cuda.synchronize()
             clock = finish_clock_watch(watcher)
-    cfg = fg.fg_select_config(w.transA, w.transB, w.M, w.N, w.K, dA.data_ptr(), w.LDA,
-                              dB.data_ptr(), w.LDB, dC.data_ptr(), w.LDC, quant=quant) \
-        if config < 0 else fg.fg_get_config(config)
+    # The entry (and split-K slices) the timed call ran: fg_sgemm_splitk
+    # takes no entry id and chooses with the split allowed; the stream-K line
+    # names the entry of its data-parallel rounds.
+    nsl = 1
+    if splitk:
+        cfg, nsl = fg.fg_select_config_ex(w.transA, w.transB, w.M, w.N, w.K, dA.data_ptr(),
+                                          w.LDA, dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(),
+                                          w.LDC, splits=nsplit, workspace_bytes=ws.numel() * 4)
+    elif config >= 0:
+        cfg = fg.fg_get_config(config)
+    else:
+        cfg = fg.fg_select_config_ex(w.transA, w.transB, w.M, w.N, w.K, dA.data_ptr(), w.LDA,
+                                     dB.data_ptr(), w.LDB, w.beta, dC.data_ptr(), w.LDC,
+                                     quant=quant)[0]
     output = None
     if keep_output and epilogue is None:
         # Outside every timed range: one more call on the original C (with
@@ -200,7 +212,41 @@ def time_gpu(w, steps, warmup, config=-1, splitk=False, cold=False, sample_clock
         torch.cuda.synchronize()
         output = dC.cpu().numpy()[:, :w.N]
     return {"ms_per_launch": mean, "ms_median": statistics.median(per), "ms_min": min(per),
-            "wall_s": wall, "config": cfg["name"], "clock_mhz": clock, "output": output}
+            "wall_s": wall, "config": cfg["name"], "splits": nsl, "clock_mhz": clock,
+            "output": output}
+
+
+def launch_floor(name, steps):
+    """Per-call time of the smallest kernel the library launches: fg_sgemm
+    with alpha = beta = 0 on the workload's C (C = 0, A and B unread), back to
+    back after a 0.2 s warm-up; the same event pair as time_gpu."""
+    import torch
+    import fp32_gemm_tile_amd as fg
+    from fp32_gemm_tile_amd import workloads as wl
+    w = wl.WORKLOADS[name]
+    dC = torch.empty((w.M, w.LDC), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st = fg.fg_sgemm(w.transA, w.transB, w.M, w.N, w.K, 0.0, 0, w.LDA, 0, w.LDB, 0.0,
+                         dC.data_ptr(), w.LDC, stream.cuda_stream)
+        if st != 0:
+            raise fg.FgError(st, fg.fg_last_bad_arg(), fg.fg_last_error())
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.2:
+        for _ in range(16):
+            step()
+        torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    return {"workload": name, "launch_floor_us": round(us, 3), "steps": steps,
+            "call": "fg_sgemm, alpha = beta = 0 (C = 0: one fill kernel)"}
 
 
 def measured_peaks():
@@ -384,7 +430,9 @@ def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False, cold=False,
                  quant=quant)
     tflops = w.flops / (g["ms_per_launch"] * 1e-3) / 1e12
     gbs = w.compulsory_bytes / (g["ms_per_launch"] * 1e-3) / 1e9
-    traffic = load_traffic(name, g["config"])
+    # The counter records are of plain calls (no split, no fused epilogue).
+    plain = not splitk and not streamk and epilogue is None and quant is None
+    traffic = load_traffic(name, g["config"]) if plain else None
     # Bound: the matrix core above the ridge point, HBM below it.
     hbm_bound = w.flops / w.compulsory_bytes < PEAK_FP32_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if hbm_bound:
@@ -410,7 +458,7 @@ def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False, cold=False,
         "config": {"workload": f"sgemm_{w.M}x{w.N}x{w.K}_{w.transA.lower()}{w.transB.lower()}",
                    "M": w.M, "N": w.N, "K": w.K, "transA": w.transA, "transB": w.transB,
                    "alpha": w.alpha, "beta": w.beta, "inputs": f"{w.dist} seed {w.seed}",
-                   "kernel_config": g["config"]},
+                   "kernel_config": g["config"], "splitk_slices": g["splits"]},
         "pct_of_fp32_peak": round(100 * tflops / PEAK_FP32_TFLOPS, 2),
         "ms_median": round(g["ms_median"], 4),
         "ms_min": round(g["ms_min"], 4),
@@ -475,6 +523,9 @@ def main():
     ap.add_argument("--xcd-remap", type=int, choices=(0, 1), default=1,
                     help="1: renumber workgroups so each XCD gets a contiguous run of tiles "
                          "(library default); 0: hardware round-robin order")
+    ap.add_argument("--launch-floor", action="store_true",
+                    help="time the library's smallest launch instead: C = 0 through fg_sgemm "
+                         "with alpha = beta = 0 on the workload's C (one fill kernel)")
     ap.add_argument("--splitk", type=int, nargs="?", const=-1, default=None,
                     help="time fg_sgemm_splitk (256 MiB workspace) instead of fg_sgemm; "
                          "optional value = split count (default: library-chosen)")
@@ -495,6 +546,10 @@ def main():
             fg.fg_set_few_row_threads(args.few_row_threads) != fg.FG_OK:
         print(f"bench.py: {fg.fg_last_error()}", file=sys.stderr)
         sys.exit(2)
+
+    if args.launch_floor:
+        print(json.dumps(launch_floor(args.workload, args.steps)), flush=True)
+        return
 
     if args.suite or args.calibrate:
         ids = range(fg.fg_num_configs()) if args.calibrate else [args.config]

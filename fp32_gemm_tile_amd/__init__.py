@@ -138,6 +138,10 @@ def load_library(path: str = LIB_PATH):
     lib.fg_select_config_quant.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64,
                                            i32, ctypes.POINTER(fg_config)]
     lib.fg_select_config_quant.restype = i32
+    lib.fg_select_config_ex.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, f32, vp, i64,
+                                        i32, ctypes.c_size_t, i32, ctypes.POINTER(fg_config),
+                                        ctypes.POINTER(i32)]
+    lib.fg_select_config_ex.restype = i32
     lib.fg_last_bad_arg.argtypes = []
     lib.fg_last_bad_arg.restype = i32
     lib.fg_last_error.argtypes = []
@@ -273,6 +277,25 @@ def fg_select_config(transA, transB, M, N, K, A=0, lda=None, B=0, ldb=None, C=0,
         _raise_if(lib.fg_select_config_quant(ta, tb, M, N, K, A or None, lda, B or None, ldb,
                                              C or None, ldc, kind, ctypes.byref(c)))
     return c.as_dict()
+
+
+def fg_select_config_ex(transA, transB, M, N, K, A=0, lda=None, B=0, ldb=None, beta=0.0, C=0,
+                        ldc=None, splits=1, workspace_bytes=0, quant=None):
+    """(entry, split-K slices) a call runs with config_id -1: fg_sgemm
+    (splits=1), fg_sgemm_splitk (splits 0 = library choice bounded by
+    workspace_bytes, or a count) or fg_sgemm_quant (quant, a format name or
+    FG_QUANT_* code), with beta taken into account."""
+    ta, tb = _op(transA), _op(transB)
+    lda = lda if lda is not None else max(1, K if ta == FG_OP_N else M)
+    ldb = ldb if ldb is not None else max(1, N if tb == FG_OP_N else K)
+    ldc = ldc if ldc is not None else max(1, N)
+    kind = 0 if quant is None else (quant if isinstance(quant, int) else _QUANTS[quant])
+    c = fg_config()
+    n = ctypes.c_int32(0)
+    _raise_if(load_library().fg_select_config_ex(ta, tb, M, N, K, A or None, lda, B or None, ldb,
+                                                 beta, C or None, ldc, splits, workspace_bytes,
+                                                 kind, ctypes.byref(c), ctypes.byref(n)))
+    return c.as_dict(), n.value
 
 
 def fg_last_bad_arg() -> int:

@@ -590,6 +590,68 @@ fg_status fg_select_config_quant(fg_op transA, fg_op transB, int64_t M, int64_t 
 
 namespace {
 
+// The table entry and split-K slice count of a call (the part of run_gemm
+// that fg_select_config_ex reports, so the query and the call cannot
+// disagree). splits: 1 = no split-K, 0 = choose (bounded by the workspace),
+// > 1 = requested; have_ws: a workspace of ws_bytes is given. config_id >= 0
+// forces an entry (argument config_arg); ws_arg numbers the workspace size
+// in the caller's argument list.
+struct Choice {
+    int idx = -1;
+    int64_t nsplit = 1;  // slices after effective_splits
+    int64_t kps = 0;     // k-tiles per slice
+};
+
+fg_status choose_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, float beta,
+                       int64_t splits, bool have_ws, size_t ws_bytes, bool quant_on,
+                       int32_t config_id, int config_arg, int ws_arg, Choice* out) {
+    const int64_t slice = M * N;  // floats per split-K partial
+    // One slice needs no workspace, so at least one is always possible.
+    int64_t max_splits =
+        have_ws && slice > 0 ? (int64_t)(ws_bytes / (sizeof(float) * (size_t)slice)) : 1;
+    if (max_splits < 1) max_splits = 1;
+    int64_t want = splits;
+    int idx;
+    if (config_id >= 0) {
+        idx = config_id;
+        if (want == 0) want = 1;
+        if (quant_on && !table()[idx].quant)
+            return fail(FG_ERR_INVALID_ARG, config_arg,
+                        "entry %s has no quantised output (another entry, or -1)",
+                        table()[idx].cfg.name);
+    } else {
+        int64_t auto_splits = 1;
+        idx = select_entry(M, N, K, ab_aligned, want == 0 ? max_splits : want, beta == 0.0f,
+                           &auto_splits, want > 1, quant_on);
+        if (want == 0) want = auto_splits;
+    }
+    if (idx < 0 || idx >= num_entries())
+        return fail(FG_ERR_UNSUPPORTED, 0, "no table entry fits this call");
+    if (table()[idx].fallback >= 0 && !ab_aligned) idx = table()[idx].fallback;
+    const Entry& en = table()[idx];
+    if (quant_on && !en.quant)
+        return fail(FG_ERR_INVALID_ARG, config_arg, "entry %s has no quantised output",
+                    en.cfg.name);
+    if (en.cfg.kind != FG_KIND_MFMA) want = 1;  // split-K runs on the MFMA kernels
+    // The few-row kernels put their blocks of rows (8 on the vector ALU, at
+    // least 16 on the matrix cores) on the grid's y dimension (at most 65535).
+    if (en.cfg.kind == FG_KIND_SKINNY && cdiv(M, 8) > 65535)
+        return fail(FG_ERR_UNSUPPORTED, 0, "the few-row entry takes at most %d rows", 65535 * 8);
+
+    int64_t kps = 0;
+    // k-tile depth of the MFMA kernels; the other kinds ignore the split.
+    const int64_t split_bk = en.cfg.kind == FG_KIND_MFMA ? en.cfg.bk : 16;
+    const int64_t nsplit = effective_splits(K, split_bk, want, &kps);
+    if (nsplit > 1 && nsplit > max_splits)
+        return fail(FG_ERR_INVALID_ARG, ws_arg,
+                    "workspace of %zu bytes holds %lld splits, need %lld", ws_bytes,
+                    (long long)max_splits, (long long)nsplit);
+    out->idx = idx;
+    out->nsplit = nsplit;
+    out->kps = kps;
+    return FG_OK;
+}
+
 // Shared body of fg_sgemm_ex and fg_sgemm_splitk. splits: 1 = no split-K,
 // 0 = choose (bounded by the workspace), > 1 = requested.
 fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, float alpha,
@@ -703,45 +765,13 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
         if (e != hipSuccess) return fail(FG_ERR_HIP, 0, "kernel launch: %s", hipGetErrorString(e));
         return FG_OK;
     }
+    Choice ch;
+    s = choose_entry(M, N, K, ab_aligned, beta, splits, ws != nullptr, ws_bytes, quant_on,
+                     config_id, config_arg, 16, &ch);
+    if (s != FG_OK) return s;
+    const Entry& en = table()[ch.idx];
     const int64_t slice = M * N;  // floats per split-K partial
-    // One slice needs no workspace, so at least one is always possible.
-    int64_t max_splits = ws ? (int64_t)(ws_bytes / (sizeof(float) * (size_t)slice)) : 1;
-    if (max_splits < 1) max_splits = 1;
-    int64_t want = splits;
-    int idx;
-    if (config_id >= 0) {
-        idx = config_id;
-        if (want == 0) want = 1;
-        if (quant_on && !table()[idx].quant)
-            return fail(FG_ERR_INVALID_ARG, config_arg,
-                        "entry %s has no quantised output (another entry, or -1)",
-                        table()[idx].cfg.name);
-    } else {
-        int64_t auto_splits = 1;
-        idx = select_entry(M, N, K, ab_aligned, want == 0 ? max_splits : want, beta == 0.0f,
-                           &auto_splits, want > 1, quant_on);
-        if (want == 0) want = auto_splits;
-    }
-    if (idx < 0 || idx >= num_entries())
-        return fail(FG_ERR_UNSUPPORTED, 0, "no table entry fits this call");
-    if (table()[idx].fallback >= 0 && !ab_aligned) idx = table()[idx].fallback;
-    const Entry& en = table()[idx];
-    if (quant_on && !en.quant)
-        return fail(FG_ERR_INVALID_ARG, config_arg, "entry %s has no quantised output",
-                    en.cfg.name);
-    if (en.cfg.kind != FG_KIND_MFMA) want = 1;  // split-K runs on the MFMA kernels
-    // The few-row kernels put their blocks of rows (8 on the vector ALU, at
-    // least 16 on the matrix cores) on the grid's y dimension (at most 65535).
-    if (en.cfg.kind == FG_KIND_SKINNY && cdiv(M, 8) > 65535)
-        return fail(FG_ERR_UNSUPPORTED, 0, "the few-row entry takes at most %d rows", 65535 * 8);
-
-    int64_t kps = 0;
-    // k-tile depth of the MFMA kernels; the other kinds ignore the split.
-    const int64_t split_bk = en.cfg.kind == FG_KIND_MFMA ? en.cfg.bk : 16;
-    const int64_t nsplit = effective_splits(K, split_bk, want, &kps);
-    if (nsplit > 1 && nsplit > max_splits)
-        return fail(FG_ERR_INVALID_ARG, 16, "workspace of %zu bytes holds %lld splits, need %lld",
-                    ws_bytes, (long long)max_splits, (long long)nsplit);
+    const int64_t nsplit = ch.nsplit, kps = ch.kps;
 
     s = check_device();
     if (s != FG_OK) return s;
@@ -807,6 +837,30 @@ fg_status fg_sgemm_splitk(fg_op transA, fg_op transB, int64_t M, int64_t N, int6
         return fail(FG_ERR_INVALID_ARG, 15, "workspace is not 4-byte aligned");
     return run_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1,
                     splits, (float*)workspace, workspace ? workspace_bytes : 0);
+}
+
+fg_status fg_select_config_ex(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                              const float* A, int64_t lda, const float* B, int64_t ldb,
+                              float beta, const float* C, int64_t ldc, int32_t splits,
+                              size_t workspace_bytes, int32_t quant_kind, fg_config* out,
+                              int32_t* splits_out) {
+    clear_error();
+    fg_status s = validate(transA, transB, M, N, K, 1.0f, A, lda, B, ldb, C, ldc, false);
+    if (s != FG_OK) return s;
+    if (splits < 0) return fail(FG_ERR_INVALID_ARG, 13, "splits < 0");
+    if (quant_kind != FG_QUANT_NONE && quant_kind != FG_QUANT_BF16 &&
+        quant_kind != FG_QUANT_INT8_ROW)
+        return fail(FG_ERR_INVALID_ARG, 15, "unknown quantised format %d", quant_kind);
+    if (!out) return fail(FG_ERR_INVALID_ARG, 16, "out is NULL");
+    const int32_t f = build_flags(A, lda, B, ldb, C, ldc, beta);
+    const bool ab_aligned = (f & fg::FLAG_VEC_A) && (f & fg::FLAG_VEC_B);
+    Choice ch;
+    s = choose_entry(M, N, K, ab_aligned, beta, splits, workspace_bytes > 0, workspace_bytes,
+                     quant_kind != FG_QUANT_NONE, -1, 0, 14, &ch);
+    if (s != FG_OK) return s;
+    *out = table()[ch.idx].cfg;
+    if (splits_out) *splits_out = (int32_t)ch.nsplit;
+    return FG_OK;
 }
 
 fg_status fg_sgemm_splitk_noalloc(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,

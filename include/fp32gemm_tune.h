@@ -91,6 +91,27 @@ fg_status fg_select_config_quant(fg_op transA, fg_op transB, int64_t M, int64_t 
                                  fg_config* out);
 
 /*
+ * The table entry and split-K slice count a call with config_id -1 runs,
+ * from everything that decides them (fg_select_config takes beta = 0 and no
+ * split): beta (argument 10; with beta != 0 the cost of reading C enters the
+ * choice), splits (13) as fg_sgemm_splitk takes it (1: fg_sgemm, no split;
+ * 0: the library's count, bounded by the workspace; > 1: that count, also
+ * bounded by K as the call bounds it), workspace_bytes (14; 0 = no
+ * workspace) and quant_kind (15, fg_quant_kind: the entry fg_sgemm_quant
+ * runs). *out (16) receives the entry, *splits_out (17, may be NULL) the
+ * slices the call runs (1 = none). The same validation and the same errors
+ * as the call: FG_ERR_INVALID_ARG (bad argument 14) when the workspace holds
+ * fewer slices than a requested count needs. Stream-K calls plan their own
+ * split (fg_sgemm_streamk_workspace_size). Pointers are only inspected.
+ * Host only.
+ */
+fg_status fg_select_config_ex(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K,
+                              const float* A, int64_t lda, const float* B, int64_t ldb,
+                              float beta, const float* C, int64_t ldc, int32_t splits,
+                              size_t workspace_bytes, int32_t quant_kind, fg_config* out,
+                              int32_t* splits_out);
+
+/*
  * Constants shared by the cost models of the table entries (fitted together
  * with the entries' efficiencies by the tuner and compiled in; settable for
  * a refit). FG_ERR_INVALID_ARG for an unknown constant (argument 1) or a

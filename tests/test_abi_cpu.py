@@ -514,6 +514,45 @@ def test_select_config_quant_skips_entries_without_it():
         fg.fg_select_config("N", "N", 8, 8, 8, quant=7)
 
 
+def test_select_config_ex_reports_what_the_call_runs():
+    """fg_select_config_ex: with beta = 0, no split and no quantised output it
+    is fg_select_config; a requested split runs on a matrix-core entry with
+    that many slices (bounded by K); the library's own split stays inside the
+    workspace; a workspace too small for a requested count is the call's own
+    error (bad argument 14)."""
+    shapes = [(8192, 8192, 8192), (4096, 4096, 4096), (3001, 2047, 1025), (1, 8192, 8192),
+              (256, 256, 256), (2048, 2048, 2048), (16384, 16384, 256), (8, 8192, 8192)]
+    for shape in shapes:
+        for ta, tb in (("N", "N"), ("T", "N"), ("N", "T")):
+            plain = fg.fg_select_config(ta, tb, *shape)
+            assert fg.fg_select_config_ex(ta, tb, *shape) == (plain, 1)
+            for kind in ("bf16", "int8_row"):
+                q = fg.fg_select_config(ta, tb, *shape, quant=kind)
+                assert fg.fg_select_config_ex(ta, tb, *shape, quant=kind) == (q, 1)
+    ws = 1 << 28
+    cfg, n = fg.fg_select_config_ex("N", "N", 256, 256, 256, splits=2, workspace_bytes=ws)
+    assert cfg["kind"] == fg.FG_KIND_MFMA and n == 2
+    # at most one slice per k-tile: K = 64 takes at most 64 / bk slices
+    cfg, n = fg.fg_select_config_ex("N", "N", 256, 256, 64, splits=16, workspace_bytes=ws)
+    assert n == 64 // cfg["bk"]
+    cfg, n = fg.fg_select_config_ex("N", "N", 512, 512, 65536, splits=0, workspace_bytes=ws)
+    assert n > 1 and n * 512 * 512 * 4 <= ws
+    assert fg.fg_select_config_ex("N", "N", 512, 512, 65536, splits=0)[1] == 1  # no workspace
+    with pytest.raises(fg.FgError) as e:
+        fg.fg_select_config_ex("N", "N", 512, 512, 65536, splits=8, workspace_bytes=4 << 20)
+    assert e.value.status == fg.FG_ERR_INVALID_ARG and e.value.bad_arg == 14
+    lib = fg.load_library()
+    c = fg.fg_config()
+    n = ctypes.c_int32(0)
+    call = lambda splits=1, kind=0, out=ctypes.byref(c): lib.fg_select_config_ex(
+        0, 0, 64, 64, 64, None, 64, None, 64, 0.0, None, 64, splits, 0, kind, out,
+        ctypes.byref(n))
+    assert call() == fg.FG_OK
+    assert call(splits=-1) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 13
+    assert call(kind=9) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 15
+    assert call(out=None) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 16
+
+
 def test_quant_validation_needs_no_gpu():
     """fg_sgemm_quant checks its quantised-output description (argument 15)
     before any device work; an empty result needs nothing."""
