@@ -598,11 +598,13 @@ sgemm_mfma_kernel(GemmParams p) {
             // one access, and NB single stores per row would each scatter over
             // the row with a stride of NB elements. Instead each chunk passes
             // through a slice of the idle operand ring that belongs to this
-            // wave: the lanes write their accumulators there, then read it
-            // back so that lane l holds element l + 64 j of the chunk (local
-            // row e / WN, column e % WN), and one single-element store (or old
-            // C read) covers 64 consecutive elements of a row of C (WN = 32:
-            // two rows of 32).
+            // wave (the results staged in shared memory before they are
+            // stored, as in "Optimising fp32 GEMM on A100", Kernel 6, there
+            // for wider stores): the lanes write their accumulators there,
+            // then read it back so that lane l holds element l + 64 j of the
+            // chunk (local row e / WN, column e % WN), and one single-element
+            // store (or old C read) covers 64 consecutive elements of a row of
+            // C (WN = 32: two rows of 32).
             constexpr int HR = 64 / MR;  // lane groups = rows per register
             constexpr int V = CH * NB;   // elements per lane per chunk
             static_assert(NW * 64 * V <= NS * (OpA::kStage + OpB::kStage), "slices fit in LDS");
