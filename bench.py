@@ -20,6 +20,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C5a]
                        [--no-cpu] [--no-probes] [--no-extras] [--copy-probe]
                        [--config ID] [--group-m G] [--xcd-remap 0|1]
                        [--epilogue ACT] [--quant bf16|int8_row] [--launch-floor]
+                       [--ops NN|NT|TN|TT]
 """
 from __future__ import annotations
 
@@ -432,7 +433,7 @@ def run_one(name, steps, warmup, with_cpu, config=-1, splitk=False, cold=False,
     gbs = w.compulsory_bytes / (g["ms_per_launch"] * 1e-3) / 1e9
     # The counter records are of plain calls (no split, no fused epilogue).
     plain = not splitk and not streamk and epilogue is None and quant is None
-    traffic = load_traffic(name, g["config"]) if plain else None
+    traffic = load_traffic(name, g["config"]) if plain and isinstance(name, str) else None
     # Bound: the matrix core above the ridge point, HBM below it.
     hbm_bound = w.flops / w.compulsory_bytes < PEAK_FP32_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if hbm_bound:
@@ -523,6 +524,9 @@ def main():
     ap.add_argument("--xcd-remap", type=int, choices=(0, 1), default=1,
                     help="1: renumber workgroups so each XCD gets a contiguous run of tiles "
                          "(library default); 0: hardware round-robin order")
+    ap.add_argument("--ops", choices=("NN", "NT", "TN", "TT"), default=None,
+                    help="operand layouts instead of the workload's (square workloads with "
+                         "dense leading dimensions only: the same buffers read in that layout)")
     ap.add_argument("--launch-floor", action="store_true",
                     help="time the library's smallest launch instead: C = 0 through fg_sgemm "
                          "with alpha = beta = 0 on the workload's C (one fill kernel)")
@@ -582,7 +586,18 @@ def main():
     # short kernel's first few calls run before the clock has ramped up
     # (2048^3 reads about 12% slower after only the warm-up calls).
     with_cpu = not args.no_cpu
-    r = run_one(args.workload, args.steps, args.warmup, False, args.config, _splitk_arg(args),
+    target = args.workload
+    if args.ops:
+        import dataclasses
+        from fp32_gemm_tile_amd import workloads as wl
+        w0 = wl.WORKLOADS[args.workload]
+        if not (w0.M == w0.N == w0.K and w0.lda is None and w0.ldb is None and w0.ldc is None):
+            print("bench.py: --ops takes a square workload with dense leading dimensions",
+                  file=sys.stderr)
+            sys.exit(2)
+        target = dataclasses.replace(w0, name=f"{w0.name}_{args.ops}", transA=args.ops[0],
+                                     transB=args.ops[1])
+    r = run_one(target, args.steps, args.warmup, False, args.config, _splitk_arg(args),
                 args.cold, sample_clock=not args.no_probes, epilogue=args.epilogue,
                 streamk=args.streamk, min_warm_s=0.2, keep_output=with_cpu, quant=args.quant)
     # The 4096^3 shape of the metric, and one GPU's row block of 8192^3 split
@@ -602,7 +617,8 @@ def main():
         r["measured_peaks"] = mp
     if with_cpu:
         from fp32_gemm_tile_amd import workloads as wl
-        r["cpu_baseline"] = cpu_baseline(wl.WORKLOADS[args.workload], r.pop("_output", None))
+        r["cpu_baseline"] = cpu_baseline(target if args.ops else wl.WORKLOADS[args.workload],
+                                         r.pop("_output", None))
         # every element of the timed calls' result against the oracle
         r["parity"] = r["cpu_baseline"].get("parity")
     if args.copy_probe:

@@ -25,7 +25,8 @@ FETCH_SIZE / WRITE_SIZE to bytes. Derived figures:
 
 Usage (on the GPU machine, from the repository root):
     python -m fp32_gemm_tile_amd.counters --workload C3 --out gpurun_out/counters_C3 \
-        [--config ID] [--group-m G] [--xcd-remap 0|1] [--passes trace fetch ...]
+        [--config ID] [--group-m G] [--xcd-remap 0|1] [--ops NN|NT|TN|TT]
+        [--passes trace fetch ...]
     python -m fp32_gemm_tile_amd.counters --summarize gpurun_out/counters_C3
     python -m fp32_gemm_tile_amd.counters --out gpurun_out/bench_trace --bench-trace [ARGS]
 (the last: bench.py with ARGS -- none for its default run -- under the
@@ -71,6 +72,8 @@ def bench_args(a):
     for flag in ("splitk", "streamk"):
         if getattr(a, flag):
             out.append(f"--{flag}")
+    if a.ops:
+        out += ["--ops", a.ops]
     return out
 
 
@@ -344,6 +347,8 @@ def main(argv=None):
     ap.add_argument("--xcd-remap", type=int, choices=(0, 1), default=1)
     ap.add_argument("--splitk", action="store_true")
     ap.add_argument("--streamk", action="store_true")
+    ap.add_argument("--ops", choices=("NN", "NT", "TN", "TT"), default=None,
+                    help="operand layouts instead of the workload's (bench.py --ops)")
     ap.add_argument("--passes", nargs="+", default=list(PASSES), choices=list(PASSES))
     ap.add_argument("--timeout", type=int, default=150, help="seconds per pass (SIGKILL)")
     ap.add_argument("--summarize", default=None, help="only summarise an existing directory")
@@ -359,9 +364,12 @@ def main(argv=None):
         res, md = summarize(a.summarize)
         print(md)
         return 0
-    out = os.path.abspath(a.out or os.path.join(ROOT, "gpurun_out", f"counters_{a.workload}"))
+    # with --ops the records are named for the workload and the layouts
+    # (bench.py reads traffic records of the workloads as defined only)
+    name = a.workload + (f"_{a.ops}" if a.ops else "")
+    out = os.path.abspath(a.out or os.path.join(ROOT, "gpurun_out", f"counters_{name}"))
     os.makedirs(out, exist_ok=True)
-    meta = {"workload": a.workload, "commands": {}}
+    meta = {"workload": name, "commands": {}}
     for p in a.passes:
         meta["commands"][p] = run_pass(p, a, out)
         with open(os.path.join(out, "meta.json"), "w") as f:

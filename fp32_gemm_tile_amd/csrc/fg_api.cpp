@@ -385,9 +385,16 @@ int select_entry(int64_t M, int64_t N, int64_t K, bool ab_aligned, int64_t max_s
 
 // Raster order of the matrix-core kernels (fg_set_raster in fp32gemm_tune.h;
 // for measurements): band height in tile rows, and whether workgroup ids are
-// renumbered so each XCD gets a contiguous run of tiles.
-constexpr int kDefaultGroupM = 4;
-std::atomic<int> g_group_m{kDefaultGroupM};
+// renumbered so each XCD gets a contiguous run of tiles. The default band
+// depends on how B is stored; HBM reads per 8192^3 launch, bands of 4 / 8
+// tile rows: NN 3.22 / 3.66 GB, TN 3.22 / 3.22, TT 3.49 / 3.22, NT 11.5 / 6.6,
+// at equal speed.
+constexpr int kGroupMKxN = 4, kGroupMNxK = 8;
+std::atomic<int> g_group_m{0};  // 0: the default of the layout
+int group_m_for(fg_op transB) {
+    const int g = g_group_m.load(std::memory_order_relaxed);
+    return g ? g : (transB == FG_OP_T ? kGroupMNxK : kGroupMKxN);
+}
 // Workgroup size of the few-row kernel's K x N form (fg_set_few_row_threads;
 // 0 = automatic).
 std::atomic<int> g_few_row_threads{0};
@@ -735,7 +742,7 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
         if (s != FG_OK) return s;
         p.tiles_m = (int32_t)cdiv(M, en.cfg.bm);
         p.tiles_n = (int32_t)cdiv(N, en.cfg.bn);
-        p.group_m = std::min(g_group_m.load(std::memory_order_relaxed), p.tiles_m);
+        p.group_m = std::min(group_m_for(transB), p.tiles_m);
         hipError_t e = hipSuccess;
         if (plan.full > 0) {
             fg::GemmParams d = p;
@@ -780,7 +787,7 @@ fg_status run_gemm(fg_op transA, fg_op transB, int64_t M, int64_t N, int64_t K, 
     p.tiles_n = (int32_t)cdiv(N, en.cfg.bn);
     const int64_t nblocks = (int64_t)p.tiles_m * p.tiles_n;
     if (nblocks > 0x7FFFFFFF) return fail(FG_ERR_UNSUPPORTED, 0, "too many tiles");
-    p.group_m = std::min(g_group_m.load(std::memory_order_relaxed), p.tiles_m);
+    p.group_m = std::min(group_m_for(transB), p.tiles_m);
     p.kt_per_split = (int32_t)kps;
     p.c_split_stride = 0;
 
@@ -1004,7 +1011,7 @@ fg_status fg_set_raster(int32_t group_m, int32_t xcd_remap) {
         return fail(FG_ERR_INVALID_ARG, 1, "group_m %d outside 0..4096", group_m);
     if (xcd_remap != 0 && xcd_remap != 1)
         return fail(FG_ERR_INVALID_ARG, 2, "xcd_remap must be 0 or 1");
-    g_group_m.store(group_m == 0 ? kDefaultGroupM : group_m);
+    g_group_m.store(group_m);
     g_xcd_remap.store(xcd_remap);
     return FG_OK;
 }

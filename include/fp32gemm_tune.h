@@ -53,8 +53,9 @@ fg_status fg_set_efficiency(int32_t config_id, double eff, double eff1);
  * process (for measurements, e.g. of how much each part of the order saves;
  * the defaults are what the library is tuned with):
  *   1 group_m   : output tiles are visited in bands of group_m tile rows,
- *                 column by column inside a band (0 = the default, 4;
- *                 1 = plain row-major order); at most 4096
+ *                 column by column inside a band (0 = the default: 4 when B
+ *                 is stored K x N, 8 when it is stored N x K; 1 = plain
+ *                 row-major order); at most 4096
  *   2 xcd_remap : 1 (default) renumbers workgroups so that each of the 8
  *                 XCDs receives a contiguous run of tiles (when the grid is a
  *                 multiple of 8); 0 keeps the hardware's round-robin order
@@ -132,7 +133,8 @@ typedef enum fg_model_constant {
 fg_status fg_get_model_constant(int32_t which, double* value);
 fg_status fg_set_model_constant(int32_t which, double value);
 
-/* The current raster settings (arguments 1, 2: outputs, non-NULL). */
+/* The current raster settings (arguments 1, 2: outputs, non-NULL); group_m 0
+ * means the default of each layout. */
 fg_status fg_get_raster(int32_t* group_m, int32_t* xcd_remap);
 
 /*

@@ -582,13 +582,14 @@ assert st in NO_DEVICE, st
 def test_raster_setting_validation():
     """fg_set_raster changes the tile order only through an explicit call;
     nothing in the environment does."""
-    assert fg.fg_get_raster() == (4, 1)
+    assert fg.fg_get_raster() == (0, 1)  # band height by layout, XCD renumbering on
     try:
         assert fg.fg_set_raster(-1, 1) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 1
         assert fg.fg_set_raster(4097, 1) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 1
         assert fg.fg_set_raster(4, 2) == fg.FG_ERR_INVALID_ARG and fg.fg_last_bad_arg() == 2
         assert fg.fg_set_raster(1, 0) == fg.FG_OK and fg.fg_get_raster() == (1, 0)
-        assert fg.fg_set_raster(0, 1) == fg.FG_OK and fg.fg_get_raster() == (4, 1)
+        assert fg.fg_set_raster(4, 1) == fg.FG_OK and fg.fg_get_raster() == (4, 1)
+        assert fg.fg_set_raster(0, 1) == fg.FG_OK and fg.fg_get_raster() == (0, 1)
     finally:
         fg.fg_set_raster(0, 1)
     src = open(os.path.join(ROOT, "fp32_gemm_tile_amd", "csrc", "fg_api.cpp")).read()

@@ -215,6 +215,31 @@ def test_unaligned_c_rows_every_config(cfg, ta, tb):
             assert np.all(full[:, N:] == 2468.0), (cfg, ta, tb, M, N, K, beta)
 
 
+@pytest.mark.parametrize("ta,tb", OPS)
+def test_raster_bands_give_identical_results(ta, tb):
+    """The tile order (band height, XCD renumbering) never changes a result:
+    every tile is computed once with the same sums. 256 x 256 tiles on an
+    11 x 7 grid (partial last bands for every band height tried) and on a
+    grid that is a multiple of 8 (where the renumbering applies); C starts as
+    NaN, so a tile left out shows."""
+    import torch
+    for (M, N, K) in [(2700, 1700, 96), (2048, 1024, 64)]:
+        w = wl.custom(M, N, K, ta, tb, dist="int8", seed=M + K)
+        A, B, C = wl.make_inputs(w)
+        outs = {}
+        try:
+            for g, x in [(1, 0), (0, 1), (0, 0), (3, 1), (8, 1), (16, 0)]:
+                assert fg.fg_set_raster(g, x) == fg.FG_OK
+                outs[(g, x)], _ = run_fg(w, A, B, config=config_id(HEADLINE))
+        finally:
+            fg.fg_set_raster(0, 1)
+        ref = outs[(1, 0)]
+        cref, _ = oracle.gemm(ta, tb, M, N, K, 1.0, A, w.LDA, B, w.LDB, 0.0, None, w.LDC)
+        assert np.array_equal(ref.astype(np.float64), cref), (ta, tb, M, N, K)
+        for key, out in outs.items():
+            assert np.array_equal(out, ref), (ta, tb, M, N, K, key)
+
+
 def test_guard_rows_outside_c():
     """Nothing is written past the last row of C (the buffer continues)."""
     import torch
