@@ -344,11 +344,13 @@ int32_t fg_num_configs(void);
 fg_status fg_get_config(int32_t id, fg_config* out);
 
 /*
- * The configuration fg_sgemm would use for this call (shape, layouts and the
- * 16-byte alignment of the pointers and leading dimensions), without
- * launching anything. Pointers are only inspected, never dereferenced; they
- * may be NULL (then treated as 16-byte aligned). Same validation as fg_sgemm.
- * Host only.
+ * The configuration fg_sgemm would use for this call with beta == 0 (shape,
+ * layouts and the 16-byte alignment of the pointers and leading dimensions),
+ * without launching anything; with beta != 0 the cost of reading C can change
+ * the choice (fg_select_config_ex in fp32gemm_tune.h takes beta, a split-K
+ * request and a quantised output). Pointers are only inspected, never
+ * dereferenced; they may be NULL (then treated as 16-byte aligned). Same
+ * validation as fg_sgemm. Host only.
  */
 fg_status fg_select_config(fg_op transA, fg_op transB, int64_t M, int64_t N,
                            int64_t K, const float* A, int64_t lda,
