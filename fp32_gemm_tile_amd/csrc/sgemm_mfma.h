@@ -122,7 +122,7 @@ struct Operand {
     // bits above that (bits 2-3 for BK = 16, 1-3 for 32, bit 3 for 8).
     __device__ static int swz(int pr) { return ((pr * BK) >> 6) & (kCH - 1); }
 
-    __device__ void init(int tid, int ld) {
+    __device__ __forceinline__ void init(int tid, int ld) {
 #pragma unroll
         for (int q = 0; q < kVPT; ++q) {
             const int v = tid + NT * q;
@@ -146,7 +146,7 @@ struct Operand {
 
     // rows_left: valid tile rows (k rows for MN, m/n rows otherwise);
     // len: valid elements along the contiguous direction.
-    __device__ void load(__amdgpu_buffer_rsrc_t r, bool fast, bool vec, int rows_left,
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, bool fast, bool vec, int rows_left,
                          int len) {
         if (fast) {
 #pragma unroll
@@ -161,7 +161,7 @@ struct Operand {
         }
     }
 
-    __device__ void store_lds(float* buf) const {
+    __device__ __forceinline__ void store_lds(float* buf) const {
 #pragma unroll
         for (int q = 0; q < kVPT; ++q)
             if (act[q]) *reinterpret_cast<f4*>(buf + lds[q]) = reg[q];
@@ -169,7 +169,7 @@ struct Operand {
 
     // Operands of this lane for all KPL k-steps and XB blocks:
     // frag[s][x] = op(X) at k = KPL h + s, block x, lane position i.
-    __device__ static void read_frags(const float* buf, int wbase, int i, int h,
+    __device__ __forceinline__ static void read_frags(const float* buf, int wbase, int i, int h,
                                       float (&frag)[kKPL][XB]) {
         if constexpr (MN) {
 #pragma unroll
@@ -235,7 +235,7 @@ struct DmaOperand {
 
     uint32_t voff[kPerWave];
 
-    __device__ void init(int wave, int lane, int ld) {
+    __device__ __forceinline__ void init(int wave, int lane, int ld) {
 #pragma unroll
         for (int q = 0; q < kPerWave; ++q) {
             const int j = wave + NW * q;
@@ -252,7 +252,7 @@ struct DmaOperand {
         }
     }
 
-    __device__ void issue(__amdgpu_buffer_rsrc_t r, float* stage, int wave) const {
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, float* stage, int wave) const {
         // Device pass only: in clang's host pass the LDS address-space cast
         // makes it drop the launch stubs of later template instances.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -356,6 +356,10 @@ sgemm_mfma_kernel(GemmParams p) {
     // The same limit for the epilogue that stages C through LDS when C's rows
     // are unaligned (with 256 accumulators its registers spilled).
     constexpr bool kStageC = NB >= 2 && MB * NB * NREG <= 128;
+    // The fused and quantised epilogue's staged copy (twelve specialisations,
+    // each fully inlined) only where the accumulators are at most 64 per
+    // lane: with 128 one instance took over half an hour to compile.
+    constexpr bool kStageFused = kStageC && MB * NB * NREG <= 64;
 
     __shared__ f4 smem[NS * (OpA::kStage + OpB::kStage) / 4];
     float* sA = reinterpret_cast<float*>(smem);
@@ -577,6 +581,81 @@ sgemm_mfma_kernel(GemmParams p) {
     const int col0 = wave_n * WN + NB * eli;  // first of this lane's NB columns
     const int cols_left = p.N - n0 - col0;
     const bool full_vec = vec_c && cols_left >= NB;
+    // The epilogue works in chunks of CH accumulator registers of one block
+    // row (8 values per lane).
+    constexpr int CH = NB >= 8 ? 1 : (8 / NB < NREG ? 8 / NB : NREG);
+    constexpr int NQ = MB * (NREG / CH);  // chunks
+    static_assert(NREG % CH == 0, "whole chunks");
+    // Rows of C not aligned for a lane's NB adjacent columns to be one access
+    // (odd ldc or a misaligned base): NB single stores per row would each
+    // scatter over the row with a stride of NB elements. Instead each chunk
+    // passes through a slice of the idle operand ring that belongs to the
+    // wave (the results staged in shared memory before they are stored, as
+    // in "Optimising fp32 GEMM on A100", Kernel 6, there for wider stores):
+    // the lanes write their accumulators there, then read it back so that
+    // lane l holds element l + 64 j of the chunk (local row e / WN, column
+    // e % WN), and one single-element store (or old C read) covers 64
+    // consecutive elements of a row of C (WN = 32: two rows of 32). Compiled
+    // where the accumulators leave room for it (kStageC).
+    constexpr int HR = 64 / MR;  // lane groups = rows per register
+    constexpr int V = CH * NB;   // elements per lane per chunk
+    const bool stage_c = kStageC && !vec_c;
+    const int nrow = p.M - m0, ncol = p.N - n0 - wave_n * WN;
+    // Elements past M or N get a byte offset past the end of a resource that
+    // spans at most 2^31 bytes from the tile origin (every element of a tile
+    // lies below that: at most 255 rows of at most 2^21 elements), so that
+    // their loads read 0 and their stores are dropped with no branch: a
+    // branch around each access made the compiler wait for every earlier
+    // store before each use of the old C.
+    constexpr uint32_t kOut = 0xFFFFFFF0u;
+    constexpr int64_t kSpan = int64_t(1) << 29;  // elements (2^31 bytes)
+    const int64_t c_ext = tile_ws ? (int64_t)BM * BN : p.c_extent - c_org;
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(Cs + c_org, c_ext < kSpan ? c_ext : kSpan);
+    // Tile row and wave column of element j of chunk q: with WN >= 64 the row
+    // is the same for the whole wave (a scalar) and the column is the lane's
+    // plus a constant; with WN = 32 the two halves of the wave take two
+    // consecutive local rows.
+    const int lsub = WN >= 64 ? 0 : elane / WN, lcol = WN >= 64 ? elane : elane % WN;
+    auto elem_rc = [&](int q, int j, int& row, int& col) __attribute__((always_inline)) {
+        const int a = q / (NREG / CH), r0 = (q % (NREG / CH)) * CH;
+        const int lr = WN >= 64 ? (64 * j) / WN : (64 / WN) * j + lsub;
+        col = WN >= 64 ? lcol + (64 * j) % WN : lcol;
+        row = wave_m * WM + MB * Mfma<MR>::row(r0 + lr / HR, lr % HR) + a;
+    };
+    auto c_off = [&](int row, int col) __attribute__((always_inline)) -> uint32_t {
+        return row < nrow && col < ncol ? (uint32_t)(row * p.ldc + wave_n * WN + col) * 4u
+                                        : kOut;
+    };
+    auto load_cs = [&](int q, float (&cin)[V]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            int row, col;
+            elem_rc(q, j, row, col);
+            cin[j] = ld1(rt, c_off(row, col));
+        }
+    };
+    // Chunk q of this lane's accumulators into the wave's slice, and back in
+    // the row order: sv[j] = element j of the chunk.
+    auto stage_chunk = [&](float* slice, int q, float (&sv)[V]) __attribute__((always_inline)) {
+        const int a = q / (NREG / CH), r0 = (q % (NREG / CH)) * CH;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            float* const d = slice + (i * HR + elh) * WN + NB * eli;
+            if constexpr (NB == 4) {
+                *reinterpret_cast<f4*>(d) = f4{acc[a][0][r0 + i], acc[a][1][r0 + i],
+                                               acc[a][2][r0 + i], acc[a][3][r0 + i]};
+            } else if constexpr (NB == 2) {
+                *reinterpret_cast<f2*>(d) = f2{acc[a][0][r0 + i], acc[a][1][r0 + i]};
+            } else {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) d[b] = acc[a][b][r0 + i];
+            }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int j = 0; j < V; ++j) sv[j] = slice[elane + 64 * j];
+        wave_lds_sync();  // read before the next chunk rewrites the slice
+    };
     // Two copies of the store loop, chosen by a uniform branch: the plain
     // one and the fused epilogue. One loop holding both grew past what the
     // compiler fully unrolls, and the accumulators then went to scratch
@@ -590,80 +669,20 @@ sgemm_mfma_kernel(GemmParams p) {
         // this one's stores: loads and stores share one counter and no load
         // may pass an earlier store to the same buffer, so reading element by
         // element between the stores would cost a memory round trip per row.
-        constexpr int CH = NB >= 8 ? 1 : (8 / NB < NREG ? 8 / NB : NREG);
-        constexpr int NQ = MB * (NREG / CH);  // chunks
-        static_assert(NREG % CH == 0, "whole chunks");
-        if (kStageC && !vec_c) {
-            // C's rows are not aligned for a lane's NB adjacent columns to be
-            // one access, and NB single stores per row would each scatter over
-            // the row with a stride of NB elements. Instead each chunk passes
-            // through a slice of the idle operand ring that belongs to this
-            // wave (the results staged in shared memory before they are
-            // stored, as in "Optimising fp32 GEMM on A100", Kernel 6, there
-            // for wider stores): the lanes write their accumulators there,
-            // then read it back so that lane l holds element l + 64 j of the
-            // chunk (local row e / WN, column e % WN), and one single-element
-            // store (or old C read) covers 64 consecutive elements of a row of
-            // C (WN = 32: two rows of 32).
-            constexpr int HR = 64 / MR;  // lane groups = rows per register
-            constexpr int V = CH * NB;   // elements per lane per chunk
-            static_assert(NW * 64 * V <= NS * (OpA::kStage + OpB::kStage), "slices fit in LDS");
+        if (stage_c) {
+            static_assert(!kStageC || NW * 64 * V <= NS * (OpA::kStage + OpB::kStage),
+                          "slices fit in LDS");
             float* const slice = sA + wave * (64 * V);
-            const int nrow = p.M - m0, ncol = p.N - n0 - wave_n * WN;
-            // Elements past M or N get a byte offset past the end of a
-            // resource that spans at most 2^31 bytes from the tile origin
-            // (every element of a tile lies below that: at most 255 rows of
-            // at most 2^21 elements), so that their loads read 0 and their
-            // stores are dropped with no branch: a branch around each access
-            // made the compiler wait for every earlier store before each use
-            // of the old C.
-            constexpr uint32_t kOut = 0xFFFFFFF0u;
-            const int64_t c_ext = tile_ws ? (int64_t)BM * BN : p.c_extent - c_org;
-            const __amdgpu_buffer_rsrc_t rt =
-                make_rsrc(Cs + c_org, c_ext < (int64_t(1) << 29) ? c_ext : (int64_t(1) << 29));
-            // Local row and column of element j: with WN >= 64 the row is the
-            // same for the whole wave (a scalar) and the column is the lane's
-            // plus a constant; with WN = 32 the two halves of the wave take
-            // two consecutive local rows.
-            const int lsub = WN >= 64 ? 0 : elane / WN, lcol = WN >= 64 ? elane : elane % WN;
-            auto elem = [&](int q, int j) -> uint32_t {
-                const int a = q / (NREG / CH), r0 = (q % (NREG / CH)) * CH;
-                const int lr = WN >= 64 ? (64 * j) / WN : (64 / WN) * j + lsub;
-                const int col = WN >= 64 ? lcol + (64 * j) % WN : lcol;
-                const int row = wave_m * WM + MB * Mfma<MR>::row(r0 + lr / HR, lr % HR) + a;
-                return row < nrow && col < ncol
-                           ? (uint32_t)(row * p.ldc + wave_n * WN + col) * 4u
-                           : kOut;
-            };
-            auto load_cs = [&](int q, float (&cin)[V]) {
-#pragma unroll
-                for (int j = 0; j < V; ++j) cin[j] = ld1(rt, elem(q, j));
-            };
             auto store_cs = [&](int q, const float (&cin)[V], bool with_c) {
-                const int a = q / (NREG / CH), r0 = (q % (NREG / CH)) * CH;
-#pragma unroll
-                for (int i = 0; i < CH; ++i) {
-                    float* const d = slice + (i * HR + elh) * WN + NB * eli;
-                    if constexpr (NB == 4) {
-                        *reinterpret_cast<f4*>(d) = f4{acc[a][0][r0 + i], acc[a][1][r0 + i],
-                                                       acc[a][2][r0 + i], acc[a][3][r0 + i]};
-                    } else if constexpr (NB == 2) {
-                        *reinterpret_cast<f2*>(d) = f2{acc[a][0][r0 + i], acc[a][1][r0 + i]};
-                    } else {
-#pragma unroll
-                        for (int b = 0; b < NB; ++b) d[b] = acc[a][b][r0 + i];
-                    }
-                }
-                wave_lds_sync();
                 float sv[V];
-#pragma unroll
-                for (int j = 0; j < V; ++j) sv[j] = slice[elane + 64 * j];
-                wave_lds_sync();  // read before the next chunk rewrites the slice
+                stage_chunk(slice, q, sv);
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
+                    int row, col;
+                    elem_rc(q, j, row, col);
                     float v = alpha * sv[j];
                     if (with_c) v += beta * cin[j];
-                    st1_nt(rt, elem(q, j), v);
+                    st1_nt(rt, c_off(row, col), v);
                 }
             };
             lds_barrier();  // every wave is done reading the operand ring
@@ -897,27 +916,94 @@ sgemm_mfma_kernel(GemmParams p) {
                 }
             }
         };
+        // The same element order on staged rows (rows of C not aligned; see
+        // stage_chunk): element j of chunk q at tile row `row` and wave column
+        // `col`, its slice after the vectors above; Q's codes one element at
+        // a time, past-the-end offsets for elements outside C as for C.
+        constexpr int kVec = (3 * BM + 2 * BN + 3) / 4 * 4;  // floats of the vectors
+        static_assert(!kStageFused || kVec + NW * 64 * V <= NS * (OpA::kStage + OpB::kStage),
+                      "vectors and slices fit in LDS");
+        const int64_t q_bytes = quant ? (p.q_extent - q_org) * qes : 0;
+        const __amdgpu_buffer_rsrc_t rqt =
+            make_rsrc_bytes(static_cast<char*>(p.qout) + (quant ? q_org * qes : 0),
+                            q_bytes < 4 * kSpan ? q_bytes : 4 * kSpan);
+        auto store_tile_staged = [&](auto tag, auto qtag) __attribute__((always_inline)) {
+            constexpr int ACT = decltype(tag)::value;
+            constexpr int QK = decltype(qtag)::value;
+            float* const slice = vr + kVec + wave * (64 * V);
+            auto store_cs = [&](int q, const float (&cin)[V], bool with_c) __attribute__((always_inline)) {
+                float sv[V];
+                stage_chunk(slice, q, sv);
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    int row, col;
+                    elem_rc(q, j, row, col);
+                    const int tcol = wave_n * WN + col;
+                    const float sr = alpha * vr[row];
+                    float v = (sr * vr[2 * BM + tcol]) * sv[j];
+                    if (with_c) v += beta * cin[j];
+                    v = activate_t<ACT>((v + vr[BM + row]) + vr[2 * BM + BN + tcol]);
+                    const bool in = row < nrow && col < ncol;
+                    if constexpr (QK == QUANT_BF16)
+                        __builtin_amdgcn_raw_buffer_store_b16(
+                            (uint16_t)bf16_code(v), rqt,
+                            in ? (uint32_t)(row * p.ldq + tcol) * 2u : kOut, 0, 0);
+                    else if constexpr (QK == QUANT_INT8_ROW)
+                        __builtin_amdgcn_raw_buffer_store_b8(
+                            (uint8_t)int8_code(v, vr[2 * BM + 2 * BN + row]), rqt,
+                            in ? (uint32_t)(row * p.ldq + tcol) : kOut, 0, 0);
+                    st1_nt(rt, c_off(row, col), v);
+                }
+            };
+            float s0[V] = {}, s1[V] = {};
+            if (beta0) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) store_cs(q, s0, false);
+            } else {
+                load_cs(0, s0);
+#pragma unroll
+                for (int q = 0; q < NQ; q += 2) {
+                    if (q + 1 < NQ) load_cs(q + 1, s1);
+                    store_cs(q, s0, true);
+                    if (q + 1 < NQ) {
+                        if (q + 2 < NQ) load_cs(q + 2, s0);
+                        store_cs(q + 1, s1, true);
+                    }
+                }
+            }
+        };
         // One copy of the store loop per activation and quantised format,
         // chosen by plain switches (through a further generic lambda the
         // compiler kept the accumulators in scratch memory).
-#define FG_STORE_BY_ACT(QK)                                                               \
+#define FG_STORE_BY_ACT(F, QK)                                                            \
     switch (p.act) {                                                                     \
-        case ACT_RELU: store_tile(ActTag<ACT_RELU>{}, ActTag<QK>{}); break;              \
-        case ACT_GELU: store_tile(ActTag<ACT_GELU>{}, ActTag<QK>{}); break;              \
-        case ACT_SILU: store_tile(ActTag<ACT_SILU>{}, ActTag<QK>{}); break;              \
-        default: store_tile(ActTag<ACT_NONE>{}, ActTag<QK>{}); break;                    \
+        case ACT_RELU: F(ActTag<ACT_RELU>{}, ActTag<QK>{}); break;                       \
+        case ACT_GELU: F(ActTag<ACT_GELU>{}, ActTag<QK>{}); break;                       \
+        case ACT_SILU: F(ActTag<ACT_SILU>{}, ActTag<QK>{}); break;                       \
+        default: F(ActTag<ACT_NONE>{}, ActTag<QK>{}); break;                             \
     }
-        if constexpr (kQuant) {
-            if (!quant) {
-                FG_STORE_BY_ACT(QUANT_NONE)
-            } else if (p.qkind == QUANT_BF16) {
-                FG_STORE_BY_ACT(QUANT_BF16)
+#define FG_STORE_BY_QUANT(F)                                                              \
+    if constexpr (kQuant) {                                                              \
+        if (!quant) {                                                                    \
+            FG_STORE_BY_ACT(F, QUANT_NONE)                                               \
+        } else if (p.qkind == QUANT_BF16) {                                              \
+            FG_STORE_BY_ACT(F, QUANT_BF16)                                               \
+        } else {                                                                         \
+            FG_STORE_BY_ACT(F, QUANT_INT8_ROW)                                           \
+        }                                                                                \
+    } else {                                                                             \
+        FG_STORE_BY_ACT(F, QUANT_NONE)                                                   \
+    }
+        if constexpr (kStageFused) {
+            if (stage_c) {
+                FG_STORE_BY_QUANT(store_tile_staged)
             } else {
-                FG_STORE_BY_ACT(QUANT_INT8_ROW)
+                FG_STORE_BY_QUANT(store_tile)
             }
         } else {
-            FG_STORE_BY_ACT(QUANT_NONE)
+            FG_STORE_BY_QUANT(store_tile)
         }
+#undef FG_STORE_BY_QUANT
 #undef FG_STORE_BY_ACT
     }
 }

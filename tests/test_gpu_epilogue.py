@@ -33,8 +33,9 @@ def _vectors(rng, M, N, kind="normal", which=(True, True, True, True)):
     return [v if on else None for v, on in zip(vs, which)]
 
 
-def run_fused(w, A, B, C, vecs, act, config=-1, c_fill=np.nan):
-    """fg_sgemm_fused on host arrays; returns the M x N result."""
+def run_fused(w, A, B, C, vecs, act, config=-1, c_fill=np.nan, full=False):
+    """fg_sgemm_fused on host arrays; returns the M x N result (and, with
+    full, the whole C buffer as read back)."""
     import torch
     dA, _ba = to_device(A)
     dB, _bb = to_device(B)
@@ -52,7 +53,8 @@ def run_fused(w, A, B, C, vecs, act, config=-1, c_fill=np.nan):
     if st != fg.FG_OK:
         raise fg.FgError(st, fg.fg_last_bad_arg(), fg.fg_last_error())
     s.synchronize()
-    return dC.cpu().numpy().reshape(C.shape)[:, :w.N].copy()
+    buf = dC.cpu().numpy().reshape(C.shape)
+    return (buf[:, :w.N].copy(), buf) if full else buf[:, :w.N].copy()
 
 
 def reference(w, A, B, C, vecs, act):
@@ -103,6 +105,19 @@ def test_fused_integer_exact_every_config(config):
         out = run_fused(w, A, B, C, vecs, act, config=config)
         d, _, _, _ = reference(w, A, B, C, vecs, act)
         assert np.array_equal(out, d.astype(np.float32)), (config, ops, act)
+    # Rows of C not 16-byte aligned (odd ldc; the matrix-core entries stage
+    # the result through LDS there), ragged M and N; C's padding is a guard
+    # band.
+    for ops, act in (("NN", "relu"), ("TT", "none")):
+        w = workloads.custom(97, 131, 45, ops[0], ops[1], alpha=-1.0, beta=2.0, dist="int8",
+                             seed=60 + config, ldc=133)
+        A, B, C = workloads.make_inputs(w)
+        C[:, w.N:] = 2468.0
+        vecs = _vectors(np.random.default_rng(61 + config), w.M, w.N, kind="int")
+        out, buf = run_fused(w, A, B, C, vecs, act, config=config, full=True)
+        d, _, _, _ = reference(w, A, B, C, vecs, act)
+        assert np.array_equal(out, d.astype(np.float32)), (config, ops, act, "ldc 133")
+        assert np.all(buf[:, w.N:] == 2468.0), (config, ops, act, "padding written")
 
 
 @pytest.mark.parametrize("act", ["relu", "gelu"])
