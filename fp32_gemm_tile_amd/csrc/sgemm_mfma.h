@@ -357,9 +357,10 @@ sgemm_mfma_kernel(GemmParams p) {
     // are unaligned (with 256 accumulators its registers spilled).
     constexpr bool kStageC = NB >= 2 && MB * NB * NREG <= 128;
     // The fused and quantised epilogue's staged copy (twelve specialisations,
-    // each fully inlined) only where the accumulators are at most 64 per
-    // lane: with 128 one instance took over half an hour to compile.
-    constexpr bool kStageFused = kStageC && MB * NB * NREG <= 64;
+    // each fully inlined) only where the accumulators are at most 32 per
+    // lane: with 64 it doubled the library's build time, with 128 one
+    // instance took over half an hour to compile.
+    constexpr bool kStageFused = kStageC && MB * NB * NREG <= 32;
 
     __shared__ f4 smem[NS * (OpA::kStage + OpB::kStage) / 4];
     float* sA = reinterpret_cast<float*>(smem);
